@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the GDN decode state step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Headline workload (the metric is quoted on it): a Qwen3.5-shaped Gated
+DeltaNet layer -- 16 key / 32 value heads, d_k = d_v = 128, conv width 4 over
+8192 q|k|v channels, bf16 inputs, fp32 state -- decoding B = 64 requests, one
+token each, in place on a pool of 1024 slots.  Slot indices are distinct per
+call, taken as consecutive 64-blocks of a seeded permutation of the pool that
+is redrawn every 16 calls, so a slot comes back only after ~15 calls (about
+1.9 GiB of other state in between, far above the 256 MB Infinity Cache).
+
+A step is one gdn_decode_step call through the C ABI: conv update, head prep
+and the gated delta rule for all 64 requests, in one kernel.  W warm-up steps,
+then K timed steps between two HIP events on the launch stream.  One JSON line
+goes to stdout.  Other paths of the state step are measured the same way and
+reported under "paths".
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as ct
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+DECODE_KERNEL = "decode_kernel<128, 4, bf16, false>"
+
+
+def log(msg: str):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# algorithmic bytes (what the method must move; see the design notes)
+
+def decode_bytes(shape, B: int, T: int = 1, spec: bool = False) -> int:
+    """HBM bytes of one decode call: state read + write (or T snapshot writes),
+    conv window read + write, x, alpha, beta, taps, out, indices."""
+    act = 2 if shape.dtype == "bf16" else 4
+    C, W1 = shape.channels, shape.conv_width - 1
+    state = shape.n_v_heads * shape.d_v * shape.d_k * 4
+    conv = W1 * C * act
+    n_state_w = T if spec else 1
+    per_req = state * (1 + n_state_w) + conv * (1 + n_state_w)
+    per_tok = C * act + shape.n_v_heads * act * (shape.d_k if shape.gate == "channel" else 1) \
+        + shape.n_v_heads * act + shape.n_v_heads * shape.d_v * 4
+    return B * per_req + B * T * per_tok + C * shape.conv_width * act + B * 4
+
+
+def source_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_src: str):
+    """HBM bytes per launch from the committed PMC summary, if it was taken on
+    the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "decode_qwen35_b64_traffic.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("source_sha256_16") != source_hash(kernel_src):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------
+
+class DecodeBench:
+    """Pre-built C-ABI argument blocks for back-to-back decode calls, so the
+    host loop issues launches far faster than the GPU retires them."""
+
+    def __init__(self, torch, gdn, synth, shape, B, slots, n_calls, seed, n_inputs=64,
+                 n_distinct_slots=64):
+        self.torch = torch
+        rs = synth.streams(seed)
+        base = synth.make_pool(shape, n_distinct_slots, np.arange(n_distinct_slots), rs)
+        self.w_host = synth.make_conv_w(shape, rs)
+        x, al, be = synth.make_tokens(shape, (n_inputs, B, 1), rs)
+        self.idx_host = synth.rotating_indices(slots, B, n_calls, rs["indices"])
+        self.inputs_host = (x, al, be)
+        self.base = base
+        dev = _dev(torch)
+        reps = -(-slots // n_distinct_slots)
+        self.ssm = dev(base.ssm).repeat(reps, 1, 1, 1)[:slots].contiguous()
+        self.conv = dev(base.conv).repeat(reps, 1, 1)[:slots].contiguous()
+        self.w = dev(self.w_host)
+        self.x, self.al, self.be = dev(x), dev(al), dev(be)
+        self.idx = dev(self.idx_host)
+        self.out = torch.empty((B, 1, shape.n_v_heads, shape.d_v), dtype=torch.float32,
+                               device="cuda")
+        self.g = gdn.Layer(shape.n_k_heads, shape.n_v_heads, shape.d_k, shape.d_v,
+                           shape.conv_width, shape.gate, shape.dtype)
+        self.L = self.g.c_struct()
+        self.P = gdn.GdnPool(self.ssm.data_ptr(), self.conv.data_ptr(), slots)
+        self.fn = gdn.lib().gdn_decode_step
+        self.stream = ct.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self.B = B
+        self.n_inputs = n_inputs
+        self.inputs = [gdn.GdnInputs(self.x[i].data_ptr(), self.al[i].data_ptr(),
+                                     self.be[i].data_ptr(), self.w.data_ptr(), None)
+                       for i in range(n_inputs)]
+        self.idx_ptrs = [ct.c_void_p(self.idx[c].data_ptr()) for c in range(n_calls)]
+        self.out_ptr = ct.c_void_p(self.out.data_ptr())
+        self.Lref, self.Pref = ct.byref(self.L), ct.byref(self.P)
+        self.inref = [ct.byref(i) for i in self.inputs]
+
+    def call(self, c: int):
+        st = self.fn(self.Lref, self.Pref, self.idx_ptrs[c], self.B, 1,
+                     self.inref[c % self.n_inputs], self.out_ptr, None, self.stream)
+        if st != 0:
+            raise RuntimeError(f"gdn_decode_step failed with status {st}")
+
+
+def _dev(torch):
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+    return dev
+
+
+def time_calls(torch, fn, first: int, n: int) -> float:
+    """Milliseconds for n back-to-back calls fn(first..first+n-1) on the
+    current stream, between two HIP events."""
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for c in range(first, first + n):
+        fn(c)
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e)
+
+
+def cpu_baseline(synth, shape, bench: DecodeBench, budget_s: float):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload:
+    consecutive calls of the same index stream on fp64 copies of the pool."""
+    import oracle
+    o = oracle.Layer(shape.n_k_heads, shape.n_v_heads, shape.d_k, shape.d_v, shape.conv_width,
+                     shape.gate)
+    nthreads = oracle.default_threads()
+    n_distinct = bench.base.ssm.shape[0]
+    slots = int(bench.ssm.shape[0])
+    reps = -(-slots // n_distinct)
+    s64 = np.tile(oracle.as_f64(bench.base.ssm), (reps, 1, 1, 1))[:slots].copy()
+    c64 = np.tile(oracle.as_f64(bench.base.conv), (reps, 1, 1))[:slots].copy()
+    x, al, be = bench.inputs_host
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        i = n % bench.n_inputs
+        oracle.decode(o, s64, c64, bench.idx_host[n], x[i], al[i], be[i], bench.w_host,
+                      nthreads=nthreads)
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget_s or n >= bench.idx_host.shape[0]:
+            break
+    return {"value": round(bench.B * n / dt, 2), "unit": "tokens/s", "cores": nthreads,
+            "kind": "oracle",
+            "sample": f"{n} consecutive B={bench.B} decode calls of the headline workload "
+                      f"(fp64 oracle, {nthreads} threads, {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the cpu_baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the state step shards across GPUs with no "
+              "exchange (requests or key-head groups per GPU), so only --gpus 1 is run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import hybrid_linear_attention_decode_amd as gdn
+    from hybrid_linear_attention_decode_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    gdn.lib()
+
+    shape = synth.QWEN35
+    B, slots = 64, 1024
+    K, W = args.steps, args.warmup
+    log(f"bench: generating headline workload (B={B}, pool {slots}, {W}+{K} calls)")
+    bench = DecodeBench(torch, gdn, synth, shape, B, slots, W + K, seed=5)
+    for c in range(W):
+        bench.call(c)
+    torch.cuda.synchronize()
+    log("bench: warm-up done, timing")
+    ms = time_calls(torch, bench.call, W, K)
+    ms_step = ms / K
+    nbytes = decode_bytes(shape, B)
+    achieved = nbytes / (ms_step * 1e-3) / 1e9
+    tok_s = B / (ms_step * 1e-3)
+    log(f"bench: {ms_step * 1e3:.2f} us/call, {tok_s:.0f} tok/s, {achieved:.0f} GB/s")
+
+    kernel_src = os.path.join(ROOT, "hybrid_linear_attention_decode_amd", "csrc",
+                              "gdn_decode.hip")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic_from_profile(kernel_src), "kernel": DECODE_KERNEL,
+                "algorithmic_bytes_per_launch": nbytes}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle sample")
+        cpu = cpu_baseline(synth, shape, bench, args.cpu_budget)
+
+    rec = {
+        "metric": "GDN decode tokens/s and achieved HBM GB/s (fraction of peak) at B=64",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "GDN decode, Qwen3.5-shaped layer (16 key / 32 value heads, "
+                               "d_k=d_v=128, conv width 4, 8192 channels), B=64, T=1, "
+                               "pool 1024, bf16 inputs, fp32 state",
+                   "global_batch": B, "tokens_per_request": 1, "pool_slots": slots},
+        "hbm_gbps": round(achieved, 1),
+        "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

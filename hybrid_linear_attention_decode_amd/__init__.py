@@ -1,0 +1,243 @@
+"""Python binding of libgdn (include/gdn.h): argument marshalling only.
+
+Every step of the state path runs in the HIP kernels of ``libgdn.so``; this
+module turns torch tensors (device memory) and the current HIP stream into the
+plain pointers and sizes of the C ABI, and raises ``GdnError`` on a non-OK
+status.  There is no fallback: if the library is not built, every call fails
+loudly.  Build it with ``python -m hybrid_linear_attention_decode_amd.build``.
+
+Entry points (same names as the C ABI):
+    gdn_decode_step, gdn_spec_decode_commit, gdn_prefill_chunked,
+    gdn_prefill_workspace_size, gdn_slot_copy, gdn_slot_zero, gdn_status_string
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+from dataclasses import dataclass
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+
+GDN_OK = 0
+GDN_ERR_NULL_ARG = 1
+GDN_ERR_BAD_SHAPE = 2
+GDN_ERR_BAD_DTYPE = 3
+GDN_ERR_UNSUPPORTED = 4
+GDN_ERR_WORKSPACE = 5
+GDN_ERR_LAUNCH = 6
+
+GDN_F32, GDN_BF16 = 0, 1
+GDN_GATE_SCALAR, GDN_GATE_CHANNEL = 0, 1
+GDN_F_CONV_SILU, GDN_F_L2NORM_QK = 1, 2
+
+EXPORTED = ("gdn_decode_step", "gdn_spec_decode_commit", "gdn_prefill_chunked",
+            "gdn_prefill_workspace_size", "gdn_slot_copy", "gdn_slot_zero", "gdn_status_string")
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {gdn_status_string(status)} (status {status})")
+        self.status = status
+
+
+class GdnLayer(ct.Structure):
+    _fields_ = [("n_k_heads", ct.c_int32), ("n_v_heads", ct.c_int32), ("d_k", ct.c_int32),
+                ("d_v", ct.c_int32), ("conv_width", ct.c_int32), ("gate", ct.c_int32),
+                ("act_dtype", ct.c_int32), ("flags", ct.c_uint32), ("q_scale", ct.c_float),
+                ("l2_eps", ct.c_float)]
+
+
+class GdnPool(ct.Structure):
+    _fields_ = [("ssm", ct.c_void_p), ("conv", ct.c_void_p), ("num_slots", ct.c_int64)]
+
+
+class GdnSpecCache(ct.Structure):
+    _fields_ = [("ssm", ct.c_void_p), ("conv", ct.c_void_p), ("t_max", ct.c_int32)]
+
+
+class GdnInputs(ct.Structure):
+    _fields_ = [("x", ct.c_void_p), ("alpha", ct.c_void_p), ("beta", ct.c_void_p),
+                ("conv_w", ct.c_void_p), ("conv_b", ct.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ct.CDLL:
+    """The loaded libgdn.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libgdn.so is not built ({LIB_PATH}); run "
+                               "python -m hybrid_linear_attention_decode_amd.build")
+        L = ct.CDLL(LIB_PATH)
+        P, i32, i64 = ct.c_void_p, ct.c_int32, ct.c_int64
+        lp = ct.POINTER(GdnLayer)
+        pp = ct.POINTER(GdnPool)
+        sp = ct.POINTER(GdnSpecCache)
+        ip = ct.POINTER(GdnInputs)
+        L.gdn_decode_step.argtypes = [lp, pp, P, i32, i32, ip, P, sp, P]
+        L.gdn_spec_decode_commit.argtypes = [lp, pp, P, sp, P, i32, P]
+        L.gdn_prefill_chunked.argtypes = [lp, pp, P, P, i32, P, i32, i32, i32, ip, P, P,
+                                          ct.c_size_t, P]
+        L.gdn_prefill_workspace_size.argtypes = [lp, i32, i32, i32, i32]
+        L.gdn_prefill_workspace_size.restype = ct.c_size_t
+        L.gdn_slot_copy.argtypes = [lp, pp, P, P, i32, P]
+        L.gdn_slot_zero.argtypes = [lp, pp, P, i32, P]
+        L.gdn_status_string.argtypes = [ct.c_int]
+        L.gdn_status_string.restype = ct.c_char_p
+        for f in ("gdn_decode_step", "gdn_spec_decode_commit", "gdn_prefill_chunked",
+                  "gdn_slot_copy", "gdn_slot_zero"):
+            getattr(L, f).restype = ct.c_int
+        _lib = L
+    return _lib
+
+
+def gdn_status_string(status: int) -> str:
+    return lib().gdn_status_string(int(status)).decode()
+
+
+@dataclass
+class Layer:
+    """One linear-attention layer (mirrors gdn_layer)."""
+    n_k_heads: int
+    n_v_heads: int
+    d_k: int
+    d_v: int
+    conv_width: int = 4
+    gate: str = "scalar"          # "scalar" (GDN) or "channel" (KDA)
+    act_dtype: str = "bf16"       # "bf16" or "f32"
+    conv_silu: bool = True
+    l2norm: bool = True
+    q_scale: float | None = None  # default 1/sqrt(d_k)
+    l2_eps: float = 1e-6
+
+    @property
+    def channels(self) -> int:
+        return 2 * self.n_k_heads * self.d_k + self.n_v_heads * self.d_v
+
+    @property
+    def torch_act_dtype(self):
+        import torch
+        return torch.bfloat16 if self.act_dtype == "bf16" else torch.float32
+
+    def c_struct(self) -> GdnLayer:
+        qs = self.q_scale if self.q_scale is not None else self.d_k ** -0.5
+        flags = (GDN_F_CONV_SILU if self.conv_silu else 0) | (GDN_F_L2NORM_QK if self.l2norm else 0)
+        return GdnLayer(self.n_k_heads, self.n_v_heads, self.d_k, self.d_v, self.conv_width,
+                        GDN_GATE_CHANNEL if self.gate == "channel" else GDN_GATE_SCALAR,
+                        GDN_BF16 if self.act_dtype == "bf16" else GDN_F32, flags, float(qs),
+                        float(self.l2_eps))
+
+
+def _ptr(t):
+    return None if t is None else ct.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ct.c_void_p(s.cuda_stream)
+
+
+def _dev(*tensors):
+    for t in tensors:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("libgdn takes contiguous device tensors")
+
+
+def _check(status: int, what: str):
+    if status != GDN_OK:
+        raise GdnError(status, what)
+
+
+def _pool(ssm, conv) -> GdnPool:
+    return GdnPool(_ptr(ssm), _ptr(conv), ssm.shape[0])
+
+
+def _spec(spec_ssm, spec_conv):
+    if spec_ssm is None:
+        return None
+    return ct.byref(GdnSpecCache(_ptr(spec_ssm), _ptr(spec_conv), spec_ssm.shape[1]))
+
+
+def gdn_decode_step(layer: Layer, ssm, conv, mamba_pool_indices, x, alpha, beta, conv_w,
+                    conv_b=None, out=None, spec_ssm=None, spec_conv=None, stream=None):
+    """x [B, T, C]; returns out [B, T, H_v, d_v] fp32.  See include/gdn.h."""
+    import torch
+    _dev(ssm, conv, mamba_pool_indices, x, alpha, beta, conv_w, conv_b, out, spec_ssm, spec_conv)
+    B, T = x.shape[0], x.shape[1]
+    if mamba_pool_indices.dtype != torch.int32 or mamba_pool_indices.numel() != B:
+        raise ValueError("mamba_pool_indices must be int32 [B]")
+    if out is None:
+        out = torch.empty((B, T, layer.n_v_heads, layer.d_v), dtype=torch.float32, device=x.device)
+    L = layer.c_struct()
+    P = _pool(ssm, conv)
+    inp = GdnInputs(_ptr(x), _ptr(alpha), _ptr(beta), _ptr(conv_w), _ptr(conv_b))
+    st = lib().gdn_decode_step(ct.byref(L), ct.byref(P), _ptr(mamba_pool_indices), B, T,
+                               ct.byref(inp), _ptr(out), _spec(spec_ssm, spec_conv),
+                               _stream(stream))
+    _check(st, "gdn_decode_step")
+    return out
+
+
+def gdn_spec_decode_commit(layer: Layer, ssm, conv, mamba_pool_indices, spec_ssm, spec_conv,
+                           accepted_len, stream=None):
+    _dev(ssm, conv, mamba_pool_indices, spec_ssm, spec_conv, accepted_len)
+    L = layer.c_struct()
+    P = _pool(ssm, conv)
+    st = lib().gdn_spec_decode_commit(ct.byref(L), ct.byref(P), _ptr(mamba_pool_indices),
+                                      _spec(spec_ssm, spec_conv), _ptr(accepted_len),
+                                      mamba_pool_indices.numel(), _stream(stream))
+    _check(st, "gdn_spec_decode_commit")
+
+
+def gdn_slot_copy(layer: Layer, ssm, conv, src, dst, stream=None):
+    _dev(ssm, conv, src, dst)
+    if src.numel() != dst.numel():
+        raise ValueError("src and dst differ in length")
+    L = layer.c_struct()
+    P = _pool(ssm, conv)
+    st = lib().gdn_slot_copy(ct.byref(L), ct.byref(P), _ptr(src), _ptr(dst), src.numel(),
+                             _stream(stream))
+    _check(st, "gdn_slot_copy")
+
+
+def gdn_slot_zero(layer: Layer, ssm, conv, idx, stream=None):
+    _dev(ssm, conv, idx)
+    L = layer.c_struct()
+    P = _pool(ssm, conv)
+    st = lib().gdn_slot_zero(ct.byref(L), ct.byref(P), _ptr(idx), idx.numel(), _stream(stream))
+    _check(st, "gdn_slot_zero")
+
+
+def gdn_prefill_workspace_size(layer: Layer, N: int, max_seqlen: int, total_tokens: int,
+                               chunk: int = 64) -> int:
+    L = layer.c_struct()
+    return int(lib().gdn_prefill_workspace_size(ct.byref(L), N, max_seqlen, total_tokens, chunk))
+
+
+def gdn_prefill_chunked(layer: Layer, ssm, conv, dst_slots, init_slot, cu_seqlens, max_seqlen,
+                        x, alpha, beta, conv_w, conv_b=None, out=None, workspace=None,
+                        chunk: int = 64, stream=None):
+    """x [total, C]; cu_seqlens [N+1] int32 (device); returns out [total, H_v, d_v] fp32."""
+    import torch
+    _dev(ssm, conv, dst_slots, init_slot, cu_seqlens, x, alpha, beta, conv_w, conv_b, out,
+         workspace)
+    N = dst_slots.numel()
+    total = x.shape[0]
+    if out is None:
+        out = torch.empty((total, layer.n_v_heads, layer.d_v), dtype=torch.float32,
+                          device=x.device)
+    need = gdn_prefill_workspace_size(layer, N, max_seqlen, total, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    L = layer.c_struct()
+    P = _pool(ssm, conv)
+    inp = GdnInputs(_ptr(x), _ptr(alpha), _ptr(beta), _ptr(conv_w), _ptr(conv_b))
+    st = lib().gdn_prefill_chunked(ct.byref(L), ct.byref(P), _ptr(dst_slots), _ptr(init_slot),
+                                   N, _ptr(cu_seqlens), int(max_seqlen), int(total), int(chunk),
+                                   ct.byref(inp), _ptr(out), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "gdn_prefill_chunked")
+    return out

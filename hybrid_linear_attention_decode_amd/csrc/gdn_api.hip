@@ -1,0 +1,211 @@
+// gdn_api.hip -- the C ABI of libgdn (declared in include/gdn.h): host-side
+// validation of every host-checkable argument, then one asynchronous launch
+// on the caller's stream.  Nothing is allocated and no global state is kept.
+#include "gdn.h"
+#include "gdn_internal.hpp"
+
+#include <stdint.h>
+
+namespace {
+
+using gdn::DecodeArgs;
+using gdn::SlotArgs;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t channels(const gdn_layer* L) {
+  return 2 * static_cast<int64_t>(L->n_k_heads) * L->d_k +
+         static_cast<int64_t>(L->n_v_heads) * L->d_v;
+}
+
+size_t act_size(const gdn_layer* L) { return L->act_dtype == GDN_BF16 ? 2 : 4; }
+
+gdn_status check_layer(const gdn_layer* L) {
+  if (!L) return GDN_ERR_NULL_ARG;
+  if (L->gate != GDN_GATE_SCALAR && L->gate != GDN_GATE_CHANNEL) return GDN_ERR_BAD_DTYPE;
+  if (L->act_dtype != GDN_F32 && L->act_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
+  if (L->n_k_heads <= 0 || L->n_v_heads <= 0) return GDN_ERR_BAD_SHAPE;
+  if (L->n_v_heads % L->n_k_heads) return GDN_ERR_BAD_SHAPE;
+  if (L->n_k_heads > 65535) return GDN_ERR_BAD_SHAPE;
+  if (L->d_k <= 0 || L->d_v <= 0 || L->conv_width < 1) return GDN_ERR_BAD_SHAPE;
+  if (L->flags & ~(GDN_F_CONV_SILU | GDN_F_L2NORM_QK)) return GDN_ERR_BAD_SHAPE;
+  if (!(L->l2_eps >= 0.f) || !(L->q_scale == L->q_scale)) return GDN_ERR_BAD_SHAPE;
+  if (L->d_k != 16 && L->d_k != 32 && L->d_k != 64 && L->d_k != 128) return GDN_ERR_UNSUPPORTED;
+  if (L->d_v % 16 || L->d_v > 256) return GDN_ERR_UNSUPPORTED;
+  if (L->conv_width > 4) return GDN_ERR_UNSUPPORTED;
+  return GDN_OK;
+}
+
+gdn_status check_pool(const gdn_layer* L, const gdn_pool* P) {
+  if (!P || !P->ssm) return GDN_ERR_NULL_ARG;
+  if (L->conv_width > 1 && !P->conv) return GDN_ERR_NULL_ARG;
+  if (P->num_slots < 0 || P->num_slots > INT32_MAX) return GDN_ERR_BAD_SHAPE;
+  if (!aligned16(P->ssm) || (P->conv && !aligned16(P->conv))) return GDN_ERR_BAD_SHAPE;
+  return GDN_OK;
+}
+
+gdn_status check_spec(const gdn_layer* L, const gdn_spec_cache* S) {
+  if (!S->ssm) return GDN_ERR_NULL_ARG;
+  if (L->conv_width > 1 && !S->conv) return GDN_ERR_NULL_ARG;
+  if (S->t_max < 1) return GDN_ERR_BAD_SHAPE;
+  if (!aligned16(S->ssm) || (S->conv && !aligned16(S->conv))) return GDN_ERR_BAD_SHAPE;
+  return GDN_OK;
+}
+
+gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH; }
+
+SlotArgs slot_args(const gdn_layer* L, const gdn_pool* P, int32_t n) {
+  SlotArgs a{};
+  a.n = n;
+  a.num_slots = P->num_slots;
+  a.ssm_vec = static_cast<int64_t>(L->n_v_heads) * L->d_v * L->d_k / 4;
+  a.conv_vec = static_cast<int64_t>(L->conv_width - 1) * channels(L) *
+               static_cast<int64_t>(act_size(L)) / 16;
+  a.ssm = P->ssm;
+  a.conv = P->conv;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(gdn_status s) {
+  switch (s) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL_ARG: return "a required pointer is NULL";
+    case GDN_ERR_BAD_SHAPE: return "inconsistent or out-of-range sizes or misaligned pointer";
+    case GDN_ERR_BAD_DTYPE: return "unknown dtype or gate kind";
+    case GDN_ERR_UNSUPPORTED: return "shape not supported by the built kernels";
+    case GDN_ERR_WORKSPACE: return "prefill workspace missing or too small";
+    case GDN_ERR_LAUNCH: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+gdn_status gdn_decode_step(const gdn_layer* L, const gdn_pool* P, const int32_t* idx, int32_t B,
+                           int32_t T, const gdn_inputs* in, float* out,
+                           const gdn_spec_cache* spec, void* stream) {
+  gdn_status st = check_layer(L);
+  if (st != GDN_OK) return st;
+  if ((st = check_pool(L, P)) != GDN_OK) return st;
+  if (B < 0 || B > 65535 || T < 1) return GDN_ERR_BAD_SHAPE;
+  if (!idx || !in || !out) return GDN_ERR_NULL_ARG;
+  if (!in->x || !in->alpha || !in->beta || !in->conv_w) return GDN_ERR_NULL_ARG;
+  if (spec) {
+    if ((st = check_spec(L, spec)) != GDN_OK) return st;
+    if (T > spec->t_max) return GDN_ERR_BAD_SHAPE;
+  }
+  const int G = L->n_v_heads / L->n_k_heads;
+  if (!gdn::decode_rows_per_lane(L->d_k, G * L->d_v, 2 * L->d_k + G * L->d_v))
+    return GDN_ERR_UNSUPPORTED;
+  if (B == 0) return GDN_OK;
+
+  DecodeArgs a{};
+  a.Hk = L->n_k_heads;
+  a.Hv = L->n_v_heads;
+  a.dv = L->d_v;
+  a.W = L->conv_width;
+  a.C = static_cast<int32_t>(channels(L));
+  a.G = G;
+  a.B = B;
+  a.T = T;
+  a.num_slots = P->num_slots;
+  a.silu = (L->flags & GDN_F_CONV_SILU) ? 1 : 0;
+  a.l2norm = (L->flags & GDN_F_L2NORM_QK) ? 1 : 0;
+  a.q_scale = L->q_scale;
+  a.eps = L->l2_eps;
+  a.ssm = P->ssm;
+  a.conv = P->conv;
+  a.idx = idx;
+  a.x = in->x;
+  a.alpha = in->alpha;
+  a.beta = in->beta;
+  a.w = in->conv_w;
+  a.bias = in->conv_b;
+  a.out = out;
+  a.spec_ssm = spec ? spec->ssm : nullptr;
+  a.spec_conv = spec ? spec->conv : nullptr;
+  a.t_max = spec ? spec->t_max : 0;
+  return from_hip(gdn::launch_decode(a, L->d_k, L->act_dtype == GDN_BF16,
+                                     L->gate == GDN_GATE_CHANNEL,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_spec_decode_commit(const gdn_layer* L, const gdn_pool* P, const int32_t* idx,
+                                  const gdn_spec_cache* spec, const int32_t* accepted_len,
+                                  int32_t B, void* stream) {
+  gdn_status st = check_layer(L);
+  if (st != GDN_OK) return st;
+  if ((st = check_pool(L, P)) != GDN_OK) return st;
+  if (!spec || !idx || !accepted_len) return GDN_ERR_NULL_ARG;
+  if ((st = check_spec(L, spec)) != GDN_OK) return st;
+  if (B < 0 || B > 65535) return GDN_ERR_BAD_SHAPE;
+  SlotArgs a = slot_args(L, P, B);
+  a.a = idx;
+  a.b = accepted_len;
+  a.spec_ssm = spec->ssm;
+  a.spec_conv = spec->conv;
+  a.t_max = spec->t_max;
+  return from_hip(gdn::launch_slots(a, gdn::kSlotCommit, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_slot_copy(const gdn_layer* L, const gdn_pool* P, const int32_t* src,
+                         const int32_t* dst, int32_t n, void* stream) {
+  gdn_status st = check_layer(L);
+  if (st != GDN_OK) return st;
+  if ((st = check_pool(L, P)) != GDN_OK) return st;
+  if (n < 0 || n > 65535) return GDN_ERR_BAD_SHAPE;
+  if (n > 0 && (!src || !dst)) return GDN_ERR_NULL_ARG;
+  SlotArgs a = slot_args(L, P, n);
+  a.a = src;
+  a.b = dst;
+  return from_hip(gdn::launch_slots(a, gdn::kSlotCopy, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_slot_zero(const gdn_layer* L, const gdn_pool* P, const int32_t* idx, int32_t n,
+                         void* stream) {
+  gdn_status st = check_layer(L);
+  if (st != GDN_OK) return st;
+  if ((st = check_pool(L, P)) != GDN_OK) return st;
+  if (n < 0 || n > 65535) return GDN_ERR_BAD_SHAPE;
+  if (n > 0 && !idx) return GDN_ERR_NULL_ARG;
+  SlotArgs a = slot_args(L, P, n);
+  a.a = idx;
+  return from_hip(gdn::launch_slots(a, gdn::kSlotZero, static_cast<hipStream_t>(stream)));
+}
+
+size_t gdn_prefill_workspace_size(const gdn_layer* L, int32_t N, int32_t max_seqlen,
+                                  int32_t total_tokens, int32_t chunk) {
+  (void)L;
+  (void)N;
+  (void)max_seqlen;
+  (void)total_tokens;
+  (void)chunk;
+  return 0;
+}
+
+gdn_status gdn_prefill_chunked(const gdn_layer* L, const gdn_pool* P, const int32_t* dst,
+                               const int32_t* init_slot, int32_t N, const int32_t* cu_seqlens,
+                               int32_t max_seqlen, int32_t total_tokens, int32_t chunk,
+                               const gdn_inputs* in, float* out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  (void)P;
+  (void)dst;
+  (void)init_slot;
+  (void)N;
+  (void)cu_seqlens;
+  (void)max_seqlen;
+  (void)total_tokens;
+  (void)chunk;
+  (void)in;
+  (void)out;
+  (void)workspace;
+  (void)workspace_bytes;
+  (void)stream;
+  gdn_status st = check_layer(L);
+  if (st != GDN_OK) return st;
+  return GDN_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

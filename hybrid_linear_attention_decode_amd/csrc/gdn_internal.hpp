@@ -1,0 +1,58 @@
+// gdn_internal.hpp -- argument blocks shared by the C-ABI entry points
+// (gdn_api.hip) and the kernel launchers (gdn_decode.hip, gdn_slots.hip,
+// gdn_prefill.hip).  Host-visible only; no device code here.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// One decode call: T tokens for B requests of one layer.
+struct DecodeArgs {
+  int32_t Hk, Hv, dv, W, C, G;
+  int32_t B, T;
+  int64_t num_slots;
+  int32_t silu, l2norm;
+  float q_scale, eps;
+  float* ssm;                // [slots][Hv][dv][dk]
+  void* conv;                // [slots][W-1][C]
+  const int32_t* idx;        // [B]
+  const void* x;             // [B*T][C]
+  const void* alpha;         // [B*T][Hv] or [B*T][Hv][dk]
+  const void* beta;          // [B*T][Hv]
+  const void* w;             // [C][W]
+  const void* bias;          // [C] or nullptr
+  float* out;                // [B*T][Hv][dv]
+  float* spec_ssm;           // [B][t_max][Hv][dv][dk] or nullptr
+  void* spec_conv;           // [B][t_max][W-1][C]
+  int32_t t_max;
+};
+
+// Bulk slot operations (copy, zero, commit of a snapshot).
+struct SlotArgs {
+  int32_t n;                 // items
+  int64_t num_slots;
+  int64_t ssm_vec;           // 16-byte vectors per ssm slot
+  int64_t conv_vec;          // 16-byte vectors per conv slot
+  float* ssm;
+  void* conv;
+  const int32_t* a;          // copy: src; zero: idx; commit: mamba_pool_indices
+  const int32_t* b;          // copy: dst; commit: accepted_len
+  const float* spec_ssm;     // commit only
+  const void* spec_conv;
+  int32_t t_max;
+};
+
+enum SlotMode { kSlotCopy = 0, kSlotZero = 1, kSlotCommit = 2 };
+
+// Launchers: return hipSuccess or the launch error.  The caller has validated
+// every host-checkable argument.
+hipError_t launch_decode(const DecodeArgs& a, int dk, int act_bf16, int kda, hipStream_t s);
+hipError_t launch_slots(const SlotArgs& a, SlotMode mode, hipStream_t s);
+
+// Rows-per-lane choice of the decode kernel for a shape; 0 when unsupported.
+int decode_rows_per_lane(int dk, int rows_per_group, int channels_per_group);
+int decode_threads(int dk, int nr, int rows_per_group);
+
+}  // namespace gdn

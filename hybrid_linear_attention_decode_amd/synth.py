@@ -96,15 +96,24 @@ class Pool:
 
 
 def make_pool(shape: Shape, num_slots: int, live, rs: dict) -> Pool:
-    """Pool whose `live` slots hold random state; every other slot is NaN."""
-    live = np.asarray(live, dtype=np.int32)
+    """Pool whose `live` slots (sorted order) hold random state; every other
+    slot is NaN."""
+    live = np.unique(np.asarray(live, dtype=np.int32))
     W1, C = shape.conv_width - 1, shape.channels
-    ssm = np.full((num_slots, shape.n_v_heads, shape.d_v, shape.d_k), np.nan, np.float32)
-    conv = np.full((num_slots, W1, C), np.nan, np.float32)
-    if live.size:
-        ssm[live] = _normal(rs["pool_ssm"], (live.size, shape.n_v_heads, shape.d_v, shape.d_k),
-                            1.0 / np.sqrt(shape.d_k))
-        conv[live] = _normal(rs["pool_conv"], (live.size, W1, C))
+    per_slot = (shape.n_v_heads, shape.d_v, shape.d_k)
+    ssm = np.empty((num_slots,) + per_slot, np.float32)
+    conv = np.empty((num_slots, W1, C), np.float32)
+    scale = np.float32(1.0 / np.sqrt(shape.d_k))
+    if live.size == num_slots:   # draw straight into the pool (same values)
+        rs["pool_ssm"].standard_normal(dtype=np.float32, out=ssm)
+        ssm *= scale
+        rs["pool_conv"].standard_normal(dtype=np.float32, out=conv)
+    else:
+        ssm.fill(np.nan)
+        conv.fill(np.nan)
+        if live.size:
+            ssm[live] = _normal(rs["pool_ssm"], (live.size,) + per_slot, scale)
+            conv[live] = _normal(rs["pool_conv"], (live.size, W1, C))
     return Pool(ssm, encode(conv, shape.dtype), live)
 
 
@@ -153,11 +162,16 @@ class DecodeCase:
 
 
 def decode_case(shape: Shape, B: int, T: int, num_slots: int, n_calls: int, seed: int,
-                all_live: bool = False) -> DecodeCase:
+                all_live: bool = False, rotate: bool = True) -> DecodeCase:
     """Decode workload: every slot that any call touches is live; the rest of
-    the pool is NaN-poisoned unless all_live."""
+    the pool is NaN-poisoned unless all_live.  rotate=False keeps one seeded
+    draw of B distinct slots for every call."""
     rs = streams(seed)
-    idx = rotating_indices(num_slots, B, n_calls, rs["indices"])
+    if rotate:
+        idx = rotating_indices(num_slots, B, n_calls, rs["indices"])
+    else:
+        one = rs["indices"].permutation(num_slots)[:B].astype(np.int32)
+        idx = np.tile(one, (n_calls, 1))
     live = np.arange(num_slots, dtype=np.int32) if all_live else np.unique(idx)
     pool = make_pool(shape, num_slots, live, rs)
     w = make_conv_w(shape, rs)

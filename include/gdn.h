@@ -1,0 +1,205 @@
+/*
+ * gdn.h -- C ABI of libgdn: the per-request recurrent-state step of the
+ * linear-attention layers of hybrid models (Gated DeltaNet, and the KDA
+ * variant with a per-key-channel gate), on AMD Instinct MI355X (gfx950).
+ *
+ * What the calls compute.  For every request b with slot s = mamba_pool_indices[b]
+ * and every token t:
+ *   1. causal depthwise conv update of the conv window of slot s:
+ *        win = (conv[s][0..W-2][c], x_t[c]),  y_c = sum_j conv_w[c][j] win[j] (+ conv_b[c]),
+ *        conv[s] <- win[1..W-1],  a = SiLU(y)               (GDN_F_CONV_SILU)
+ *   2. head prep: a = q | k | v (head-major), q^ = q (|q|^2+eps)^-1/2 q_scale,
+ *      k^ = k (|k|^2+eps)^-1/2 (GDN_F_L2NORM_QK); value head h reads key head
+ *      h / (H_v/H_k);
+ *   3. gated delta rule, in place on the fp32 state S (d_v x d_k) of slot s:
+ *        S' = alpha S (GDN)  or  S' = S diag(alpha) (KDA, alpha in R^{d_k}),
+ *        u = beta (v - S' k^),  S <- S' + u k^T,  o = S q^
+ *      i.e. S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *      o_t = S_t q_t.
+ * The pages behind this library name the layers (Gated DeltaNet in Qwen3.5,
+ * KDA in Kimi K3) and describe the state machinery these calls serve, but
+ * print no formula:
+ *   - aitujian.cn, "TokenSpeed" AICon talk, section "Why agentic inference
+ *     needs a new engine": the context of these layers is a continuously
+ *     iterated SSM state plus a conv state that must be updated, saved and
+ *     restored;
+ *   - "TokenSpeed alcanza 580 tps con Qwen3.5-397B-A17B en GPU", section
+ *     "Scheduler dual": per-request mamba_pool_indices, state updated in place
+ *     every decode step, a spec_cache of per-speculative-step Conv/SSM
+ *     snapshots for rollback, prefill populating the state;
+ *   - same page, section "Ciclo de vida de slots": working vs checkpoint slots;
+ *   - same page, section "Riesgo de correctitud: estado obsoleto": the slot
+ *     allocator never clears memory, so a fresh working slot is safe only by
+ *     copy-on-write from a clean checkpoint or by explicit zeroing.
+ *
+ * Conventions for every entry point.
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns and
+ *     allocates every buffer; the library allocates nothing, keeps no global
+ *     state and is safe to call from several host threads.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     default stream).  Returning GDN_OK means "validated and enqueued".
+ *   - Host-checkable errors (NULL pointers, shapes, dtypes, unsupported sizes,
+ *     T > t_max, workspace too small) return a GDN_ERR_* code with nothing
+ *     enqueued.  A failed launch returns GDN_ERR_LAUNCH.
+ *   - Device-resident indices are not range-checked on the host.  A slot index
+ *     < 0 or >= num_slots skips that row (no read, no write, output untouched);
+ *     an accepted length outside [0, t_max] is treated as 0.  Destination slots
+ *     of one call must be distinct (two rows updating one slot race).
+ *   - `out` must not alias any input or either pool.
+ *
+ * Layouts (row-major; act = gdn_layer.act_dtype, C = 2 H_k d_k + H_v d_v):
+ *   pool.ssm   [num_slots][H_v][d_v][d_k] fp32  (row = value index, contiguous
+ *                                                over key index)
+ *   pool.conv  [num_slots][W-1][C]        act   (oldest input first)
+ *   x          [rows][C]                  act   (channel order q | k | v)
+ *   alpha      [rows][H_v]  or  [rows][H_v][d_k] (KDA)   act, values in (0, 1]
+ *   beta       [rows][H_v]                act
+ *   conv_w     [C][W] act;  conv_b [C] act or NULL
+ *   out        [rows][H_v][d_v]           fp32
+ *   spec.ssm   [B][t_max][H_v][d_v][d_k]  fp32;  spec.conv [B][t_max][W-1][C] act
+ * Decode rows are b*T + t; prefill rows are token positions given by cu_seqlens.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_NULL_ARG = 1,    /* a required pointer is NULL */
+  GDN_ERR_BAD_SHAPE = 2,   /* inconsistent or out-of-range sizes */
+  GDN_ERR_BAD_DTYPE = 3,   /* unknown dtype / gate enum */
+  GDN_ERR_UNSUPPORTED = 4, /* valid but not built (e.g. d_k not in {16,32,64,128}) */
+  GDN_ERR_WORKSPACE = 5,   /* prefill workspace missing or too small */
+  GDN_ERR_LAUNCH = 6       /* the HIP launch failed */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef enum {
+  GDN_GATE_SCALAR = 0, /* GDN: one alpha per (token, value head) */
+  GDN_GATE_CHANNEL = 1 /* KDA: alpha[d_k] per (token, value head) */
+} gdn_gate;
+
+enum {
+  GDN_F_CONV_SILU = 1u << 0, /* SiLU after the conv */
+  GDN_F_L2NORM_QK = 1u << 1  /* L2-normalise q and k per head */
+};
+
+/* (host) layer description */
+typedef struct {
+  int32_t n_k_heads, n_v_heads; /* H_v % H_k == 0 */
+  int32_t d_k, d_v;             /* d_k in {16, 32, 64, 128}; d_v a multiple of 16, <= 256 */
+  int32_t conv_width;           /* W in 1..4; W == 1 means no conv state */
+  int32_t gate;                 /* gdn_gate */
+  int32_t act_dtype;            /* gdn_dtype of x, alpha, beta, conv_w, conv_b, conv state */
+  uint32_t flags;               /* GDN_F_* */
+  float q_scale;                /* usually 1/sqrt(d_k) */
+  float l2_eps;                 /* usually 1e-6 */
+} gdn_layer;
+
+/* (host) struct of device pointers: the state pools */
+typedef struct {
+  float* ssm;
+  void* conv; /* may be NULL when conv_width == 1 */
+  int64_t num_slots;
+} gdn_pool;
+
+/* (host) struct of device pointers: per-draft-token snapshots */
+typedef struct {
+  float* ssm;
+  void* conv;
+  int32_t t_max;
+} gdn_spec_cache;
+
+/* (host) struct of device pointers: per-token inputs */
+typedef struct {
+  const void* x;
+  const void* alpha;
+  const void* beta;
+  const void* conv_w;
+  const void* conv_b; /* NULL: no bias */
+} gdn_inputs;
+
+/*
+ * Decode T >= 1 tokens per request ("Scheduler dual": the state of the slot
+ * named by mamba_pool_indices is updated in place every decode step; with a
+ * spec cache, per-speculative-step Conv/SSM snapshots are kept for rollback).
+ *   mamba_pool_indices [B] int32 (device); B >= 0; 1 <= T.
+ *   out [B][T][H_v][d_v] fp32: o_t for every token.
+ *   spec == NULL: conv and ssm of each slot are updated in place after T tokens.
+ *   spec != NULL: T <= spec->t_max; the state after token t (0-based) goes to
+ *     spec->ssm[b][t] and spec->conv[b][t]; the pool is only read.
+ */
+gdn_status gdn_decode_step(const gdn_layer* layer, const gdn_pool* pool,
+                           const int32_t* mamba_pool_indices, int32_t B, int32_t T,
+                           const gdn_inputs* in, float* out, const gdn_spec_cache* spec,
+                           void* stream);
+
+/*
+ * Rollback / commit after verification ("Scheduler dual": rollback from the
+ * spec_cache when verification fails).  For each b with L = accepted_len[b]:
+ * L > 0 copies snapshot L-1 (ssm and conv) into slot mamba_pool_indices[b];
+ * L == 0 leaves the slot as it was before the draft.  Bitwise copy.
+ *   accepted_len [B] int32 (device), each in [0, spec->t_max].
+ */
+gdn_status gdn_spec_decode_commit(const gdn_layer* layer, const gdn_pool* pool,
+                                  const int32_t* mamba_pool_indices,
+                                  const gdn_spec_cache* spec, const int32_t* accepted_len,
+                                  int32_t B, void* stream);
+
+/*
+ * Chunked prefill of N variable-length sequences ("Scheduler dual": prefill
+ * populates the initial state; "Riesgo de correctitud": a fresh working slot
+ * starts from a clean checkpoint copy or from zeros).
+ *   dst_slots [N] int32 (device): the working slot each sequence writes.
+ *   init_slot [N] int32 (device) or NULL: -1 = start from zero state and zero
+ *     conv window; s >= 0 = start from slot s (s == dst continues in place,
+ *     any other s is a copy-on-write source that is only read).  NULL means
+ *     init_slot == dst_slots.  No init slot may be another sequence's dst.
+ *   cu_seqlens [N+1] int32 (device), cu_seqlens[0] == 0, non-decreasing;
+ *     max_seqlen (host) >= every length; total_tokens (host) == cu_seqlens[N].
+ *   chunk: 64 (the only chunk length built).
+ *   out [total][H_v][d_v] fp32.
+ *   workspace: device scratch of at least gdn_prefill_workspace_size() bytes,
+ *     256-byte aligned.
+ */
+gdn_status gdn_prefill_chunked(const gdn_layer* layer, const gdn_pool* pool,
+                               const int32_t* dst_slots, const int32_t* init_slot, int32_t N,
+                               const int32_t* cu_seqlens, int32_t max_seqlen,
+                               int32_t total_tokens, int32_t chunk, const gdn_inputs* in,
+                               float* out, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* Bytes of workspace gdn_prefill_chunked needs for these sizes (0 on bad args). */
+size_t gdn_prefill_workspace_size(const gdn_layer* layer, int32_t N, int32_t max_seqlen,
+                                  int32_t total_tokens, int32_t chunk);
+
+/*
+ * Copy-on-write of n slots ("Riesgo de correctitud": a fresh working slot is
+ * made clean by copying a known-clean checkpoint): dst[i] <- src[i], both
+ * pools, bitwise.  src / dst [n] int32 (device).  The dst slots must be
+ * distinct and must not appear among the src slots.
+ */
+gdn_status gdn_slot_copy(const gdn_layer* layer, const gdn_pool* pool, const int32_t* src,
+                         const int32_t* dst, int32_t n, void* stream);
+
+/*
+ * Explicit zeroing of n slots ("Riesgo de correctitud": the other way to make
+ * a fresh working slot clean): ssm and conv rows <- +0.0.  idx [n] (device).
+ */
+gdn_status gdn_slot_zero(const gdn_layer* layer, const gdn_pool* pool, const int32_t* idx,
+                         int32_t n, void* stream);
+
+/* Static string for a status code (never NULL). */
+const char* gdn_status_string(gdn_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H */

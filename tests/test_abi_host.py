@@ -1,0 +1,113 @@
+"""libgdn loads without a GPU, exports every symbol include/gdn.h declares,
+and rejects bad arguments on the host before anything is enqueued.  No call
+here reaches a HIP API: every case returns during validation (or is B = 0)."""
+import ctypes as ct
+import os
+import re
+
+import pytest
+
+import hybrid_linear_attention_decode_amd as gdn
+from hybrid_linear_attention_decode_amd import GdnInputs, GdnLayer, GdnPool, GdnSpecCache
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    syms = declared_symbols()
+    assert set(syms) == set(gdn.EXPORTED)
+    L = gdn.lib()
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def test_status_strings():
+    for st in range(7):
+        assert gdn.gdn_status_string(st)
+    assert gdn.gdn_status_string(99) == "unknown status"
+
+
+FAKE = ct.c_void_p(0x10000)  # never dereferenced: every call below fails validation
+
+
+def qwen_layer(**kw):
+    d = dict(n_k_heads=16, n_v_heads=32, d_k=128, d_v=128, conv_width=4)
+    d.update(kw)
+    return gdn.Layer(**d).c_struct()
+
+
+def decode(L, pool=None, idx=FAKE, B=4, T=1, inp=None, out=FAKE, spec=None):
+    pool = pool or GdnPool(FAKE, FAKE, 8)
+    inp = inp or GdnInputs(FAKE, FAKE, FAKE, FAKE, None)
+    return gdn.lib().gdn_decode_step(ct.byref(L), ct.byref(pool), idx, B, T, ct.byref(inp),
+                                     out, spec, None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_v_heads", 24, gdn.GDN_ERR_BAD_SHAPE),      # 24 % 16 != 0
+    ("n_k_heads", 0, gdn.GDN_ERR_BAD_SHAPE),
+    ("d_k", 96, gdn.GDN_ERR_UNSUPPORTED),
+    ("d_v", 40, gdn.GDN_ERR_UNSUPPORTED),
+    ("d_v", 512, gdn.GDN_ERR_UNSUPPORTED),
+    ("conv_width", 0, gdn.GDN_ERR_BAD_SHAPE),
+    ("conv_width", 5, gdn.GDN_ERR_UNSUPPORTED),
+    ("gate", 7, gdn.GDN_ERR_BAD_DTYPE),
+    ("act_dtype", 3, gdn.GDN_ERR_BAD_DTYPE),
+    ("flags", 8, gdn.GDN_ERR_BAD_SHAPE),
+])
+def test_bad_layer(field, value, status):
+    L = qwen_layer()
+    setattr(L, field, value)
+    assert decode(L) == status
+
+
+def test_bad_decode_arguments():
+    L = qwen_layer()
+    assert gdn.lib().gdn_decode_step(None, None, FAKE, 1, 1, None, FAKE, None, None) == \
+        gdn.GDN_ERR_NULL_ARG
+    assert decode(L, pool=GdnPool(None, FAKE, 8)) == gdn.GDN_ERR_NULL_ARG
+    assert decode(L, pool=GdnPool(FAKE, None, 8)) == gdn.GDN_ERR_NULL_ARG
+    assert decode(L, idx=None) == gdn.GDN_ERR_NULL_ARG
+    assert decode(L, out=None) == gdn.GDN_ERR_NULL_ARG
+    assert decode(L, inp=GdnInputs(FAKE, None, FAKE, FAKE, None)) == gdn.GDN_ERR_NULL_ARG
+    assert decode(L, T=0) == gdn.GDN_ERR_BAD_SHAPE
+    assert decode(L, B=-1) == gdn.GDN_ERR_BAD_SHAPE
+    assert decode(L, B=70000) == gdn.GDN_ERR_BAD_SHAPE
+    assert decode(L, pool=GdnPool(ct.c_void_p(0x10004), FAKE, 8)) == gdn.GDN_ERR_BAD_SHAPE
+    spec = GdnSpecCache(FAKE, FAKE, 3)
+    assert decode(L, T=4, spec=ct.byref(spec)) == gdn.GDN_ERR_BAD_SHAPE   # T > t_max
+    spec0 = GdnSpecCache(None, FAKE, 7)
+    assert decode(L, T=4, spec=ct.byref(spec0)) == gdn.GDN_ERR_NULL_ARG
+    # a conv-less layer (W = 1) needs no conv pool; B = 0 enqueues nothing
+    L1 = qwen_layer(conv_width=1)
+    assert decode(L1, pool=GdnPool(FAKE, None, 8), B=0) == gdn.GDN_OK
+
+
+def test_bad_slot_and_commit_arguments():
+    L = qwen_layer()
+    pool = GdnPool(FAKE, FAKE, 8)
+    lib = gdn.lib()
+    assert lib.gdn_slot_copy(ct.byref(L), ct.byref(pool), None, FAKE, 2, None) == \
+        gdn.GDN_ERR_NULL_ARG
+    assert lib.gdn_slot_copy(ct.byref(L), ct.byref(pool), FAKE, FAKE, -1, None) == \
+        gdn.GDN_ERR_BAD_SHAPE
+    assert lib.gdn_slot_zero(ct.byref(L), ct.byref(pool), None, 3, None) == gdn.GDN_ERR_NULL_ARG
+    assert lib.gdn_slot_zero(ct.byref(L), ct.byref(pool), None, 0, None) == gdn.GDN_OK
+    assert lib.gdn_spec_decode_commit(ct.byref(L), ct.byref(pool), FAKE, None, FAKE, 4,
+                                      None) == gdn.GDN_ERR_NULL_ARG
+    bad_spec = GdnSpecCache(FAKE, FAKE, 0)
+    assert lib.gdn_spec_decode_commit(ct.byref(L), ct.byref(pool), FAKE, ct.byref(bad_spec),
+                                      FAKE, 4, None) == gdn.GDN_ERR_BAD_SHAPE
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(gdn, "_lib", None)
+    monkeypatch.setattr(gdn, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        gdn.lib()

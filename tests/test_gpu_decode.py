@@ -1,0 +1,330 @@
+"""GPU parity of the decode path, the speculative snapshots/commit and the slot
+operations, through the C ABI, against the fp64 oracle on the same seeded
+inputs.  Bar: outputs max|do|/max|o| <= 2e-3; final state <= 1e-4 after 16
+fp32 steps; slot indexing, copy, zero and rollback bit-exact."""
+import numpy as np
+import pytest
+
+import oracle
+import hybrid_linear_attention_decode_amd as gdn
+from hybrid_linear_attention_decode_amd import synth
+from tests.harness import OUT_TOL, STATE_TOL_16, bits, dev, host, layers, rel_err, shadow
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    return torch
+
+
+class DevCase:
+    """Device copies of a seeded decode case."""
+
+    def __init__(self, case: synth.DecodeCase):
+        self.ssm = dev(case.pool.ssm)
+        self.conv = dev(case.pool.conv)
+        self.w = dev(case.conv_w)
+        self.case = case
+
+    def call(self, g, c, out=None, spec=None, idx=None):
+        cs = self.case
+        ix = dev(cs.indices[c] if idx is None else idx)
+        spec_ssm, spec_conv = spec if spec is not None else (None, None)
+        return gdn.gdn_decode_step(g, self.ssm, self.conv, ix, dev(cs.x[c]), dev(cs.alpha[c]),
+                                   dev(cs.beta[c]), self.w, out=out, spec_ssm=spec_ssm,
+                                   spec_conv=spec_conv)
+
+
+def run_oracle(o, case, s64, c64, calls, T=None):
+    outs = []
+    for c in calls:
+        outs.append(oracle.decode(o, s64, c64, case.indices[c], case.x[c], case.alpha[c],
+                                  case.beta[c], case.conv_w))
+    return outs
+
+
+def test_tiny_fp32_16_steps():
+    """Tiny GDN decode: B=1, 2/2 heads, d=16, 96 channels, pool 4, 16 steps,
+    fp32 throughout.  State within 1e-4 after 16 steps; other slots untouched."""
+    torch = _torch()
+    case = synth.decode_case(synth.TINY, B=1, T=1, num_slots=4, n_calls=16, seed=0, rotate=False)
+    g, o = layers(synth.TINY)
+    d = DevCase(case)
+    before = bits(d.ssm), bits(d.conv)
+    outs = [host(d.call(g, c)) for c in range(16)]
+    torch.cuda.synchronize()
+    s64, c64 = shadow(case.pool)
+    refs = run_oracle(o, case, s64, c64, range(16))
+    for c in range(16):
+        assert rel_err(outs[c], refs[c]) <= OUT_TOL
+    slot = int(case.indices[0, 0])
+    assert rel_err(host(d.ssm)[slot], s64[slot]) <= STATE_TOL_16
+    np.testing.assert_array_equal(host(d.conv)[slot], c64[slot].astype(np.float32))
+    others = [s for s in range(4) if s != slot]
+    np.testing.assert_array_equal(bits(d.ssm)[others], before[0][others])
+    np.testing.assert_array_equal(bits(d.conv)[others], before[1][others])
+
+
+def test_tiny_multi_token_call_equals_single_steps_bitwise():
+    case = synth.decode_case(synth.TINY, B=1, T=1, num_slots=4, n_calls=16, seed=0, rotate=False)
+    g, _ = layers(synth.TINY)
+    a, b = DevCase(case), DevCase(case)
+    outs = [a.call(g, c) for c in range(16)]
+    torch = _torch()
+    x = dev(case.x[:, 0, 0][None])                       # [1, 16, C]
+    al = dev(case.alpha[:, 0, 0][None])
+    be = dev(case.beta[:, 0, 0][None])
+    o16 = gdn.gdn_decode_step(g, b.ssm, b.conv, dev(case.indices[0]), x, al, be, b.w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(o16)[0], np.stack([bits(t)[0, 0] for t in outs]))
+    np.testing.assert_array_equal(bits(a.ssm), bits(b.ssm))
+    np.testing.assert_array_equal(bits(a.conv), bits(b.conv))
+
+
+@pytest.mark.parametrize("n_calls", [1000])
+def test_qwen35_b16_full_run(n_calls):
+    """Qwen3.5-shaped layer: B=16, 16/32 heads, d=128, 8192 channels, bf16
+    inputs, fp32 state, pool 256 with rotating distinct indices, T=1, every
+    output of every call against the oracle, then the final pool."""
+    torch = _torch()
+    case = synth.decode_case(synth.QWEN35, B=16, T=1, num_slots=256, n_calls=n_calls, seed=1)
+    g, o = layers(synth.QWEN35)
+    d = DevCase(case)
+    out = torch.empty((n_calls, 16, 1, 32, 128), dtype=torch.float32, device="cuda")
+    x, al, be, ix = dev(case.x), dev(case.alpha), dev(case.beta), dev(case.indices)
+    for c in range(n_calls):
+        gdn.gdn_decode_step(g, d.ssm, d.conv, ix[c], x[c], al[c], be[c], d.w, out=out[c])
+    torch.cuda.synchronize()
+    got = host(out)
+    s64, c64 = shadow(case.pool)
+    worst = 0.0
+    for c in range(n_calls):
+        ref = oracle.decode(o, s64, c64, case.indices[c], case.x[c], case.alpha[c],
+                            case.beta[c], case.conv_w)
+        worst = max(worst, rel_err(got[c], ref))
+    print(f"qwen35 B=16 x {n_calls} calls: worst max|do|/max|o| = {worst:.3e}")
+    assert worst <= OUT_TOL
+    live = np.unique(case.indices)
+    assert rel_err(host(d.ssm)[live], s64[live]) <= OUT_TOL
+    np.testing.assert_array_equal(host(d.conv)[live],
+                                  synth.f32_to_bf16_bits(c64[live].astype(np.float32)))
+
+
+@pytest.mark.parametrize("shape,B", [(synth.QWEN35, 64), (synth.TINY, 64)])
+def test_spec_draft_commit_equals_recomputation(shape, B):
+    """Speculative decode commit: 7 draft tokens per request, snapshots into
+    spec_cache, accepted length uniform in 0..7, commit; each working slot is
+    bit-exact versus an in-place decode of only the accepted prefix, and the
+    draft outputs match the oracle."""
+    torch = _torch()
+    T, slots = 7, (1024 if shape is synth.QWEN35 else 256)
+    case = synth.decode_case(shape, B=B, T=T, num_slots=slots, n_calls=1, seed=2)
+    acc = synth.accepted_lengths(B, T, seed=2)
+    assert acc.min() == 0 and acc.max() == T
+    g, o = layers(shape)
+    a, r = DevCase(case), DevCase(case)
+    pre_ssm, pre_conv = bits(a.ssm), bits(a.conv)
+    sp_ssm = torch.full((B, T) + tuple(a.ssm.shape[1:]), float("nan"), device="cuda")
+    sp_conv = torch.zeros((B, T) + tuple(a.conv.shape[1:]), dtype=a.conv.dtype, device="cuda")
+    out = a.call(g, 0, spec=(sp_ssm, sp_conv))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(a.ssm), pre_ssm)           # draft leaves the pool
+    np.testing.assert_array_equal(bits(a.conv), pre_conv)
+    gdn.gdn_spec_decode_commit(g, a.ssm, a.conv, dev(case.indices[0]), sp_ssm, sp_conv, dev(acc))
+    # recomputation: requests grouped by accepted length, in-place decode of L tokens
+    for L in range(1, T + 1):
+        sel = np.nonzero(acc == L)[0]
+        if sel.size == 0:
+            continue
+        o_r = gdn.gdn_decode_step(g, r.ssm, r.conv, dev(case.indices[0][sel]),
+                                  dev(case.x[0][sel, :L]), dev(case.alpha[0][sel, :L]),
+                                  dev(case.beta[0][sel, :L]), r.w)
+        np.testing.assert_array_equal(bits(o_r), bits(out)[sel, :L])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(a.ssm), bits(r.ssm))
+    np.testing.assert_array_equal(bits(a.conv), bits(r.conv))
+    # draft outputs and snapshots against the oracle
+    s64, c64 = shadow(case.pool)
+    sp64 = np.zeros((B, T) + s64.shape[1:])
+    spc64 = np.zeros((B, T) + c64.shape[1:])
+    ref = oracle.decode(o, s64, c64, case.indices[0], case.x[0], case.alpha[0], case.beta[0],
+                        case.conv_w, spec_ssm=sp64, spec_conv=spc64)
+    assert rel_err(host(out), ref) <= OUT_TOL
+    assert rel_err(host(sp_ssm), sp64) <= OUT_TOL
+    got_c = host(sp_conv)
+    want_c = spc64.astype(np.float32)
+    if shape.dtype == "bf16":
+        want_c = synth.f32_to_bf16_bits(want_c)
+    np.testing.assert_array_equal(got_c, want_c)
+
+
+def test_slot_zero_copy_bitwise_and_isolated():
+    torch = _torch()
+    shape = synth.QWEN35
+    rs = synth.streams(7)
+    pool = synth.make_pool(shape, 24, np.arange(24), rs)
+    g, _ = layers(shape)
+    ssm, conv = dev(pool.ssm), dev(pool.conv)
+    s0, c0 = bits(ssm), bits(conv)
+    src = np.array([3, 11, 20], np.int32)
+    dst = np.array([7, 0, 15], np.int32)
+    gdn.gdn_slot_copy(g, ssm, conv, dev(src), dev(dst))
+    zi = np.array([5, -1, 23, 999], np.int32)               # pad and out-of-range skipped
+    gdn.gdn_slot_zero(g, ssm, conv, dev(zi))
+    torch.cuda.synchronize()
+    s1, c1 = bits(ssm), bits(conv)
+    for a_, b_ in zip(src, dst):
+        np.testing.assert_array_equal(s1[b_], s0[a_])
+        np.testing.assert_array_equal(c1[b_], c0[a_])
+    for z in (5, 23):
+        assert not s1[z].any() and not c1[z].any()          # +0.0 bit patterns
+    untouched = [k for k in range(24) if k not in (7, 0, 15, 5, 23)]
+    np.testing.assert_array_equal(s1[untouched], s0[untouched])
+    np.testing.assert_array_equal(c1[untouched], c0[untouched])
+
+
+def test_beta0_alpha1_state_unchanged_bitwise():
+    torch = _torch()
+    case = synth.decode_case(synth.QWEN35, B=8, T=3, num_slots=16, n_calls=1, seed=8)
+    g, _ = layers(synth.QWEN35)
+    d = DevCase(case)
+    s0 = bits(d.ssm)
+    ones = synth.f32_to_bf16_bits(np.ones(case.alpha.shape[1:], np.float32))
+    zeros = synth.f32_to_bf16_bits(np.zeros(case.beta.shape[1:], np.float32))
+    gdn.gdn_decode_step(g, d.ssm, d.conv, dev(case.indices[0]), dev(case.x[0]), dev(ones),
+                        dev(zeros), d.w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(d.ssm), s0)
+
+
+def test_skipped_rows_and_permutation_bitwise():
+    """Negative (pad) and out-of-range indices leave rows untouched; permuting
+    requests and their slots permutes the results bit for bit."""
+    torch = _torch()
+    case = synth.decode_case(synth.QWEN35, B=6, T=2, num_slots=16, n_calls=1, seed=9)
+    g, _ = layers(synth.QWEN35)
+    idx = case.indices[0].copy()
+    idx[1], idx[4] = -1, 16                                 # pad row, out-of-range row
+    a, b = DevCase(case), DevCase(case)
+    s0 = bits(a.ssm)
+    out_a = torch.full((6, 2, 32, 128), 7.0, device="cuda")
+    a.call(g, 0, out=out_a, idx=idx)
+    p = np.array([3, 5, 0, 2, 1, 4])
+    out_b = torch.full((6, 2, 32, 128), 7.0, device="cuda")
+    gdn.gdn_decode_step(g, b.ssm, b.conv, dev(idx[p]), dev(case.x[0][p]), dev(case.alpha[0][p]),
+                        dev(case.beta[0][p]), b.w, out=out_b)
+    torch.cuda.synchronize()
+    oa = host(out_a)
+    assert (oa[1] == 7.0).all() and (oa[4] == 7.0).all()
+    np.testing.assert_array_equal(bits(out_a)[p], bits(out_b))
+    np.testing.assert_array_equal(bits(a.ssm), bits(b.ssm))
+    np.testing.assert_array_equal(bits(a.conv), bits(b.conv))
+    touched = set(int(i) for i in idx if 0 <= i < 16)
+    for k in range(16):
+        if k not in touched:
+            np.testing.assert_array_equal(bits(a.ssm)[k], s0[k])
+
+
+def test_poisoned_fresh_slots_clean_after_zero_or_cow():
+    """NaN-poisoned free slots never leak after explicit zeroing or CoW from a
+    clean checkpoint; CoW-then-decode equals decoding the checkpoint's state."""
+    torch = _torch()
+    shape = synth.QWEN35
+    case = synth.decode_case(shape, B=4, T=2, num_slots=12, n_calls=1, seed=10)
+    g, o = layers(shape)
+    d = DevCase(case)
+    live = case.pool.live
+    fresh = np.array([s for s in range(12) if s not in set(live.tolist())][:4], np.int32)
+    assert np.isnan(host(d.ssm)[fresh]).all()
+    gdn.gdn_slot_zero(g, d.ssm, d.conv, dev(fresh[:2]))
+    gdn.gdn_slot_copy(g, d.ssm, d.conv, dev(live[:2]), dev(fresh[2:]))
+    out = d.call(g, 0, idx=fresh)
+    torch.cuda.synchronize()
+    assert np.isfinite(host(out)).all()
+    assert np.isfinite(host(d.ssm)[fresh]).all()
+    s64, c64 = shadow(case.pool)
+    s64[fresh[:2]] = 0.0
+    c64[fresh[:2]] = 0.0
+    s64[fresh[2:]] = s64[live[:2]]
+    c64[fresh[2:]] = c64[live[:2]]
+    ref = oracle.decode(o, s64, c64, fresh, case.x[0], case.alpha[0], case.beta[0], case.conv_w)
+    assert rel_err(host(out), ref) <= OUT_TOL
+
+
+@pytest.mark.parametrize("kw", [
+    dict(shape=synth.Shape(4, 16, 64, 32, 2, "scalar", "f32"), layer=dict(conv_silu=False)),
+    dict(shape=synth.Shape(2, 2, 32, 48, 1, "channel", "bf16"), layer=dict(l2norm=False)),
+    dict(shape=synth.Shape(1, 4, 16, 64, 3, "channel", "f32"), layer=dict(q_scale=0.5)),
+    dict(shape=synth.Shape(8, 8, 128, 256, 4, "scalar", "bf16"), layer=dict()),
+])
+def test_other_shapes_against_oracle(kw):
+    """d_k in {16, 32, 64, 128}, d_v != d_k, GQA 1:1 / 2:1 / 4:1, conv widths
+    1-4, both gates and dtypes, flags off; 5 steps of T=2."""
+    torch = _torch()
+    shape = kw["shape"]
+    case = synth.decode_case(shape, B=3, T=2, num_slots=8, n_calls=5, seed=11)
+    g, o = layers(shape, **kw["layer"])
+    d = DevCase(case)
+    outs = [d.call(g, c) for c in range(5)]
+    torch.cuda.synchronize()
+    s64, c64 = shadow(case.pool)
+    refs = run_oracle(o, case, s64, c64, range(5))
+    for c in range(5):
+        assert rel_err(host(outs[c]), refs[c]) <= OUT_TOL
+    live = case.pool.live
+    assert rel_err(host(d.ssm)[live], s64[live]) <= STATE_TOL_16
+
+
+def test_kda_decode_with_slot_prep():
+    """KDA-style decode (per-channel gate), 32/32 heads, d=128: a quarter of the
+    requests on zeroed fresh slots, a quarter CoW from checkpoints, then decode;
+    3 steps against the oracle."""
+    torch = _torch()
+    shape = synth.KDA
+    B, slots = 16, 64
+    case = synth.decode_case(shape, B=B, T=1, num_slots=slots, n_calls=3, seed=4,
+                             all_live=True, rotate=False)
+    g, o = layers(shape)
+    d = DevCase(case)
+    idx = case.indices[0]
+    fresh, cow = idx[:4], idx[4:8]
+    ckpt = np.array([s for s in range(slots) if s not in set(idx.tolist())][:4], np.int32)
+    # poison the fresh slots first, as a recycled slot would be
+    d.ssm[dev(fresh).long()] = float("nan")
+    gdn.gdn_slot_zero(g, d.ssm, d.conv, dev(fresh))
+    gdn.gdn_slot_copy(g, d.ssm, d.conv, dev(ckpt), dev(cow))
+    outs = [d.call(g, c) for c in range(3)]
+    torch.cuda.synchronize()
+    s64, c64 = shadow(case.pool)
+    oracle.slot_zero(o, s64, c64, fresh)
+    oracle.slot_copy(o, s64, c64, ckpt, cow)
+    refs = run_oracle(o, case, s64, c64, range(3))
+    for c in range(3):
+        assert rel_err(host(outs[c]), refs[c]) <= OUT_TOL
+    assert rel_err(host(d.ssm)[idx], s64[idx]) <= OUT_TOL
+
+
+def test_64bit_offsets_top_slots():
+    """A pool above 2 GiB (1100 Qwen3.5 slots, 2.3 GB): the top slots are
+    addressed correctly (byte offsets beyond int32)."""
+    torch = _torch()
+    shape = synth.QWEN35
+    n = 1100
+    g, o = layers(shape)
+    rs = synth.streams(12)
+    top = np.array([1099, 1024], np.int32)
+    small = synth.make_pool(shape, 2, np.arange(2), rs)
+    ssm = torch.zeros((n, 32, 128, 128), dtype=torch.float32, device="cuda")
+    conv = torch.zeros((n, 3, shape.channels), dtype=torch.bfloat16, device="cuda")
+    ssm[dev(top).long()] = dev(small.ssm)
+    conv[dev(top).long()] = dev(small.conv)
+    x, al, be = synth.make_tokens(shape, (2, 1), rs)
+    w = synth.make_conv_w(shape, rs)
+    out = gdn.gdn_decode_step(g, ssm, conv, dev(top), dev(x), dev(al), dev(be), dev(w))
+    torch.cuda.synchronize()
+    s64, c64 = shadow(small)
+    ref = oracle.decode(o, s64, c64, np.array([0, 1], np.int32), x, al, be, w)
+    assert rel_err(host(out), ref) <= OUT_TOL
+    assert rel_err(host(ssm[dev(top).long()]), s64) <= OUT_TOL
+    assert float(ssm[:1024].abs().sum()) == 0.0 and float(ssm[1025:1099].abs().sum()) == 0.0
