@@ -97,8 +97,10 @@ gdn_status gdn_decode_step(const gdn_layer* L, const gdn_pool* P, const int32_t*
     if (T > spec->t_max) return GDN_ERR_BAD_SHAPE;
   }
   const int G = L->n_v_heads / L->n_k_heads;
-  if (!gdn::decode_rows_per_lane(L->d_k, G * L->d_v, 2 * L->d_k + G * L->d_v))
+  if (!gdn::decode_rows_per_wave(L->d_k, G, L->d_v, L->conv_width - 1,
+                                 L->gate == GDN_GATE_CHANNEL))
     return GDN_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(B) * L->n_k_heads > INT32_MAX) return GDN_ERR_BAD_SHAPE;
   if (B == 0) return GDN_OK;
 
   DecodeArgs a{};

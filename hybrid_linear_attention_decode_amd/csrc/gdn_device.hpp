@@ -50,22 +50,76 @@ constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within 8 lanes
 
-// Sum over aligned groups of N lanes (N = 4 or 8); every lane of the group
+constexpr int kDppRowMirror = 0x140;  // lane i <- lane 15-i within 16 lanes
+
+// Sum over aligned groups of N lanes (N = 4, 8 or 16); every lane of the group
 // ends with the same bits (each step adds a commuted pair).
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
-  static_assert(N == 4 || N == 8, "group of 4 or 8 lanes");
+  static_assert(N == 4 || N == 8 || N == 16, "group of 4, 8 or 16 lanes");
   v = v + dpp<kDppQuadXor1>(v);
   v = v + dpp<kDppQuadXor2>(v);
-  if constexpr (N == 8) v = v + dpp<kDppHalfMirror>(v);
+  if constexpr (N >= 8) v = v + dpp<kDppHalfMirror>(v);
+  if constexpr (N == 16) v = v + dpp<kDppRowMirror>(v);
   return v;
 }
 
-// Butterfly sum over the 64 lanes of a wave; identical bits in every lane.
+// Sum over the 64 lanes of a wave: DPP sums inside each row of 16 lanes, then
+// the four row sums read into scalars and added in a fixed order, so every
+// lane (and every wave summing the same data) gets the same bits.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = v + __shfl_xor(v, m, 64);
-  return v;
+  v = group_sum<16>(v);
+  const int iv = __float_as_int(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(iv, 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(iv, 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(iv, 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(iv, 48));
+  return (r0 + r1) + (r2 + r3);
 }
+
+// Copies global -> LDS without registers (gfx950 global_load_lds).  The LDS
+// address is wave-uniform; each active lane writes at lds + 4*lane (SIZE 2
+// or 4: one zero-extended dword per lane) or lds + 16*lane (SIZE 16).
+// Counted by the vector-memory counter like a load; the compiler does not
+// order later LDS reads after it -- see vm_wait.
+#define GDN_LDS_DMA(SRC, LDS, SIZE, AUX)                                                 \
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(SRC), \
+                                   (__attribute__((address_space(3))) void*)(LDS), SIZE, 0, AUX)
+template <int SIZE>
+__device__ __forceinline__ void lds_dma(const void* src, void* lds);
+template <>
+__device__ __forceinline__ void lds_dma<2>(const void* src, void* lds) {
+  GDN_LDS_DMA(src, lds, 2, 0);
+}
+template <>
+__device__ __forceinline__ void lds_dma<4>(const void* src, void* lds) {
+  GDN_LDS_DMA(src, lds, 4, 0);
+}
+template <>
+__device__ __forceinline__ void lds_dma<16>(const void* src, void* lds) {
+  GDN_LDS_DMA(src, lds, 16, 2 /* non-temporal */);
+}
+#undef GDN_LDS_DMA
+__device__ __forceinline__ void lds_dma16(const float* src, float* lds) { lds_dma<16>(src, lds); }
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+// It also keeps the compiler from moving memory accesses across it.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Wait for this wave's LDS operations.
+__device__ __forceinline__ void lgkm_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier for LDS traffic only: this wave's LDS accesses complete,
+// then all waves meet.  Unlike __syncthreads() it does not wait for global
+// memory (or the LDS copies in flight), which keep streaming across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// A value the compiler may keep in a scalar register (it is wave-uniform).
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 }  // namespace gdn

@@ -12,6 +12,7 @@ namespace gdn {
 struct DecodeArgs {
   int32_t Hk, Hv, dv, W, C, G;
   int32_t B, T;
+  int32_t tchunk;             // tokens prepared per LDS chunk (1..T)
   int64_t num_slots;
   int32_t silu, l2norm;
   float q_scale, eps;
@@ -51,8 +52,7 @@ enum SlotMode { kSlotCopy = 0, kSlotZero = 1, kSlotCommit = 2 };
 hipError_t launch_decode(const DecodeArgs& a, int dk, int act_bf16, int kda, hipStream_t s);
 hipError_t launch_slots(const SlotArgs& a, SlotMode mode, hipStream_t s);
 
-// Rows-per-lane choice of the decode kernel for a shape; 0 when unsupported.
-int decode_rows_per_lane(int dk, int rows_per_group, int channels_per_group);
-int decode_threads(int dk, int nr, int rows_per_group);
+// Rows of state per wave of the decode kernel for a shape; 0 when unsupported.
+int decode_rows_per_wave(int dk, int G, int dv, int W1, int kda);
 
 }  // namespace gdn

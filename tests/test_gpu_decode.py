@@ -195,7 +195,14 @@ def test_beta0_alpha1_state_unchanged_bitwise():
     gdn.gdn_decode_step(g, d.ssm, d.conv, dev(case.indices[0]), dev(case.x[0]), dev(ones),
                         dev(zeros), d.w)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(bits(d.ssm), s0)
+    # equal as values: the fp32 normal draw holds a few exact zeros, and an
+    # added signed-zero update may turn -0.0 into +0.0 (still equal)
+    live = case.indices[0]
+    np.testing.assert_array_equal(host(d.ssm)[live], case.pool.ssm[live])
+    nz = case.pool.ssm[live] != 0
+    np.testing.assert_array_equal(bits(d.ssm)[live][nz], s0[live][nz])
+    rest = np.setdiff1d(np.arange(16), live)
+    np.testing.assert_array_equal(bits(d.ssm)[rest], s0[rest])
 
 
 def test_skipped_rows_and_permutation_bitwise():
