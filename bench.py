@@ -33,7 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
-DECODE_KERNEL = "decode_kernel<128, 4, bf16, false>"
+DECODE_KERNEL = "decode_kernel<128, 32, bf16, false>"
 
 
 def log(msg: str):
@@ -76,16 +76,18 @@ def traffic_from_profile(kernel_src: str):
 # ----------------------------------------------------------------------------
 
 class DecodeBench:
-    """Pre-built C-ABI argument blocks for back-to-back decode calls, so the
-    host loop issues launches far faster than the GPU retires them."""
+    """Device pools, inputs and pre-built C-ABI argument blocks for
+    back-to-back decode calls, so the host loop issues launches far faster
+    than the GPU retires them.  The pool holds n_distinct_slots seeded slot
+    states replicated over all slots (values do not change the traffic)."""
 
     def __init__(self, torch, gdn, synth, shape, B, slots, n_calls, seed, n_inputs=64,
-                 n_distinct_slots=64):
+                 n_distinct_slots=64, T=1, spec=False):
         self.torch = torch
         rs = synth.streams(seed)
         base = synth.make_pool(shape, n_distinct_slots, np.arange(n_distinct_slots), rs)
         self.w_host = synth.make_conv_w(shape, rs)
-        x, al, be = synth.make_tokens(shape, (n_inputs, B, 1), rs)
+        x, al, be = synth.make_tokens(shape, (n_inputs, B, T), rs)
         self.idx_host = synth.rotating_indices(slots, B, n_calls, rs["indices"])
         self.inputs_host = (x, al, be)
         self.base = base
@@ -96,7 +98,7 @@ class DecodeBench:
         self.w = dev(self.w_host)
         self.x, self.al, self.be = dev(x), dev(al), dev(be)
         self.idx = dev(self.idx_host)
-        self.out = torch.empty((B, 1, shape.n_v_heads, shape.d_v), dtype=torch.float32,
+        self.out = torch.empty((B, T, shape.n_v_heads, shape.d_v), dtype=torch.float32,
                                device="cuda")
         self.g = gdn.Layer(shape.n_k_heads, shape.n_v_heads, shape.d_k, shape.d_v,
                            shape.conv_width, shape.gate, shape.dtype)
@@ -104,7 +106,7 @@ class DecodeBench:
         self.P = gdn.GdnPool(self.ssm.data_ptr(), self.conv.data_ptr(), slots)
         self.fn = gdn.lib().gdn_decode_step
         self.stream = ct.c_void_p(torch.cuda.current_stream().cuda_stream)
-        self.B = B
+        self.B, self.T = B, T
         self.n_inputs = n_inputs
         self.inputs = [gdn.GdnInputs(self.x[i].data_ptr(), self.al[i].data_ptr(),
                                      self.be[i].data_ptr(), self.w.data_ptr(), None)
@@ -113,10 +115,18 @@ class DecodeBench:
         self.out_ptr = ct.c_void_p(self.out.data_ptr())
         self.Lref, self.Pref = ct.byref(self.L), ct.byref(self.P)
         self.inref = [ct.byref(i) for i in self.inputs]
+        self.spec = None
+        if spec:
+            self.spec_ssm = torch.empty((B, T) + tuple(self.ssm.shape[1:]), dtype=torch.float32,
+                                        device="cuda")
+            self.spec_conv = torch.empty((B, T) + tuple(self.conv.shape[1:]),
+                                         dtype=self.conv.dtype, device="cuda")
+            self.S = gdn.GdnSpecCache(self.spec_ssm.data_ptr(), self.spec_conv.data_ptr(), T)
+            self.spec = ct.byref(self.S)
 
     def call(self, c: int):
-        st = self.fn(self.Lref, self.Pref, self.idx_ptrs[c], self.B, 1,
-                     self.inref[c % self.n_inputs], self.out_ptr, None, self.stream)
+        st = self.fn(self.Lref, self.Pref, self.idx_ptrs[c], self.B, self.T,
+                     self.inref[c % self.n_inputs], self.out_ptr, self.spec, self.stream)
         if st != 0:
             raise RuntimeError(f"gdn_decode_step failed with status {st}")
 
@@ -172,6 +182,120 @@ def cpu_baseline(synth, shape, bench: DecodeBench, budget_s: float):
                       f"(fp64 oracle, {nthreads} threads, {dt:.1f} s)"}
 
 
+def path_record(ms_per_call: float, nbytes: float, tokens: int, what: str) -> dict:
+    gbs = nbytes / (ms_per_call * 1e-3) / 1e9
+    return {"what": what, "us_per_call": round(ms_per_call * 1e3, 2),
+            "tokens_per_s": round(tokens / (ms_per_call * 1e-3), 1),
+            "algorithmic_bytes": int(nbytes), "hbm_gbps": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def bench_decode_b16(torch, gdn, synth, K=500, W=50):
+    """Qwen3.5-shaped decode at B=16 on a 256-slot pool (reuse after 15 calls)."""
+    shape = synth.QWEN35
+    b = DecodeBench(torch, gdn, synth, shape, 16, 256, W + K, seed=1)
+    for c in range(W):
+        b.call(c)
+    ms = time_calls(torch, b.call, W, K) / K
+    return path_record(ms, decode_bytes(shape, 16), 16,
+                       "GDN decode, Qwen3.5 shape, B=16, T=1, pool 256")
+
+
+def bench_spec(torch, gdn, synth, K=100, W=10):
+    """Speculative draft of 7 tokens for B=64 into spec_cache (working slots
+    untouched), then the commit of accepted lengths ~ U{0..7}."""
+    shape = synth.QWEN35
+    B, T = 64, 7
+    b = DecodeBench(torch, gdn, synth, shape, B, 1024, W + K, seed=2, n_inputs=8, T=T, spec=True)
+    for c in range(W):
+        b.call(c)
+    ms_draft = time_calls(torch, b.call, W, K) / K
+    draft = path_record(ms_draft, decode_bytes(shape, B, T, spec=True), B * T,
+                        "speculative draft, Qwen3.5 shape, B=64, 7 tokens, snapshots per token")
+    acc_host = synth.accepted_lengths(B, T, seed=2)
+    acc = torch.from_numpy(acc_host).cuda()
+    fn = gdn.lib().gdn_spec_decode_commit
+    acc_ptr = ct.c_void_p(acc.data_ptr())
+
+    def commit(c):
+        st = fn(b.Lref, b.Pref, b.idx_ptrs[c], b.spec, acc_ptr, B, b.stream)
+        if st != 0:
+            raise RuntimeError(f"gdn_spec_decode_commit failed with status {st}")
+    for c in range(W):
+        commit(c)
+    ms_commit = time_calls(torch, commit, W, K) / K
+    slot_bytes = shape.n_v_heads * shape.d_v * shape.d_k * 4 + \
+        (shape.conv_width - 1) * shape.channels * 2
+    commit_bytes = 2 * slot_bytes * int(np.count_nonzero(acc_host)) + 8 * B
+    rec = path_record(ms_commit, commit_bytes, int(acc_host.sum()),
+                      "commit of accepted lengths ~U{0..7}, B=64 (tokens = accepted)")
+    return draft, rec
+
+
+def bench_kda_stack(torch, gdn, synth, K=20, W=3, layers=48):
+    """KDA-style decode (per-channel gate), B=64, 32/32 heads, d=128, 48
+    layers each with its own 1024-slot pool.  A step: slot preparation in
+    every layer (16 fresh working slots zeroed, 16 copied from distinct
+    checkpoint slots), then the 48 decode calls back to back."""
+    shape = synth.KDA
+    B, slots = 64, 1024
+    base = DecodeBench(torch, gdn, synth, shape, B, slots, 1, seed=4, n_inputs=4)
+    rs = synth.streams(4)
+    roles = [rs["slot_roles"].permutation(slots).astype(np.int32) for _ in range(W + K)]
+    dev = _dev(torch)
+    idx = dev(np.stack([r[:64] for r in roles]))           # requests' working slots
+    fresh = dev(np.stack([r[:16] for r in roles]))
+    cow_dst = dev(np.stack([r[16:32] for r in roles]))
+    cow_src = dev(np.stack([r[64:80] for r in roles]))     # checkpoints, not in the batch
+    pools, convs, ws = [], [], []
+    for l in range(layers):
+        pools.append(base.ssm.clone())
+        convs.append(base.conv.clone())
+        ws.append(base.w)
+    lib = gdn.lib()
+    L = base.L
+    P = [gdn.GdnPool(pools[l].data_ptr(), convs[l].data_ptr(), slots) for l in range(layers)]
+    Pr = [ct.byref(p) for p in P]
+    ptr = lambda t: ct.c_void_p(t.data_ptr())
+    idx_p = [ptr(idx[c]) for c in range(W + K)]
+    fr_p = [ptr(fresh[c]) for c in range(W + K)]
+    dst_p = [ptr(cow_dst[c]) for c in range(W + K)]
+    src_p = [ptr(cow_src[c]) for c in range(W + K)]
+    Lr, stream = ct.byref(L), base.stream
+
+    def step(c):
+        for l in range(layers):
+            assert lib.gdn_slot_zero(Lr, Pr[l], fr_p[c], 16, stream) == 0
+            assert lib.gdn_slot_copy(Lr, Pr[l], src_p[c], dst_p[c], 16, stream) == 0
+        for l in range(layers):
+            assert lib.gdn_decode_step(Lr, Pr[l], idx_p[c], B, 1, base.inref[(c + l) % 4],
+                                       base.out_ptr, None, stream) == 0
+    for c in range(W):
+        step(c)
+    ms = time_calls(torch, step, W, K) / K
+    slot_bytes = shape.n_v_heads * shape.d_v * shape.d_k * 4 + \
+        (shape.conv_width - 1) * shape.channels * 2
+    prep_bytes = layers * (16 * slot_bytes + 16 * 2 * slot_bytes)
+    nbytes = layers * decode_bytes(shape, B) + prep_bytes
+    rec = path_record(ms, nbytes, B, "KDA decode stack: B=64, 32/32 heads, d=128, 48 layers, "
+                                     "per step 16 zeroed + 16 copied slots per layer")
+    rec["ms_per_step"] = rec.pop("us_per_call") / 1e3
+    rec["prep_bytes"] = int(prep_bytes)
+    del pools, convs
+    return rec
+
+
+def copy_calibration(torch, mib: int = 256, reps: int = 5):
+    """A plain device copy of known size, for scaling the PMC byte counters."""
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, device="cuda")
+    b = torch.empty(n, device="cuda")
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} copies of {mib} MiB (read {mib} MiB + write {mib} MiB each)")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +304,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["all", "decode", "paths", "copy"], default="all",
+                    help="profiling runs: just the headline decode, the other paths, or a "
+                         "plain copy of known size")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -197,6 +324,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     gdn.lib()
+    if args.only == "copy":
+        copy_calibration(torch)
+        return
+    if args.only == "paths":
+        for r in (bench_decode_b16(torch, gdn, synth), *bench_spec(torch, gdn, synth),
+                  bench_kda_stack(torch, gdn, synth)):
+            print(json.dumps(r), flush=True)
+        return
 
     shape = synth.QWEN35
     B, slots = 64, 1024
@@ -221,8 +356,17 @@ def main():
                 "traffic": traffic_from_profile(kernel_src), "kernel": DECODE_KERNEL,
                 "algorithmic_bytes_per_launch": nbytes}
 
+    paths = None
+    if args.only == "all":
+        log("bench: other paths (B=16 decode, speculative draft + commit, KDA 48-layer stack)")
+        d16 = bench_decode_b16(torch, gdn, synth)
+        draft, commit = bench_spec(torch, gdn, synth)
+        kda = bench_kda_stack(torch, gdn, synth)
+        paths = {"decode_qwen35_b16": d16, "spec_draft_qwen35_b64_t7": draft,
+                 "spec_commit_qwen35_b64": commit, "kda_stack_b64_48layers": kda}
+
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.only == "all":
         log("bench: timing the oracle sample")
         cpu = cpu_baseline(synth, shape, bench, args.cpu_budget)
 
@@ -247,6 +391,7 @@ def main():
         "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "paths": paths,
     }
     print(json.dumps(rec), flush=True)
 
