@@ -179,6 +179,7 @@ gdn_status gdn_slot_zero(const gdn_layer* L, const gdn_pool* P, const int32_t* i
 
 size_t gdn_prefill_workspace_size(const gdn_layer* L, int32_t N, int32_t max_seqlen,
                                   int32_t total_tokens, int32_t chunk) {
+  // The fused kernel keeps every intermediate in registers and LDS.
   (void)L;
   (void)N;
   (void)max_seqlen;
@@ -192,22 +193,51 @@ gdn_status gdn_prefill_chunked(const gdn_layer* L, const gdn_pool* P, const int3
                                int32_t max_seqlen, int32_t total_tokens, int32_t chunk,
                                const gdn_inputs* in, float* out, void* workspace,
                                size_t workspace_bytes, void* stream) {
-  (void)P;
-  (void)dst;
-  (void)init_slot;
-  (void)N;
-  (void)cu_seqlens;
-  (void)max_seqlen;
-  (void)total_tokens;
-  (void)chunk;
-  (void)in;
-  (void)out;
   (void)workspace;
   (void)workspace_bytes;
-  (void)stream;
   gdn_status st = check_layer(L);
   if (st != GDN_OK) return st;
-  return GDN_ERR_UNSUPPORTED;
+  if ((st = check_pool(L, P)) != GDN_OK) return st;
+  if (N < 0 || N > 65535 || max_seqlen < 0 || total_tokens < 0) return GDN_ERR_BAD_SHAPE;
+  if (chunk != 64) return GDN_ERR_UNSUPPORTED;
+  if (!gdn::prefill_supported(L->d_k, L->gate == GDN_GATE_CHANNEL)) return GDN_ERR_UNSUPPORTED;
+  const int32_t nblk = (L->d_v + 63) / 64;
+  if (static_cast<int64_t>(N) * L->n_v_heads * nblk > INT32_MAX) return GDN_ERR_BAD_SHAPE;
+  if (N == 0) return GDN_OK;
+  if (!dst || !cu_seqlens || !in) return GDN_ERR_NULL_ARG;
+  if (total_tokens > 0 && (!in->x || !in->alpha || !in->beta || !in->conv_w || !out))
+    return GDN_ERR_NULL_ARG;
+  if (in->x && !aligned16(in->x)) return GDN_ERR_BAD_SHAPE;
+  if (out && !aligned16(out)) return GDN_ERR_BAD_SHAPE;
+
+  gdn::PrefillArgs a{};
+  a.Hk = L->n_k_heads;
+  a.Hv = L->n_v_heads;
+  a.dv = L->d_v;
+  a.W = L->conv_width;
+  a.C = static_cast<int32_t>(channels(L));
+  a.G = L->n_v_heads / L->n_k_heads;
+  a.N = N;
+  a.nblk = nblk;
+  a.total = total_tokens;
+  a.num_slots = P->num_slots;
+  a.silu = (L->flags & GDN_F_CONV_SILU) ? 1 : 0;
+  a.l2norm = (L->flags & GDN_F_L2NORM_QK) ? 1 : 0;
+  a.q_scale = L->q_scale;
+  a.eps = L->l2_eps;
+  a.ssm = P->ssm;
+  a.conv = P->conv;
+  a.dst = dst;
+  a.init = init_slot;
+  a.cu = cu_seqlens;
+  a.x = in->x;
+  a.alpha = in->alpha;
+  a.beta = in->beta;
+  a.w = in->conv_w;
+  a.bias = in->conv_b;
+  a.out = out;
+  return from_hip(gdn::launch_prefill(a, L->d_k, L->act_dtype == GDN_BF16,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

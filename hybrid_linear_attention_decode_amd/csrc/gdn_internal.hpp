@@ -47,12 +47,37 @@ struct SlotArgs {
 
 enum SlotMode { kSlotCopy = 0, kSlotZero = 1, kSlotCommit = 2 };
 
+// One chunked prefill call over N sequences.
+struct PrefillArgs {
+  int32_t Hk, Hv, dv, W, C, G;
+  int32_t N;
+  int32_t nblk;              // workgroups per (sequence, value head): ceil(dv / 64)
+  int32_t total;             // cu_seqlens[N]
+  int64_t num_slots;
+  int32_t silu, l2norm;
+  float q_scale, eps;
+  float* ssm;                // [slots][Hv][dv][dk]
+  void* conv;                // [slots][W-1][C]
+  const int32_t* dst;        // [N]
+  const int32_t* init;       // [N] or nullptr (= dst)
+  const int32_t* cu;         // [N+1]
+  const void* x;             // [total][C]
+  const void* alpha;         // [total][Hv]
+  const void* beta;          // [total][Hv]
+  const void* w;             // [C][W]
+  const void* bias;          // [C] or nullptr
+  float* out;                // [total][Hv][dv]
+};
+
 // Launchers: return hipSuccess or the launch error.  The caller has validated
 // every host-checkable argument.
 hipError_t launch_decode(const DecodeArgs& a, int dk, int act_bf16, int kda, hipStream_t s);
 hipError_t launch_slots(const SlotArgs& a, SlotMode mode, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, int dk, int act_bf16, hipStream_t s);
 
 // Rows of state per wave of the decode kernel for a shape; 0 when unsupported.
 int decode_rows_per_wave(int dk, int G, int dv, int W1, int kda);
+// Nonzero when the chunked prefill kernels cover this key width and gate kind.
+int prefill_supported(int dk, int kda);
 
 }  // namespace gdn

@@ -1,0 +1,203 @@
+"""GPU parity of the chunked prefill (gdn_prefill_chunked) against the fp64
+sequential recurrence of the oracle, on the same seeded inputs.
+
+Bar (the pages give no number for prefill; the decode bar is reused):
+outputs max|do|/max|o| <= 2e-3 and final state max-normalised error <= 2e-3
+against the token-by-token recurrence; the destination conv window is
+bit-exact (it is a copy of raw inputs); slots other than the destinations
+and sequences that are skipped stay bit-identical."""
+import numpy as np
+import pytest
+
+import oracle
+import hybrid_linear_attention_decode_amd as gdn
+from hybrid_linear_attention_decode_amd import synth
+from tests.harness import OUT_TOL, bits, dev, host, layers, rel_err, shadow
+
+pytestmark = pytest.mark.gpu
+
+STATE_TOL = 2e-3
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def run_case(shape, seqlens, num_slots=None, seed=0, **layer_kw):
+    """Runs one seeded prefill case on the GPU and on the oracle; returns the
+    pieces the tests compare."""
+    torch = _torch()
+    N = len(seqlens)
+    case = synth.prefill_case(shape, seqlens, num_slots or max(4, 2 * N), seed)
+    init = case.init_slot
+    g, o = layers(shape, **layer_kw)
+    ssm, conv = dev(case.pool.ssm), dev(case.pool.conv)
+    before = bits(ssm), bits(conv)
+    total = int(case.cu_seqlens[-1])
+    out = torch.full((total, shape.n_v_heads, shape.d_v), float("nan"), device="cuda")
+    gdn.gdn_prefill_chunked(g, ssm, conv, dev(case.dst), dev(init), dev(case.cu_seqlens),
+                            max(seqlens) if seqlens else 0, dev(case.x), dev(case.alpha),
+                            dev(case.beta), dev(case.conv_w), out=out)
+    torch.cuda.synchronize()
+    s64, c64 = shadow(case.pool)
+    ref = oracle.prefill(o, s64, c64, case.dst, init, case.cu_seqlens, case.x, case.alpha,
+                         case.beta, case.conv_w)
+    return dict(case=case, init=init, out=host(out), ref=ref, ssm=host(ssm), conv=host(conv),
+                s64=s64, c64=c64, before=before, ssm_t=ssm, conv_t=conv)
+
+
+def check(r, out_tol=OUT_TOL, state_tol=STATE_TOL):
+    case = r["case"]
+    dst = case.dst
+    out_err = rel_err(r["out"], r["ref"]) if r["ref"].size else 0.0
+    st_err = rel_err(r["ssm"][dst], r["s64"][dst]) if dst.size else 0.0
+    assert out_err <= out_tol, f"output error {out_err:.3e}"
+    assert st_err <= state_tol, f"state error {st_err:.3e}"
+    np.testing.assert_array_equal(oracle.as_f64(r["conv"][dst]), r["c64"][dst])
+    others = np.setdiff1d(np.arange(case.pool.ssm.shape[0]), dst)
+    np.testing.assert_array_equal(bits(r["ssm_t"])[others], r["before"][0][others])
+    np.testing.assert_array_equal(bits(r["conv_t"])[others], r["before"][1][others])
+    return out_err, st_err
+
+
+SMALL = synth.Shape(2, 4, 32, 32, 4, "scalar", "bf16")
+
+
+def test_ragged_lengths_small_heads():
+    """Lengths around the chunk edges (1, 63, 64, 65, 130, 200), zero and CoW
+    starts, d_k = d_v = 32, GQA 2:1, bf16 inputs."""
+    r = run_case(SMALL, [1, 63, 64, 65, 130, 200], seed=1)
+    print("ragged small: out %.2e state %.2e" % check(r))
+
+
+def test_fp32_inputs_short_window():
+    """fp32 inputs, conv width 2, d_k = 64 and d_v = 48 (a partly idle
+    column block)."""
+    shape = synth.Shape(1, 2, 64, 48, 2, "scalar", "f32")
+    r = run_case(shape, [37, 128, 99], seed=2)
+    print("fp32 W=2: out %.2e state %.2e" % check(r))
+
+
+@pytest.mark.parametrize("dv", [16, 80, 128])
+def test_value_widths(dv):
+    """d_v not a multiple of 64 spreads one head over partly used blocks."""
+    shape = synth.Shape(2, 2, 128, dv, 4, "scalar", "bf16")
+    r = run_case(shape, [150, 64, 3], seed=3 + dv)
+    print("dv=%d: out %.2e state %.2e" % ((dv,) + check(r)))
+
+
+def test_no_silu_no_norm_with_conv_bias():
+    """SiLU and L2 norm switched off, conv bias on (small inputs keep the
+    un-normalised state bounded)."""
+    shape = synth.Shape(1, 1, 32, 32, 4, "scalar", "f32")
+    case = synth.prefill_case(shape, [96, 40], 4, seed=5)
+    case.x[:] *= 0.05
+    bias = (np.random.default_rng(5).standard_normal(shape.channels) * 0.05).astype(np.float32)
+    g, o = layers(shape, conv_silu=False, l2norm=False)
+    torch = _torch()
+    ssm, conv = dev(case.pool.ssm), dev(case.pool.conv)
+    out = gdn.gdn_prefill_chunked(g, ssm, conv, dev(case.dst), dev(case.init_slot),
+                                  dev(case.cu_seqlens), 96, dev(case.x), dev(case.alpha),
+                                  dev(case.beta), dev(case.conv_w), conv_b=dev(bias))
+    torch.cuda.synchronize()
+    s64, c64 = shadow(case.pool)
+    ref = oracle.prefill(o, s64, c64, case.dst, case.init_slot, case.cu_seqlens, case.x,
+                         case.alpha, case.beta, case.conv_w, conv_b=bias)
+    assert rel_err(host(out), ref) <= OUT_TOL
+    assert rel_err(host(ssm)[case.dst], s64[case.dst]) <= STATE_TOL
+
+
+def test_empty_skipped_and_in_place():
+    """Length-0 sequences copy (or zero) the initial state into the
+    destination; dst < 0 skips a sequence and leaves its output rows alone;
+    init == dst continues a live slot in place."""
+    torch = _torch()
+    shape = SMALL
+    case = synth.prefill_case(shape, [0, 70, 0, 50, 40], 12, seed=7)
+    g, o = layers(shape)
+    init = case.init_slot.copy()
+    dst = case.dst.copy()
+    init[2] = case.init_slot[1]        # empty sequence, copy-on-write start
+    live = case.init_slot[3]           # sequence 3 continues its own (live) slot
+    case.pool.ssm[dst[3]] = case.pool.ssm[live]
+    case.pool.conv[dst[3]] = case.pool.conv[live]
+    init[3] = dst[3]
+    dst[1] = -1                        # skipped
+    ssm, conv = dev(case.pool.ssm), dev(case.pool.conv)
+    before = bits(ssm), bits(conv)
+    total = int(case.cu_seqlens[-1])
+    out = torch.full((total, shape.n_v_heads, shape.d_v), float("nan"), device="cuda")
+    gdn.gdn_prefill_chunked(g, ssm, conv, dev(dst), dev(init), dev(case.cu_seqlens), 70,
+                            dev(case.x), dev(case.alpha), dev(case.beta), dev(case.conv_w),
+                            out=out)
+    torch.cuda.synchronize()
+    s64, c64 = shadow(case.pool)
+    ref = oracle.prefill(o, s64, c64, dst, init, case.cu_seqlens, case.x, case.alpha,
+                         case.beta, case.conv_w)
+    o_h = host(out)
+    cu = case.cu_seqlens
+    assert np.isnan(o_h[cu[1]:cu[2]]).all()          # skipped rows untouched
+    assert rel_err(o_h[cu[3]:], ref[cu[3]:]) <= OUT_TOL
+    written = dst[dst >= 0]
+    assert rel_err(host(ssm)[written], s64[written]) <= STATE_TOL
+    for s in (0, 2):                                 # empty: exact copies (or zeros)
+        np.testing.assert_array_equal(host(ssm)[dst[s]], s64[dst[s]].astype(np.float32))
+    np.testing.assert_array_equal(oracle.as_f64(host(conv)[written]), c64[written])
+    untouched = np.setdiff1d(np.arange(12), written)
+    np.testing.assert_array_equal(bits(ssm)[untouched], before[0][untouched])
+    np.testing.assert_array_equal(bits(conv)[untouched], before[1][untouched])
+
+
+def test_qwen35_4x8192_zero_and_cow():
+    """The full workload: 4 x 8192 tokens, 16/32 heads, d = 128, chunk 64,
+    bf16 inputs; sequences alternate zero start and copy-on-write from a
+    checkpoint slot.  Every output and final state element is compared."""
+    r = run_case(synth.QWEN35, [8192] * 4, num_slots=64, seed=11)
+    print("qwen35 4x8192: out %.2e state %.2e" % check(r))
+
+
+def test_split_prefill_equals_one_shot_bitwise():
+    """Prefill 4096 tokens, copy the slot to a fresh one (CoW), prefill the
+    next 4096 from it: bit-identical to one 8192-token prefill (the carry is
+    fp32 in both, and the split is chunk-aligned)."""
+    torch = _torch()
+    shape = synth.QWEN35
+    case = synth.prefill_case(shape, [8192], 8, seed=13)
+    g, _ = layers(shape)
+    ssm, conv = dev(case.pool.ssm), dev(case.pool.conv)
+    x, al, be, w = dev(case.x), dev(case.alpha), dev(case.beta), dev(case.conv_w)
+    one, mid, cow, two = 4, 5, 6, 7
+    i32 = lambda *v: dev(np.asarray(v, np.int32))
+    o_full = gdn.gdn_prefill_chunked(g, ssm, conv, i32(one), i32(-1), i32(0, 8192), 8192, x, al,
+                                     be, w)
+    o_a = gdn.gdn_prefill_chunked(g, ssm, conv, i32(mid), i32(-1), i32(0, 4096), 4096,
+                                  x[:4096], al[:4096], be[:4096], w)
+    gdn.gdn_slot_copy(g, ssm, conv, i32(mid), i32(cow))
+    o_b = gdn.gdn_prefill_chunked(g, ssm, conv, i32(two), i32(cow), i32(0, 4096), 4096,
+                                  x[4096:].contiguous(), al[4096:].contiguous(),
+                                  be[4096:].contiguous(), w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(o_full)[:4096], bits(o_a))
+    np.testing.assert_array_equal(bits(o_full)[4096:], bits(o_b))
+    np.testing.assert_array_equal(bits(ssm)[one], bits(ssm)[two])
+    np.testing.assert_array_equal(bits(conv)[one], bits(conv)[two])
+
+
+def test_unsupported_shapes_raise():
+    torch = _torch()
+    for shape, kw in [(synth.Shape(2, 2, 128, 128, 4, "channel", "bf16"), {}),
+                      (synth.Shape(2, 2, 16, 16, 4, "scalar", "f32"), {})]:
+        case = synth.prefill_case(shape, [64], 4, seed=0)
+        g, _ = layers(shape, **kw)
+        with pytest.raises(gdn.GdnError):
+            gdn.gdn_prefill_chunked(g, dev(case.pool.ssm), dev(case.pool.conv), dev(case.dst),
+                                    dev(case.init_slot), dev(case.cu_seqlens), 64, dev(case.x),
+                                    dev(case.alpha), dev(case.beta), dev(case.conv_w))
+    case = synth.prefill_case(SMALL, [64], 4, seed=0)
+    g, _ = layers(SMALL)
+    with pytest.raises(gdn.GdnError):
+        gdn.gdn_prefill_chunked(g, dev(case.pool.ssm), dev(case.pool.conv), dev(case.dst),
+                                dev(case.init_slot), dev(case.cu_seqlens), 64, dev(case.x),
+                                dev(case.alpha), dev(case.beta), dev(case.conv_w), chunk=32)
+    torch.cuda.synchronize()
