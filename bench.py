@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak, TFLOP/s
 DECODE_KERNEL = "decode_kernel<128, 32, bf16, false>"
 
 
@@ -285,6 +286,69 @@ def bench_kda_stack(torch, gdn, synth, K=20, W=3, layers=48):
     return rec
 
 
+def prefill_counts(shape, seqlens):
+    """Algorithmic bytes and FLOPs of one chunked prefill call, and the bf16
+    MFMA FLOPs the kernel issues.
+
+    bytes: x read, o written (fp32), alpha/beta read, taps, and per sequence
+    the final state + conv window written and the initial ones read (zero
+    starts read nothing; counted as if every start were a copy).
+    flops (dense, per (64-token chunk, value head)): the UT transform
+    (K K^T, Q K^T, T V, W = T diag(e^g) K: 5.24 M) and the state pass
+    (W S0^T, Q S0^T, P U, U^T K: 6.29 M) -- 11.53 MFLOP at d = 128.
+    issued: per workgroup (64 value columns) and chunk, 20 Gram tiles and 4
+    waves of K S0^T, Q S0^T, P U and state-update tiles on 16x16x32 MFMAs,
+    the U solve on 16x16x16 MFMAs, each product three times (hi/lo split)."""
+    act = 2 if shape.dtype == "bf16" else 4
+    C, Hv, dk, dv = shape.channels, shape.n_v_heads, shape.d_k, shape.d_v
+    total = int(sum(seqlens))
+    state = Hv * dv * dk * 4 + (shape.conv_width - 1) * C * act
+    nbytes = total * (C * act + 2 * Hv * act + Hv * dv * 4) + C * shape.conv_width * act \
+        + 2 * state * len(seqlens)
+    chunks = sum(-(-L // 64) for L in seqlens)
+    c, dense = 64, 0
+    dense += 2 * c * c * dk * 2 + c * c * dv * 2 + c * c * dk * 2     # KK^T, QK^T, TV, TK
+    dense += 2 * c * dk * dv * 2 + c * c * dv * 2 + dv * c * dk * 2   # WS, QS, PU, U^T K
+    flops = dense * chunks * Hv
+    nblk = -(-dv // 64)
+    ksl, kdt = dk // 32, dk // 16
+    m32 = 20 * ksl * 3 + 4 * (4 * ksl * 2 * 3 + 6 * 3 + kdt * 2 * 3)
+    m16 = 4 * 10 * 3
+    issued = (m32 * 16 * 16 * 32 * 2 + m16 * 16 * 16 * 16 * 2) * chunks * Hv * nblk
+    return nbytes, flops, issued
+
+
+def bench_prefill(torch, gdn, synth, K=10, W=2, seqlens=(8192,) * 4):
+    """Chunked prefill, Qwen3.5 shape, 4 x 8192 tokens, chunk 64: sequences
+    alternate a zero start and a copy-on-write start from checkpoint slots."""
+    shape = synth.QWEN35
+    case = synth.prefill_case(shape, list(seqlens), 64, seed=17)
+    dev = _dev(torch)
+    g = gdn.Layer(shape.n_k_heads, shape.n_v_heads, shape.d_k, shape.d_v, shape.conv_width,
+                  shape.gate, shape.dtype)
+    ssm, conv = dev(case.pool.ssm), dev(case.pool.conv)
+    dst, init, cu = dev(case.dst), dev(case.init_slot), dev(case.cu_seqlens)
+    x, al, be, w = dev(case.x), dev(case.alpha), dev(case.beta), dev(case.conv_w)
+    total = int(case.cu_seqlens[-1])
+    out = torch.empty((total, shape.n_v_heads, shape.d_v), dtype=torch.float32, device="cuda")
+
+    def call(_c):
+        gdn.gdn_prefill_chunked(g, ssm, conv, dst, init, cu, max(seqlens), x, al, be, w, out=out)
+    for c in range(W):
+        call(c)
+    ms = time_calls(torch, call, W, K) / K
+    nbytes, flops, issued = prefill_counts(shape, seqlens)
+    rec = path_record(ms, nbytes, total, "chunked prefill, Qwen3.5 shape, 4 x 8192 tokens, "
+                                         "chunk 64, zero / copy-on-write starts")
+    rec["algorithmic_tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
+    rec["algorithmic_flops"] = int(flops)
+    rec["mfma_issued_bf16_flops"] = int(issued)
+    rec["mfma_issued_tflops"] = round(issued / (ms * 1e-3) / 1e12, 1)
+    rec["mfma_issued_frac_of_bf16_peak"] = round(issued / (ms * 1e-3) / 1e12 /
+                                                 MFMA_BF16_PEAK_TFLOPS, 4)
+    return rec
+
+
 def copy_calibration(torch, mib: int = 256, reps: int = 5):
     """A plain device copy of known size, for scaling the PMC byte counters."""
     n = mib * (1 << 20) // 4
@@ -304,7 +368,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "decode", "paths", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "decode", "paths", "prefill", "copy"],
+                    default="all",
                     help="profiling runs: just the headline decode, the other paths, or a "
                          "plain copy of known size")
     args = ap.parse_args()
@@ -329,8 +394,11 @@ def main():
         return
     if args.only == "paths":
         for r in (bench_decode_b16(torch, gdn, synth), *bench_spec(torch, gdn, synth),
-                  bench_kda_stack(torch, gdn, synth)):
+                  bench_kda_stack(torch, gdn, synth), bench_prefill(torch, gdn, synth)):
             print(json.dumps(r), flush=True)
+        return
+    if args.only == "prefill":
+        print(json.dumps(bench_prefill(torch, gdn, synth)), flush=True)
         return
 
     shape = synth.QWEN35
@@ -358,12 +426,15 @@ def main():
 
     paths = None
     if args.only == "all":
-        log("bench: other paths (B=16 decode, speculative draft + commit, KDA 48-layer stack)")
+        log("bench: other paths (B=16 decode, speculative draft + commit, KDA 48-layer stack, "
+            "chunked prefill)")
         d16 = bench_decode_b16(torch, gdn, synth)
         draft, commit = bench_spec(torch, gdn, synth)
         kda = bench_kda_stack(torch, gdn, synth)
+        pf = bench_prefill(torch, gdn, synth)
         paths = {"decode_qwen35_b16": d16, "spec_draft_qwen35_b64_t7": draft,
-                 "spec_commit_qwen35_b64": commit, "kda_stack_b64_48layers": kda}
+                 "spec_commit_qwen35_b64": commit, "kda_stack_b64_48layers": kda,
+                 "prefill_qwen35_4x8192": pf}
 
     cpu = None
     if not args.no_cpu_baseline and args.only == "all":

@@ -17,14 +17,21 @@
 // Work split.  Rows of S are independent through the whole recurrence (row
 // i of S, U and O depend only on row i of S0), so a workgroup owns one
 // (sequence, value head, 64 value columns) and walks that sequence's chunks
-// in order, its 64x d_k slice of S^T held in MFMA accumulators across
-// chunks.  Per chunk its 4 waves:
-//   1. conv1d + SiLU + L2 norm of the chunk's q and k (8 channels x 8 tokens
-//      per thread), stored as bf16 (hi, lo) pairs; gates and prefix sums;
-//   2. the 20 lower 16x16 tiles of K K^T and Q K^T  -> A, P;
-//   3. inverses of the diagonal blocks of (I + A);
-//   4. per wave, 16 value columns: K S0^T, Q S0^T, the value conv, U, O and
-//      the state update.
+// in order, its 64 x d_k slice of S^T held in MFMA accumulators across
+// chunks.  Its 8 waves form a two-stage pipeline:
+//   producers (waves 0-3), one chunk ahead: raw q / k inputs prefetched a
+//     further chunk ahead, conv1d + SiLU + L2 norm (8 channels x 8 tokens
+//     per thread) into registers as bf16 (hi, lo) pairs, gates and log-decay
+//     prefix sums;
+//   consumers (waves 4-7), 16 value columns each: the value conv, K S0^T,
+//     Q S0^T, U, O and the state update of the current chunk.
+// Between chunks all 8 waves meet: producers store the next chunk's K, Q
+// and gates, then every wave takes some of the 20 lower 16x16 tiles of
+// K K^T and Q K^T (-> A and P); the four waves holding a diagonal tile of
+// K K^T also invert that block of (I + A) from the tile's registers:
+// with N strictly lower triangular, (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)
+// (I + N^8), and K K^T is symmetric, so both operand layouts of N come from
+// the one accumulator tile.
 // Every product runs on v_mfma_f32_16x16x{32,16}_bf16 with each fp32
 // operand split as x ~= hi + lo (two bf16), and a*b ~= ah*bh + ah*bl + al*bh
 // accumulated in fp32: about 16 significant bits per operand, which keeps
@@ -48,8 +55,9 @@ typedef short s8 __attribute__((ext_vector_type(8)));
 typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 
 constexpr int kC = 64;         // chunk length
-constexpr int kThreads = 256;  // 4 waves
-constexpr int kCols = 64;      // value columns per workgroup (16 per wave)
+constexpr int kThreads = 512;  // 4 producer + 4 consumer waves
+constexpr int kProd = 256;     // producer threads
+constexpr int kCols = 64;      // value columns per workgroup (16 per consumer wave)
 
 // x ~= hi + lo with hi = bf16(x), lo = bf16(x - hi) (round to nearest even).
 __device__ __forceinline__ void split(float x, short& hi, short& lo) {
@@ -98,47 +106,81 @@ __device__ __forceinline__ int slot(int i) {
   return (i & ~31) | (((i >> 2) & 3) << 3) | (((i >> 4) & 1) << 2) | (i & 3);
 }
 
-// LDS plan (bytes).  Rows are padded by 16 bytes so that 16 lanes reading
-// 16 consecutive rows hit distinct banks.
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane j receives element
+// (j mod 4) of the 64-bit words read by lanes 4e + j/4, e = 0..3.  Lanes
+// 4e + q reading row r0 + e, columns c0 + 4q..4q+3 thus hand lane j the
+// column c0 + j of rows r0..r0+3.
+__device__ __forceinline__ s4 ld_tr(const short* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s4*)(const_cast<short*>(p)));
+}
+
+// Raw buffer accesses (gfx9 descriptor, no stride): an access whose 32-bit
+// byte offset lies at or past num_records reads zero or is dropped, which
+// masks rows outside a sequence without branches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// SiLU with the hardware exp2 / reciprocal.
+__device__ __forceinline__ float silu(float y) {
+  return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y));
+}
+
+// LDS plan (bytes).  P, A and V^T rows are padded by 16 bytes so that 16
+// lanes reading 16 consecutive rows hit distinct banks.  K and Q rows of
+// d_k = 128 (256 bytes, all 64 banks) are instead swizzled: 16-byte chunk c
+// of row r sits at chunk c ^ (((r & 3) << 2) | ((r >> 2) & 3)).  Both read
+// patterns then touch 16 distinct chunks: 16 consecutive rows at one chunk
+// (16x16x32 operands), and 4 rows x 4 chunks (the transposing reads of K^T
+// tiles).  The planes are staggered by 64 bytes so that stores of K and Q
+// rows for the same token fall in different banks.
 template <int DK>
 struct Plan {
-  static constexpr int kRowQK = DK + 8;  // bf16 per row of K, Q   [token][dk]
-  static constexpr int kRowT = kC + 8;   // bf16 per row of K^T [dk][token], P, A [token][token]
-  static constexpr int kQK = 2 * kC * kRowQK;
-  static constexpr int kKT = 2 * DK * kRowT;
+  static constexpr bool kSwz = DK == 128;
+  static constexpr int kRowQK = kSwz ? DK : DK + 8;  // bf16 per row of K, Q   [token][dk]
+  static constexpr int kRowT = kC + 8;   // bf16 per row of P, A   [token][token]
+  static constexpr int kQK = 2 * kC * kRowQK + 64;
   static constexpr int kSq = 2 * kC * kRowT;
   static constexpr int oKh = 0, oKl = oKh + kQK, oQh = oKl + kQK, oQl = oQh + kQK;
-  static constexpr int oTh = oQl + kQK, oTl = oTh + kKT;
-  static constexpr int oPh = oTl + kKT, oPl = oPh + kSq, oAh = oPl + kSq, oAl = oAh + kSq;
-  static constexpr int kAdRow = 17;  // fp32 diagonal blocks of A: [4][16][17]
-  static constexpr int oAd = oAl + kSq;
-  static constexpr int oGate = oAd + 4 * 16 * kAdRow * 4;  // fp32 [4][64]: g, b, e^g, e^{g_c-g}
-  static constexpr int kBytes = oGate + 4 * kC * 4;
+  static constexpr int oPh = oQl + kQK, oPl = oPh + kSq, oAh = oPl + kSq, oAl = oAh + kSq;
+  static constexpr int oGate = oAl + kSq;  // fp32 [4][64]: g, b, e^g, e^{g_c - g}
+  static constexpr int kRowV = kC + 4;     // fp32 per row of V^T [value column][token]
+  static constexpr int oV = oGate + 4 * kC * 4;
+  // conv taps (4, left-padded) and bias of the workgroup's channels: q, k of
+  // the key head, then the 64 value columns
+  static constexpr int kWch = 2 * DK + kCols;
+  static constexpr int oW = oV + kCols * kRowV * 4;
+  static constexpr int oB = oW + kWch * 16;
+  static constexpr int kBytes = oB + kWch * 4;
 };
 
-// Raw input loads (bf16 or fp32 storage -> fp32).
+// Raw 8-channel rows: 16 bytes of bf16 or 32 bytes of fp32.
 template <typename Act>
-__device__ __forceinline__ void load8(const Act* p, float (&v)[8]);
-template <>
-__device__ __forceinline__ void load8<bf16>(const bf16* p, float (&v)[8]) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(w[i] << 16);
-    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+struct Row8 {
+  static constexpr int kWords = sizeof(Act) == 2 ? 4 : 8;
+  uint32_t w[kWords];
+  __device__ __forceinline__ void load(rsrc_t r, int off) {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    const u4 u = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    w[0] = u[0], w[1] = u[1], w[2] = u[2], w[3] = u[3];
+    if constexpr (kWords == 8) {
+      const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
+      w[4] = v[0], w[5] = v[1], w[6] = v[2], w[7] = v[3];
+    }
   }
-}
-template <>
-__device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
-  const f4 x = *reinterpret_cast<const f4*>(p);
-  const f4 y = *reinterpret_cast<const f4*>(p + 4);
+  __device__ __forceinline__ void merge(const Row8& o) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[i] = x[i];
-    v[4 + i] = y[i];
+    for (int i = 0; i < kWords; ++i) w[i] |= o.w[i];
   }
-}
+  __device__ __forceinline__ float get(int m) const {
+    if constexpr (kWords == 4)
+      return __uint_as_float((m & 1) ? (w[m >> 1] & 0xffff0000u) : (w[m >> 1] << 16));
+    else
+      return __uint_as_float(w[m]);
+  }
+};
 
 template <int DK, typename Act>
 struct Prefill {
@@ -151,36 +193,56 @@ struct Prefill {
   const PrefillArgs& a;
   unsigned char* lds;
   int tid, wave, lane, lr, lg;
-  int s, h, hk, e0;
+  int h, hk, e0;
   int t0, T;
-  int32_t dst, init;
+  int32_t init;
 
   __device__ short* sp(int off) const { return reinterpret_cast<short*>(lds + off); }
+  // The lane id, opaque to the compiler: offsets derived from it inside a
+  // phase are recomputed there (a few VALU ops) instead of being hoisted
+  // out of the chunk loop and kept live (or spilled) across all phases.
+  __device__ __forceinline__ static int opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+  }
+  __device__ __forceinline__ int lane_now() const { return opaque(lane); }
+  // Element offset of storage slot sl of row r in a K or Q plane.
+  __device__ __forceinline__ static int qk(int r, int sl) {
+    if constexpr (P::kSwz)
+      return r * DK + (((sl >> 3) ^ (((r & 3) << 2) | ((r >> 2) & 3))) << 3) + (sl & 7);
+    else
+      return r * P::kRowQK + sl;
+  }
   __device__ float* fp(int off) const { return reinterpret_cast<float*>(lds + off); }
 
-  // Row rho of the sequence (rho < 0: the conv window of the initial slot)
-  // at channel ch, 8 channels; zero outside the sequence and its window.
-  __device__ __forceinline__ void row8(int rho, int ch, float (&v)[8]) const {
-    const int W1 = a.W - 1;
-    if (rho >= 0 && rho < T) {
-      load8<Act>(static_cast<const Act*>(a.x) + (static_cast<int64_t>(t0) + rho) * a.C + ch, v);
-    } else if (rho < 0 && rho >= -W1 && init >= 0) {
-      load8<Act>(static_cast<const Act*>(a.conv) +
-                     (static_cast<int64_t>(init) * W1 + (W1 + rho)) * a.C + ch,
-                 v);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.f;
-    }
+  // Raw input rows for chunk c0: a descriptor over rows b0.. of the
+  // sequence (b0 = c0 - 8, or 0), ending at the sequence's last row, so rows
+  // past the end (and before row 0) read zero.  The initial conv window
+  // (W-1 rows before row 0) has its own descriptor, empty when the sequence
+  // starts from zeros.
+  __device__ __forceinline__ int chunk_base(int c0) const { return c0 >= 8 ? c0 - 8 : 0; }
+  __device__ __forceinline__ rsrc_t x_rows(int c0) const {
+    const int b0 = chunk_base(c0);
+    const int64_t rowb = static_cast<int64_t>(a.C) * sizeof(Act);
+    const int64_t n = static_cast<int64_t>(T - b0) < 80 ? T - b0 : 80;
+    return make_rsrc(static_cast<const Act*>(a.x) + (static_cast<int64_t>(t0) + b0) * a.C,
+                     static_cast<uint32_t>(n * rowb));
   }
-  __device__ __forceinline__ float row1(int rho, int ch) const {
+  __device__ __forceinline__ rsrc_t win_rows() const {
     const int W1 = a.W - 1;
-    if (rho >= 0 && rho < T)
-      return to_f32(static_cast<const Act*>(a.x)[(static_cast<int64_t>(t0) + rho) * a.C + ch]);
-    if (rho < 0 && rho >= -W1 && init >= 0)
-      return to_f32(static_cast<const Act*>(
-          a.conv)[(static_cast<int64_t>(init) * W1 + (W1 + rho)) * a.C + ch]);
-    return 0.f;
+    const bool on = init >= 0 && W1 > 0;
+    return make_rsrc(on ? static_cast<const Act*>(a.conv) + static_cast<int64_t>(init) * W1 * a.C
+                        : a.x,
+                     on ? static_cast<uint32_t>(W1 * a.C * sizeof(Act)) : 0u);
+  }
+  // Byte offsets of row rho at channel ch in the two descriptors.
+  __device__ __forceinline__ int x_off(int c0, int rho, int ch) const {
+    return (rho - chunk_base(c0)) * a.C * static_cast<int>(sizeof(Act)) +
+           ch * static_cast<int>(sizeof(Act));
+  }
+  __device__ __forceinline__ int win_off(int rho, int ch) const {
+    return (a.W - 1 + rho) * a.C * static_cast<int>(sizeof(Act)) +
+           ch * static_cast<int>(sizeof(Act));
   }
   // Conv tap jj (0..3, the last on the current token) of channel ch; taps of
   // a narrower conv are left-padded with zeros.
@@ -189,280 +251,557 @@ struct Prefill {
     return jj >= lead ? to_f32(static_cast<const Act*>(a.w)[static_cast<int64_t>(ch) * a.W + jj - lead])
                       : 0.f;
   }
-  __device__ __forceinline__ float act(float y) const {
-    return a.silu ? y / (1.0f + expf(-y)) : y;
+  __device__ __forceinline__ float act(float y) const { return a.silu ? silu(y) : y; }
+
+  // ================= producers =================
+  // Thread (co, tau): channel octet co of q|k (q first), tokens 8 tau..+7.
+  struct Prod {
+    Row8<Act> raw[11];          // rows 8 tau - 3 .. 8 tau + 7 of a chunk
+    s4 hi[8][2], lo[8][2];      // the chunk's normalised rows, not yet stored
+    float gate[4];              // wave 3: g, b, e^g, e^{g_c - g} of token = lane
+    int co, tau, ch, oc;
+    bool isk, on;
+    // value conv: channels 2 vp, 2 vp + 1 of the column block, tokens 8 vt..+7
+    uint32_t vraw[11][sizeof(Act) == 2 ? 1 : 2];
+    f4 vo[2][2];                // [channel][token half], not yet stored
+    int vp, vt, vch;
+    bool von;
+  };
+
+  __device__ void prod_init(Prod& p) const {
+    p.on = tid < 8 * kNco;
+    p.co = tid % kNco;
+    p.tau = tid / kNco;
+    p.isk = p.co >= kGrp;
+    p.oc = p.isk ? p.co - kGrp : p.co;
+    p.ch = (p.isk ? a.Hk * DK : 0) + hk * DK + 8 * p.oc;
+    p.vp = tid % 32;
+    p.vt = tid / 32;
+    p.von = e0 + 2 * p.vp < a.dv;
+    p.vch = 2 * a.Hk * DK + h * a.dv + e0 + 2 * p.vp;
   }
 
-  // ---- step 1: conv + SiLU + L2 norm of q and k for tokens 8*tau..+7 of
-  // the chunk at c0, 8 channels (octet co).  Writes K, Q as (hi, lo) rows
-  // and K^T as (hi, lo) columns.
-  __device__ void prep_qk(int c0, int co, int tau, const float (&wt)[8][4],
-                          const float (&bias)[8]) const {
-    const bool isk = co >= kGrp;
-    const int oc = isk ? co - kGrp : co;
-    const int ch = (isk ? a.Hk * DK : 0) + hk * DK + 8 * oc;
-    float raw[11][8];
-#pragma unroll
-    for (int r = 0; r < 11; ++r) row8(c0 + 8 * tau - 3 + r, ch, raw[r]);
-    float y[8][8];
-    float ss[8];
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      ss[tt] = 0.f;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        float v = bias[m];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) v = fmaf(wt[m][jj], raw[tt + jj][m], v);
-        v = act(v);
-        y[tt][m] = v;
-        ss[tt] = fmaf(v, v, ss[tt]);
+  // Taps and bias of the workgroup's channels into LDS (all threads).
+  __device__ void load_taps() const {
+    float* wt = fp(P::oW);
+    float* bs = fp(P::oB);
+    for (int i = tid; i < P::kWch; i += kThreads) {
+      int ch;
+      bool ok = true;
+      if (i < DK)
+        ch = hk * DK + i;
+      else if (i < 2 * DK)
+        ch = a.Hk * DK + hk * DK + (i - DK);
+      else {
+        ch = 2 * a.Hk * DK + h * a.dv + e0 + (i - 2 * DK);
+        ok = e0 + (i - 2 * DK) < a.dv;
       }
-    }
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      const float sum = group_sum<kGrp>(ss[tt]);
-      float sc = a.l2norm ? rsqrtf(sum + a.eps) : 1.0f;
-      if (!isk) sc *= a.q_scale;
-      if (c0 + 8 * tau + tt >= T) sc = 0.f;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) y[tt][m] *= sc;
-    }
-    // rows: token t, two groups of 4 channels at slot(8*oc) and +8
-    short* hi = sp(isk ? P::oKh : P::oQh);
-    short* lo = sp(isk ? P::oKl : P::oQl);
-    const int sb = slot(8 * oc);
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      s4 h0, l0, h1, l1;
-      split4(f4{y[tt][0], y[tt][1], y[tt][2], y[tt][3]}, h0, l0);
-      split4(f4{y[tt][4], y[tt][5], y[tt][6], y[tt][7]}, h1, l1);
-      const int row = (8 * tau + tt) * P::kRowQK + sb;
-      *reinterpret_cast<s4*>(hi + row) = h0;
-      *reinterpret_cast<s4*>(hi + row + 8) = h1;
-      *reinterpret_cast<s4*>(lo + row) = l0;
-      *reinterpret_cast<s4*>(lo + row + 8) = l1;
-    }
-    if (isk) {
-      // columns: channel 8*oc+m, tokens at slot(8*tau) and +8
-      short* th = sp(P::oTh);
-      short* tl = sp(P::oTl);
-      const int tb = slot(8 * tau);
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        s4 h0, l0, h1, l1;
-        split4(f4{y[0][m], y[1][m], y[2][m], y[3][m]}, h0, l0);
-        split4(f4{y[4][m], y[5][m], y[6][m], y[7][m]}, h1, l1);
-        const int row = (8 * oc + m) * P::kRowT + tb;
-        *reinterpret_cast<s4*>(th + row) = h0;
-        *reinterpret_cast<s4*>(th + row + 8) = h1;
-        *reinterpret_cast<s4*>(tl + row) = l0;
-        *reinterpret_cast<s4*>(tl + row + 8) = l1;
-      }
+      f4 t = {0.f, 0.f, 0.f, 0.f};
+      if (ok) t = f4{tap(ch, 0), tap(ch, 1), tap(ch, 2), tap(ch, 3)};
+      *reinterpret_cast<f4*>(wt + 4 * i) = t;
+      bs[i] = (ok && a.bias) ? to_f32(static_cast<const Act*>(a.bias)[ch]) : 0.f;
     }
   }
 
-  // ---- step 1 (one wave): log-decay prefix sums and gates of the chunk.
-  __device__ void gates(int c0) const {
-    float la = 0.f, bt = 0.f;
-    if (c0 + lane < T) {
-      const int64_t row = (static_cast<int64_t>(t0) + c0 + lane) * a.Hv + h;
-      la = fmaxf(logf(to_f32(static_cast<const Act*>(a.alpha)[row])), -80.0f);
-      bt = to_f32(static_cast<const Act*>(a.beta)[row]);
-    }
-    float g = la;
+  __device__ __forceinline__ void prod_load(Prod& p, int c0) const {
+    const rsrc_t rx = x_rows(c0);
+    const int tau = opaque(p.tau), ch = opaque(p.ch), vt = opaque(p.vt), vch = opaque(p.vch);
+    if (p.on) {
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float o = __shfl_up(g, off);
-      if (lane >= off) g += o;
+      for (int r = 0; r < 11; ++r) p.raw[r].load(rx, x_off(c0, c0 + 8 * tau - 3 + r, ch));
     }
-    const float gc = __shfl(g, 63);
-    float* gt = fp(P::oGate);
-    gt[lane] = g;
-    gt[kC + lane] = bt;
-    gt[2 * kC + lane] = expf(g);
-    gt[3 * kC + lane] = expf(gc - g);
-  }
-
-  // ---- step 2: tile q of the 20 lower tiles (10 of K K^T, then 10 of
-  // Q K^T), scaled into A (off-diagonal: (hi, lo); diagonal: fp32) and P.
-  __device__ void gram_tile(int q) const {
-    const bool isp = q >= 10;
-    const int p = isp ? q - 10 : q;
-    const int ib = p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0;
-    const int jb = p - ib * (ib + 1) / 2;
-    const short* ah = sp(isp ? P::oQh : P::oKh);
-    const short* al = sp(isp ? P::oQl : P::oKl);
-    const short* bh = sp(P::oKh);
-    const short* bl = sp(P::oKl);
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (p.von) {
 #pragma unroll
-    for (int sl = 0; sl < kSl; ++sl) {
-      const int ra = (16 * ib + lr) * P::kRowQK + 32 * sl + 8 * lg;
-      const int rb = (16 * jb + lr) * P::kRowQK + 32 * sl + 8 * lg;
-      acc = mma32x3(*reinterpret_cast<const s8*>(ah + ra), *reinterpret_cast<const s8*>(al + ra),
-                    *reinterpret_cast<const s8*>(bh + rb), *reinterpret_cast<const s8*>(bl + rb),
-                    acc);
-    }
-    const float* gt = fp(P::oGate);
-    const int i = 16 * jb + lr;
-    const float gi = gt[i];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = 16 * ib + 4 * lg + v;
-      const float dec = expf(gt[r] - gi);
-      if (isp) {
-        const float val = i <= r ? dec * acc[v] : 0.f;
-        short vh, vl;
-        split(val, vh, vl);
-        sp(P::oPh)[r * P::kRowT + slot(i)] = vh;
-        sp(P::oPl)[r * P::kRowT + slot(i)] = vl;
-      } else {
-        const float val = i < r ? gt[kC + r] * dec * acc[v] : 0.f;
-        if (ib == jb) {
-          fp(P::oAd)[(ib * 16 + (r & 15)) * P::kAdRow + (i & 15)] = val;
+      for (int r = 0; r < 11; ++r) {
+        const int off = x_off(c0, c0 + 8 * vt - 3 + r, vch);
+        if constexpr (sizeof(Act) == 2) {
+          p.vraw[r][0] = __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0);
         } else {
-          short vh, vl;
-          split(val, vh, vl);
-          sp(P::oAh)[r * P::kRowT + slot(i)] = vh;
-          sp(P::oAl)[r * P::kRowT + slot(i)] = vl;
+          typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+          const u2 v = __builtin_amdgcn_raw_buffer_load_b64(rx, off, 0, 0);
+          p.vraw[r][0] = v[0];
+          p.vraw[r][1] = v[1];
+        }
+      }
+    }
+    if (c0 == 0) {
+      // rows -3..-1 (thread tokens 0..2 of token octet 0) from the window;
+      // every other offset lies past the window and reads zero
+      const rsrc_t rw = win_rows();
+      if (p.on) {
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+          Row8<Act> wr;
+          wr.load(rw, win_off(8 * tau - 3 + r, ch));
+          p.raw[r].merge(wr);
+        }
+      }
+      if (p.von) {
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+          const int off = win_off(8 * vt - 3 + r, vch);
+          if constexpr (sizeof(Act) == 2) {
+            p.vraw[r][0] |= __builtin_amdgcn_raw_buffer_load_b32(rw, off, 0, 0);
+          } else {
+            typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+            const u2 v = __builtin_amdgcn_raw_buffer_load_b64(rw, off, 0, 0);
+            p.vraw[r][0] |= v[0];
+            p.vraw[r][1] |= v[1];
+          }
         }
       }
     }
   }
 
-  // ---- step 3 (16 lanes of wave b): column c of X_bb = (I + A_bb)^{-1} by
-  // forward substitution; stored as (hi, lo) in the diagonal block of A.
-  __device__ void diag_inverse(int b, int c) const {
-    const float* ad = fp(P::oAd) + b * 16 * P::kAdRow;
-    float x[16];
+  // conv + SiLU + L2 norm (+ q scale) of the prefetched rows of chunk c0.
+  __device__ void prod_prep(Prod& p, int c0) const {
+    const float* wl = fp(P::oW);
+    const float* bl = fp(P::oB);
+    if (p.on) {
+      f4 wt[8];
+      float bias[8];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float acc = r == c ? 1.f : 0.f;
+      for (int m = 0; m < 8; ++m) {
+        wt[m] = *reinterpret_cast<const f4*>(wl + 4 * (8 * p.co + m));
+        bias[m] = bl[8 * p.co + m];
+      }
 #pragma unroll
-      for (int i = 0; i < r; ++i) acc = fmaf(-ad[r * P::kAdRow + i], x[i], acc);
-      x[r] = acc;
+      for (int tt = 0; tt < 8; ++tt) {
+        float y[8], ss = 0.f;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          float v = bias[m];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            v = fmaf(wt[m][jj], p.raw[tt + jj].get(m), v);
+          v = act(v);
+          y[m] = v;
+          ss = fmaf(v, v, ss);
+        }
+        const float sum = group_sum<kGrp>(ss);
+        float sc = a.l2norm ? rsqrtf(sum + a.eps) : 1.0f;
+        if (!p.isk) sc *= a.q_scale;
+        if (c0 + 8 * p.tau + tt >= T) sc = 0.f;
+        split4(f4{y[0], y[1], y[2], y[3]} * sc, p.hi[tt][0], p.lo[tt][0]);
+        split4(f4{y[4], y[5], y[6], y[7]} * sc, p.hi[tt][1], p.lo[tt][1]);
+      }
     }
+    if (p.von) {
+      float xr[11][2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      short vh, vl;
-      split(x[r], vh, vl);
-      sp(P::oAh)[(16 * b + r) * P::kRowT + slot(16 * b + c)] = vh;
-      sp(P::oAl)[(16 * b + r) * P::kRowT + slot(16 * b + c)] = vl;
+      for (int r = 0; r < 11; ++r) {
+        if constexpr (sizeof(Act) == 2) {
+          xr[r][0] = __uint_as_float(p.vraw[r][0] << 16);
+          xr[r][1] = __uint_as_float(p.vraw[r][0] & 0xffff0000u);
+        } else {
+          xr[r][0] = __uint_as_float(p.vraw[r][0]);
+          xr[r][1] = __uint_as_float(p.vraw[r][1]);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const f4 vw = *reinterpret_cast<const f4*>(wl + 4 * (2 * DK + 2 * p.vp + m));
+        const float vb = bl[2 * DK + 2 * p.vp + m];
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+          float y = vb;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) y = fmaf(vw[jj], xr[tt + jj][m], y);
+          p.vo[m][tt >> 2][tt & 3] = c0 + 8 * p.vt + tt < T ? act(y) : 0.f;
+        }
+      }
+    }
+    if (wave == 3) {
+      float la = 0.f, bt = 0.f;
+      if (c0 + lane < T) {
+        const int64_t row = (static_cast<int64_t>(t0) + c0 + lane) * a.Hv + h;
+        la = fmaxf(logf(to_f32(static_cast<const Act*>(a.alpha)[row])), -80.0f);
+        bt = to_f32(static_cast<const Act*>(a.beta)[row]);
+      }
+      float g = la;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float o = __shfl_up(g, off);
+        if (lane >= off) g += o;
+      }
+      const float gc = __shfl(g, 63);
+      p.gate[0] = g;
+      p.gate[1] = bt;
+      p.gate[2] = expf(g);
+      p.gate[3] = expf(gc - g);
     }
   }
 
-  // ---- step 4: the wave's 16 value columns.  S[d] holds rows
-  // 16d + 4*lg + v (key index) of S^T at column e0 + lr (value index).
-  __device__ void columns(int c0, f4 (&S)[kDt], const float (&wv)[4], float bv) const {
-    const float* gt = fp(P::oGate);
-    // S^T as k-operand pairs of 16x16x32 MFMAs
-    s8 sbh[kSl], sbl[kSl];
+  // Store the prepared chunk: rows of K or Q (two groups of 4 channels at
+  // slot(8 oc) and +8), and the gates.
+  __device__ void prod_store(const Prod& p) const {
+    if (p.on) {
+      short* hi = sp(p.isk ? P::oKh : P::oQh);
+      short* lo = sp(p.isk ? P::oKl : P::oQl);
+      const int tau = opaque(p.tau);
+      const int sb = slot(8 * opaque(p.oc));
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        const int o0 = qk(8 * tau + tt, sb), o1 = qk(8 * tau + tt, sb + 8);
+        *reinterpret_cast<s4*>(hi + o0) = p.hi[tt][0];
+        *reinterpret_cast<s4*>(hi + o1) = p.hi[tt][1];
+        *reinterpret_cast<s4*>(lo + o0) = p.lo[tt][0];
+        *reinterpret_cast<s4*>(lo + o1) = p.lo[tt][1];
+      }
+    }
+    if (p.von) {
+      float* vt = fp(P::oV);
+      const int vp = opaque(p.vp), vtk = opaque(p.vt);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        float* row = vt + (2 * vp + m) * P::kRowV + 8 * vtk;
+        *reinterpret_cast<f4*>(row) = p.vo[m][0];
+        *reinterpret_cast<f4*>(row + 4) = p.vo[m][1];
+      }
+    }
+    if (wave == 3) {
+      float* gt = fp(P::oGate);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gt[i * kC + lane] = p.gate[i];
+    }
+  }
+
+  // ================= all waves: A, P and the diagonal inverses =========
+  // Tile coordinates: q < 6 an off-diagonal block of A, else block q - 6
+  // of P (lower, with the diagonal); q = 16 + b: diagonal block b of A.
+  __device__ __forceinline__ void tile_of(int q, int& ib, int& jb, bool& isp) const {
+    isp = q >= 6 && q < 16;
+    if (q >= 16) {
+      ib = jb = q - 16;
+    } else if (isp) {
+      const int p = q - 6;
+      ib = p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0;
+      jb = p - ib * (ib + 1) / 2;
+    } else {
+      ib = q >= 3 ? 3 : q >= 1 ? 2 : 1;
+      jb = q - (ib - 1) * ib / 2;
+    }
+  }
+
+  // Raw Gram tiles (K or Q rows ib) . (K rows jb)^T of N tiles at once: each
+  // slice's operands are read first, then the MFMAs run interleaved over the
+  // tiles' independent accumulators.
+  // Element offsets, for rows 16 blk + lr, of the 16x16x32 operand slots
+  // 32 sl + 8 lg: a per-slice base plus 16 blk rows (swizzle depends on
+  // the row only through lr).
+  __device__ __forceinline__ void op_bases(int (&ob)[kSl]) const {
+    const int l = lane_now(), r = l & 15, g = l >> 4;
+#pragma unroll
+    for (int sl = 0; sl < kSl; ++sl) ob[sl] = qk(r, 32 * sl + 8 * g);
+  }
+
+  template <int N>
+  __device__ __forceinline__ void gram(const int (&q)[N], f4 (&acc)[N]) const {
+    int ra[N], rb[N];
+    const short *ah[N], *al[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      int ib, jb;
+      bool isp;
+      tile_of(q[n], ib, jb, isp);
+      ra[n] = 16 * ib * P::kRowQK;
+      rb[n] = 16 * jb * P::kRowQK;
+      ah[n] = sp(isp ? P::oQh : P::oKh);
+      al[n] = sp(isp ? P::oQl : P::oKl);
+      acc[n] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+    int ob[kSl];
+    op_bases(ob);
+    const short* bh = sp(P::oKh);
+    const short* bl = sp(P::oKl);
 #pragma unroll
     for (int sl = 0; sl < kSl; ++sl) {
-      s4 h0, l0, h1, l1;
-      split4(S[2 * sl], h0, l0);
-      split4(S[2 * sl + 1], h1, l1);
-      sbh[sl] = cat(h0, h1);
-      sbl[sl] = cat(l0, l1);
+      s8 xh[N], xl[N], yh[N], yl[N];
+#pragma unroll
+      for (int n = 0; n < N; ++n) {
+        xh[n] = *reinterpret_cast<const s8*>(ah[n] + ra[n] + ob[sl]);
+        xl[n] = *reinterpret_cast<const s8*>(al[n] + ra[n] + ob[sl]);
+        yh[n] = *reinterpret_cast<const s8*>(bh + rb[n] + ob[sl]);
+        yl[n] = *reinterpret_cast<const s8*>(bl + rb[n] + ob[sl]);
+      }
+#pragma unroll
+      for (int n = 0; n < N; ++n) acc[n] = mma32(xl[n], yh[n], acc[n]);
+#pragma unroll
+      for (int n = 0; n < N; ++n) acc[n] = mma32(xh[n], yl[n], acc[n]);
+#pragma unroll
+      for (int n = 0; n < N; ++n) acc[n] = mma32(xh[n], yh[n], acc[n]);
     }
+  }
+
+  // Scale and store an off-diagonal A tile or a P tile as (hi, lo).
+  __device__ void store_tile(int q, const f4& acc) const {
+    const int l = lane_now(), lr = l & 15, lg = l >> 4;
+    int ib, jb;
+    bool isp;
+    tile_of(q, ib, jb, isp);
+    const float* gt = fp(P::oGate);
+    const int i = 16 * jb + lr;
+    const float gi = gt[i];
+    short* dh = sp(isp ? P::oPh : P::oAh);
+    short* dl = sp(isp ? P::oPl : P::oAl);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = 16 * ib + 4 * lg + v;
+      const float dec = expf(gt[r] - gi);
+      const float val = isp ? (i <= r ? dec * acc[v] : 0.f) : gt[kC + r] * dec * acc[v];
+      short vh, vl;
+      split(val, vh, vl);
+      dh[r * P::kRowT + slot(i)] = vh;
+      dl[r * P::kRowT + slot(i)] = vl;
+    }
+  }
+
+  // Bl(X Y) from X in A-operand layout (X[lr][4 lg + v]) and Y in
+  // B-operand layout (Y[4 lg + v][lr]); the result is in B layout.  N
+  // independent products at once, their MFMAs interleaved.
+  template <int N>
+  __device__ __forceinline__ void mm(const f4 (&x)[N], const f4 (&y)[N], f4 (&r)[N]) const {
+    s4 xh[N], xl[N], yh[N], yl[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      split4(x[n], xh[n], xl[n]);
+      split4(y[n], yh[n], yl[n]);
+      r[n] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int n = 0; n < N; ++n) r[n] = mma16(xl[n], yh[n], r[n]);
+#pragma unroll
+    for (int n = 0; n < N; ++n) r[n] = mma16(xh[n], yl[n], r[n]);
+#pragma unroll
+    for (int n = 0; n < N; ++n) r[n] = mma16(xh[n], yh[n], r[n]);
+  }
+
+  // Diagonal block b from its raw K K^T tile G: N = the strictly lower block
+  // of A, X = (I + N)^{-1}, stored in A layout (X[lr][4 lg + v]) in the
+  // diagonal block of the A planes.  All factors are polynomials in N and
+  // commute, so X^T is built in B layout: X^T = Q2 + (N^8)^T Q2,
+  // Q2 = Q1 + (N^4)^T Q1, Q1 = I - N^T + (N^2)^T - N^T (N^2)^T.
+  __device__ void diag_inverse(int b, const f4& G) const {
+    const int l = lane_now(), lr = l & 15, lg = l >> 4;
+    const float* gt = fp(P::oGate);
+    const float gi = gt[16 * b + lr], bi = gt[kC + 16 * b + lr];
+    const f4 gr = *reinterpret_cast<const f4*>(gt + 16 * b + 4 * lg);
+    const f4 br = *reinterpret_cast<const f4*>(gt + kC + 16 * b + 4 * lg);
+    f4 nb, na, id;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int rv = 4 * lg + v;
+      nb[v] = lr < rv ? br[v] * expf(gr[v] - gi) * G[v] : 0.f;  // N[rv][lr]
+      na[v] = rv < lr ? bi * expf(gi - gr[v]) * G[v] : 0.f;     // N[lr][rv]
+      id[v] = rv == lr ? 1.f : 0.f;
+    }
+    f4 l1[2];                                   // N^2 in B and A layout
+    mm<2>({na, nb}, {nb, na}, l1);
+    f4 l2[3];                                   // N^4 (B, A), N^T (N^2)^T
+    mm<3>({l1[1], l1[0], nb}, {l1[0], l1[1], l1[1]}, l2);
+    const f4 q1 = id - na + l1[1] - l2[2];
+    f4 l3[2];                                   // N^8 (B), (N^4)^T Q1
+    mm<2>({l2[1], l2[0]}, {l2[0], q1}, l3);
+    const f4 q2 = q1 + l3[1];
+    f4 l4[1];
+    mm<1>({l3[0]}, {q2}, l4);
+    const f4 xt = q2 + l4[0];
+    s4 xh, xl;
+    split4(xt, xh, xl);
+    const int o = (16 * b + lr) * P::kRowT + slot(16 * b + 4 * lg);
+    *reinterpret_cast<s4*>(sp(P::oAh) + o) = xh;
+    *reinterpret_cast<s4*>(sp(P::oAl) + o) = xl;
+  }
+
+  __device__ void gram_phase() const {
+    if (wave < 4) {
+      const int q[2] = {16 + wave, 12 + wave};
+      f4 acc[2];
+      gram<2>(q, acc);
+      store_tile(q[1], acc[1]);
+      diag_inverse(wave, acc[0]);
+    } else {
+      const int q[3] = {(wave - 4) * 3, (wave - 4) * 3 + 1, (wave - 4) * 3 + 2};
+      f4 acc[3];
+      gram<3>(q, acc);
+#pragma unroll
+      for (int n = 0; n < 3; ++n) store_tile(q[n], acc[n]);
+    }
+  }
+
+  // ================= consumers =================
+  // The wave's 16 value columns for chunk c0.  S[d] holds rows
+  // 16d + 4 lg + v (key index) of S^T at column e0 + lr (value index).
+  __device__ void columns(int c0, f4 (&S)[kDt]) const {
+    const int l = lane_now(), lr = l & 15, lg = l >> 4;
+    const float* gt = fp(P::oGate);
+    const short* kh = sp(P::oKh);
+    const short* kl = sp(P::oKl);
+    const short* qh = sp(P::oQh);
+    const short* ql = sp(P::oQl);
     // K S0^T and Q S0^T, rows 16 tb + 4 lg + v
     f4 ks[4], qs[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       ks[tb] = f4{0.f, 0.f, 0.f, 0.f};
       qs[tb] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+    int ob[kSl];
+    op_bases(ob);
 #pragma unroll
-      for (int sl = 0; sl < kSl; ++sl) {
-        const int ra = (16 * tb + lr) * P::kRowQK + 32 * sl + 8 * lg;
-        ks[tb] = mma32x3(*reinterpret_cast<const s8*>(sp(P::oKh) + ra),
-                         *reinterpret_cast<const s8*>(sp(P::oKl) + ra), sbh[sl], sbl[sl], ks[tb]);
-        qs[tb] = mma32x3(*reinterpret_cast<const s8*>(sp(P::oQh) + ra),
-                         *reinterpret_cast<const s8*>(sp(P::oQl) + ra), sbh[sl], sbl[sl], qs[tb]);
+    for (int sl = 0; sl < kSl; ++sl) {
+      s8 xh[4], xl[4], yh[4], yl[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const int ra = 16 * tb * P::kRowQK + ob[sl];
+        xh[tb] = *reinterpret_cast<const s8*>(kh + ra);
+        xl[tb] = *reinterpret_cast<const s8*>(kl + ra);
+        yh[tb] = *reinterpret_cast<const s8*>(qh + ra);
+        yl[tb] = *reinterpret_cast<const s8*>(ql + ra);
+      }
+      s4 h0, l0, h1, l1;
+      split4(S[2 * sl], h0, l0);
+      split4(S[2 * sl + 1], h1, l1);
+      const s8 sbh = cat(h0, h1), sbl = cat(l0, l1);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        ks[tb] = mma32(xl[tb], sbh, ks[tb]);
+        qs[tb] = mma32(yl[tb], sbh, qs[tb]);
+      }
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        ks[tb] = mma32(xh[tb], sbl, ks[tb]);
+        qs[tb] = mma32(yh[tb], sbl, qs[tb]);
+      }
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        ks[tb] = mma32(xh[tb], sbh, ks[tb]);
+        qs[tb] = mma32(yh[tb], sbh, qs[tb]);
       }
     }
-    // value conv at this lane's column, R = V - e^g (K S0^T)
-    const int vch = 2 * a.Hk * DK + h * a.dv + e0 + lr;
-    f4 R[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      float xr[7];
-#pragma unroll
-      for (int r = 0; r < 7; ++r) xr[r] = row1(c0 + 16 * tb + 4 * lg - 3 + r, vch);
-      const f4 gam = *reinterpret_cast<const f4*>(gt + 2 * kC + 16 * tb + 4 * lg);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float y = bv;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) y = fmaf(wv[jj], xr[v + jj], y);
-        y = act(y);
-        if (c0 + 16 * tb + 4 * lg + v >= T) y = 0.f;
-        R[tb][v] = y - gam[v] * ks[tb][v];
-      }
-    }
-    // U_b = X_bb (b_b R_b - sum_{j<b} A_bj U_j)
+    // U_b = X_bb (b_b R_b - sum_{j<b} A_bj U_j),  R = V - e^g (K S0^T)
+    const float* vt = fp(P::oV) + (e0 % kCols + lr) * P::kRowV;
     f4 U[4];
     s4 uh[4], ul[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
       const int row = (16 * b + lr) * P::kRowT;
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (b > 0) {
+        s4 ah[3], al[3];
 #pragma unroll
-      for (int jb = 0; jb < b; ++jb) {
-        const int o = row + slot(16 * jb + 4 * lg);
-        acc = mma16x3(*reinterpret_cast<const s4*>(sp(P::oAh) + o),
-                      *reinterpret_cast<const s4*>(sp(P::oAl) + o), uh[jb], ul[jb], acc);
+        for (int jb = 0; jb < b; ++jb) {
+          const int o = row + slot(16 * jb + 4 * lg);
+          ah[jb] = *reinterpret_cast<const s4*>(sp(P::oAh) + o);
+          al[jb] = *reinterpret_cast<const s4*>(sp(P::oAl) + o);
+        }
+#pragma unroll
+        for (int jb = 0; jb < b; ++jb) acc = mma16(al[jb], uh[jb], acc);
+#pragma unroll
+        for (int jb = 0; jb < b; ++jb) acc = mma16(ah[jb], ul[jb], acc);
+#pragma unroll
+        for (int jb = 0; jb < b; ++jb) acc = mma16(ah[jb], uh[jb], acc);
       }
+      const int o = row + slot(16 * b + 4 * lg);
+      const s4 xh = *reinterpret_cast<const s4*>(sp(P::oAh) + o);
+      const s4 xl = *reinterpret_cast<const s4*>(sp(P::oAl) + o);
+      const f4 V = *reinterpret_cast<const f4*>(vt + 16 * b + 4 * lg);
+      const f4 gam = *reinterpret_cast<const f4*>(gt + 2 * kC + 16 * b + 4 * lg);
       const f4 bt = *reinterpret_cast<const f4*>(gt + kC + 16 * b + 4 * lg);
       s4 zh, zl;
-      split4(bt * R[b] - acc, zh, zl);
-      const int o = row + slot(16 * b + 4 * lg);
-      U[b] = mma16x3(*reinterpret_cast<const s4*>(sp(P::oAh) + o),
-                     *reinterpret_cast<const s4*>(sp(P::oAl) + o), zh, zl,
-                     f4{0.f, 0.f, 0.f, 0.f});
+      split4(bt * (V - gam * ks[b]) - acc, zh, zl);
+      U[b] = mma16x3(xh, xl, zh, zl, f4{0.f, 0.f, 0.f, 0.f});
       split4(U[b], uh[b], ul[b]);
     }
-    // O = e^g (Q S0^T) + P U
-    const int n = T - c0;
+    // O = e^g (Q S0^T) + P U: the six (block row, 32-slice) products at once
+    {
+      constexpr int kB[6] = {0, 1, 2, 2, 3, 3}, kU[6] = {0, 0, 0, 1, 0, 1};
+      s8 ph[6], pl[6];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const f4 gam = *reinterpret_cast<const f4*>(gt + 2 * kC + 16 * b + 4 * lg);
-      f4 o = gam * qs[b];
-      const int row = (16 * b + lr) * P::kRowT;
-#pragma unroll
-      for (int u = 0; 2 * u <= b; ++u) {
-        const int off = row + 32 * u + 8 * lg;
-        o = mma32x3(*reinterpret_cast<const s8*>(sp(P::oPh) + off),
-                    *reinterpret_cast<const s8*>(sp(P::oPl) + off), cat(uh[2 * u], uh[2 * u + 1]),
-                    cat(ul[2 * u], ul[2 * u + 1]), o);
+      for (int i = 0; i < 6; ++i) {
+        const int off = (16 * kB[i] + lr) * P::kRowT + 32 * kU[i] + 8 * lg;
+        ph[i] = *reinterpret_cast<const s8*>(sp(P::oPh) + off);
+        pl[i] = *reinterpret_cast<const s8*>(sp(P::oPl) + off);
       }
+      f4 o[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int t = 16 * b + 4 * lg + v;
-        if (t < n)
-          a.out[(static_cast<int64_t>(t0) + c0 + t) * a.Hv * a.dv + static_cast<int64_t>(h) * a.dv +
-                e0 + lr] = o[v];
-      }
+      for (int b = 0; b < 4; ++b)
+        o[b] = *reinterpret_cast<const f4*>(gt + 2 * kC + 16 * b + 4 * lg) * qs[b];
+      const s8 u0h = cat(uh[0], uh[1]), u0l = cat(ul[0], ul[1]);
+      const s8 u1h = cat(uh[2], uh[3]), u1l = cat(ul[2], ul[3]);
+#pragma unroll
+      for (int i = 0; i < 6; ++i) o[kB[i]] = mma32(pl[i], kU[i] ? u1h : u0h, o[kB[i]]);
+#pragma unroll
+      for (int i = 0; i < 6; ++i) o[kB[i]] = mma32(ph[i], kU[i] ? u1l : u0l, o[kB[i]]);
+#pragma unroll
+      for (int i = 0; i < 6; ++i) o[kB[i]] = mma32(ph[i], kU[i] ? u1h : u0h, o[kB[i]]);
+      // rows t >= T - c0 lie past the descriptor and are dropped
+      const int rs = a.Hv * a.dv;
+      const int n = T - c0 < kC ? T - c0 : kC;
+      const rsrc_t ro =
+          make_rsrc(a.out + ((static_cast<int64_t>(t0) + c0) * a.Hv + h) * a.dv + e0,
+                    static_cast<uint32_t>(n) * static_cast<uint32_t>(rs) * 4u);
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[b][v]), ro,
+                                                ((16 * b + 4 * lg + v) * rs + lr) * 4, 0, 0);
     }
-    // S^T <- e^{g_c} S^T + K^T diag(e^{g_c - g}) U
-    s4 wh[4], wl[4];
+    // S^T <- e^{g_c} S^T + K^T diag(e^{g_c - g}) U; K^T tiles by transposing
+    // reads of the K rows, four key tiles at a time.
+    s8 wh[2], wl[2];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const f4 gp = *reinterpret_cast<const f4*>(gt + 3 * kC + 16 * b + 4 * lg);
-      split4(gp * U[b], wh[b], wl[b]);
+    for (int u = 0; u < 2; ++u) {
+      const f4 g0 = *reinterpret_cast<const f4*>(gt + 3 * kC + 32 * u + 4 * lg);
+      const f4 g1 = *reinterpret_cast<const f4*>(gt + 3 * kC + 32 * u + 16 + 4 * lg);
+      s4 h0, l0, h1, l1;
+      split4(g0 * U[2 * u], h0, l0);
+      split4(g1 * U[2 * u + 1], h1, l1);
+      wh[u] = cat(h0, h1);
+      wl[u] = cat(l0, l1);
     }
     const float ec = gt[2 * kC + kC - 1];
+    // K^T tile d, 32-token slice u, half hf: rows 32u + 16hf + 4 lg + lr/4,
+    // slots 32 (d>>1) + 4 (d&1) + 8 (lr&3); a base per pair D = d >> 1 plus
+    // (32u + 16hf) rows and 4 (d&1) slots.
+    int tb0[kSl];
+    {
+      const int l = lane_now(), r = l & 15, g = l >> 4;
 #pragma unroll
-    for (int d = 0; d < kDt; ++d) {
-      f4 acc = ec * S[d];
+      for (int D = 0; D < kSl; ++D) tb0[D] = qk(4 * g + (r >> 2), 32 * D + 8 * (r & 3));
+    }
+    constexpr int kG = kDt < 4 ? kDt : 4;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int off = (16 * d + lr) * P::kRowT + 32 * u + 8 * lg;
-        acc = mma32x3(*reinterpret_cast<const s8*>(sp(P::oTh) + off),
-                      *reinterpret_cast<const s8*>(sp(P::oTl) + off),
-                      cat(wh[2 * u], wh[2 * u + 1]), cat(wl[2 * u], wl[2 * u + 1]), acc);
+    for (int d0 = 0; d0 < kDt; d0 += kG) {
+      s8 th[kG][2], tl[kG][2];
+      f4 acc[kG];
+#pragma unroll
+      for (int dd = 0; dd < kG; ++dd) {
+        const int d = d0 + dd;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int r0 = tb0[d >> 1] + 32 * u * P::kRowQK + 4 * (d & 1);
+          const int r1 = r0 + 16 * P::kRowQK;
+          th[dd][u] = cat(ld_tr(kh + r0), ld_tr(kh + r1));
+          tl[dd][u] = cat(ld_tr(kl + r0), ld_tr(kl + r1));
+        }
+        acc[dd] = ec * S[d];
       }
-      S[d] = acc;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int dd = 0; dd < kG; ++dd) acc[dd] = mma32(tl[dd][u], wh[u], acc[dd]);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int dd = 0; dd < kG; ++dd) acc[dd] = mma32(th[dd][u], wl[u], acc[dd]);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int dd = 0; dd < kG; ++dd) acc[dd] = mma32(th[dd][u], wh[u], acc[dd]);
+#pragma unroll
+      for (int dd = 0; dd < kG; ++dd) S[d0 + dd] = acc[dd];
     }
   }
 };
@@ -488,73 +827,89 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
   const int u = (nb % 8 == 0) ? (bid % 8) * (nb / 8) + bid / 8 : bid;
   const int j = u % a.nblk;
   k.h = (u / a.nblk) % a.Hv;
-  k.s = u / a.nblk / a.Hv;
+  const int s = u / a.nblk / a.Hv;
   k.hk = k.h / a.G;
-  k.e0 = j * kCols + k.wave * 16;
 
-  const int t0 = a.cu[k.s], t1 = a.cu[k.s + 1];
-  k.dst = a.dst[k.s];
-  k.init = a.init ? a.init[k.s] : k.dst;
-  if (t0 < 0 || t1 < t0 || t1 > a.total || k.dst < 0 || k.dst >= a.num_slots ||
+  const int t0 = a.cu[s], t1 = a.cu[s + 1];
+  const int32_t dst = a.dst[s];
+  k.init = a.init ? a.init[s] : dst;
+  if (t0 < 0 || t1 < t0 || t1 > a.total || dst < 0 || dst >= a.num_slots ||
       k.init >= a.num_slots)
     return;
   k.t0 = t0;
   k.T = t1 - t0;
-  const bool cols = k.e0 < a.dv;
+  const int nch = (k.T + kC - 1) / kC;
 
   // P and A planes: the blocks above the diagonal stay zero.
   for (int i = k.tid; i < 4 * P::kSq / 16; i += kThreads)
     reinterpret_cast<uint4*>(lds_raw + P::oPh)[i] = uint4{0u, 0u, 0u, 0u};
+  k.e0 = j * kCols;
+  k.load_taps();
 
-  // This thread's q / k conv channels (octet co, token octet tau) and the
-  // wave's value column.
-  const bool prep = k.tid < 8 * K::kNco;
-  const int co = k.tid % K::kNco, tau = k.tid / K::kNco;
-  float wt[8][4], bias[8];
-  {
-    const int oc = co >= K::kGrp ? co - K::kGrp : co;
-    const int ch = (co >= K::kGrp ? a.Hk * DK : 0) + k.hk * DK + 8 * oc;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) wt[m][jj] = prep ? k.tap(ch + m, jj) : 0.f;
-      bias[m] = (prep && a.bias) ? to_f32(static_cast<const Act*>(a.bias)[ch + m]) : 0.f;
+  if (k.tid < kProd) {
+    // ---------------- producers ----------------
+    typename K::Prod p;
+    k.prod_init(p);
+    if (nch > 0) k.prod_load(p, 0);
+    lds_barrier();            // planes zeroed, taps loaded
+    if (nch > 0) {
+      k.prod_prep(p, 0);
+      if (nch > 1) k.prod_load(p, kC);
+      k.prod_store(p);
+      lds_barrier();
+      k.gram_phase();
+      lds_barrier();
     }
-  }
-  float wv[4], bv = 0.f;
-  const int vch = 2 * a.Hk * DK + k.h * a.dv + k.e0 + k.lr;
+    for (int c = 0; c < nch; ++c) {
+      const bool next = c + 1 < nch;
+      if (next) {
+        k.prod_prep(p, (c + 1) * kC);
+        if (c + 2 < nch) k.prod_load(p, (c + 2) * kC);
+      }
+      lds_barrier();          // consumers are done with chunk c
+      if (next) {
+        k.prod_store(p);
+        lds_barrier();
+        k.gram_phase();
+        lds_barrier();
+      }
+    }
+  } else {
+    // ---------------- consumers ----------------
+    k.e0 = j * kCols + (k.wave - 4) * 16;
+    const bool cols = k.e0 < a.dv;
+    f4 S[K::kDt];
+    const int64_t head = static_cast<int64_t>(k.h) * a.dv * DK;
+    const int64_t slot_elems = static_cast<int64_t>(a.Hv) * a.dv * DK;
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) wv[jj] = cols ? k.tap(vch, jj) : 0.f;
-  if (cols && a.bias) bv = to_f32(static_cast<const Act*>(a.bias)[vch]);
-
-  f4 S[K::kDt];
-  const int64_t head = static_cast<int64_t>(k.h) * a.dv * DK;
-  const int64_t slot_elems = static_cast<int64_t>(a.Hv) * a.dv * DK;
+    for (int d = 0; d < K::kDt; ++d) {
+      S[d] = f4{0.f, 0.f, 0.f, 0.f};
+      if (cols && k.init >= 0)
+        S[d] = *reinterpret_cast<const f4*>(a.ssm + k.init * slot_elems + head +
+                                           static_cast<int64_t>(k.e0 + k.lr) * DK + 16 * d +
+                                           4 * k.lg);
+    }
+    lds_barrier();            // planes zeroed, taps loaded
+    if (nch > 0) {
+      lds_barrier();          // producers stored chunk 0
+      k.gram_phase();
+      lds_barrier();
+    }
+    for (int c = 0; c < nch; ++c) {
+      const bool next = c + 1 < nch;
+      if (cols) k.columns(c * kC, S);
+      lds_barrier();          // chunk c consumed
+      if (next) {
+        lds_barrier();        // producers stored chunk c + 1
+        k.gram_phase();
+        lds_barrier();
+      }
+    }
+    if (cols) {
+      float* out = a.ssm + dst * slot_elems + head + static_cast<int64_t>(k.e0 + k.lr) * DK;
 #pragma unroll
-  for (int d = 0; d < K::kDt; ++d) {
-    S[d] = f4{0.f, 0.f, 0.f, 0.f};
-    if (cols && k.init >= 0)
-      S[d] = *reinterpret_cast<const f4*>(a.ssm + k.init * slot_elems + head +
-                                         static_cast<int64_t>(k.e0 + k.lr) * DK + 16 * d +
-                                         4 * k.lg);
-  }
-
-  for (int c0 = 0; c0 < k.T; c0 += kC) {
-    if (prep) k.prep_qk(c0, co, tau, wt, bias);
-    if (k.wave == 3) k.gates(c0);
-    lds_barrier();
-    for (int q = k.wave; q < 20; q += 4) k.gram_tile(q);
-    lds_barrier();
-    if (k.lane < 16) k.diag_inverse(k.wave, k.lane);
-    lds_barrier();
-    if (cols) k.columns(c0, S, wv, bv);
-    lds_barrier();
-  }
-
-  if (cols) {
-    float* out = a.ssm + k.dst * slot_elems + head + static_cast<int64_t>(k.e0 + k.lr) * DK;
-#pragma unroll
-    for (int d = 0; d < K::kDt; ++d) *reinterpret_cast<f4*>(out + 16 * d + 4 * k.lg) = S[d];
+      for (int d = 0; d < K::kDt; ++d) *reinterpret_cast<f4*>(out + 16 * d + 4 * k.lg) = S[d];
+    }
   }
 }
 
