@@ -467,27 +467,8 @@ struct Prefill {
   }
 
   // ================= all waves: A, P and the diagonal inverses =========
-  // Tile coordinates: q < 6 an off-diagonal block of A, else block q - 6
-  // of P (lower, with the diagonal); q = 16 + b: diagonal block b of A.
-  __device__ __forceinline__ void tile_of(int q, int& ib, int& jb, bool& isp) const {
-    isp = q >= 6 && q < 16;
-    if (q >= 16) {
-      ib = jb = q - 16;
-    } else if (isp) {
-      const int p = q - 6;
-      ib = p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0;
-      jb = p - ib * (ib + 1) / 2;
-    } else {
-      ib = q >= 3 ? 3 : q >= 1 ? 2 : 1;
-      jb = q - (ib - 1) * ib / 2;
-    }
-  }
-
-  // Raw Gram tiles (K or Q rows ib) . (K rows jb)^T of N tiles at once: each
-  // slice's operands are read first, then the MFMAs run interleaved over the
-  // tiles' independent accumulators.
   // Element offsets, for rows 16 blk + lr, of the 16x16x32 operand slots
-  // 32 sl + 8 lg: a per-slice base plus 16 blk rows (swizzle depends on
+  // 32 sl + 8 lg: a per-slice base plus 16 blk rows (the swizzle depends on
   // the row only through lr).
   __device__ __forceinline__ void op_bases(int (&ob)[kSl]) const {
     const int l = lane_now(), r = l & 15, g = l >> 4;
@@ -495,65 +476,78 @@ struct Prefill {
     for (int sl = 0; sl < kSl; ++sl) ob[sl] = qk(r, 32 * sl + 8 * g);
   }
 
-  template <int N>
-  __device__ __forceinline__ void gram(const int (&q)[N], f4 (&acc)[N]) const {
-    int ra[N], rb[N];
-    const short *ah[N], *al[N];
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-      int ib, jb;
-      bool isp;
-      tile_of(q[n], ib, jb, isp);
-      ra[n] = 16 * ib * P::kRowQK;
-      rb[n] = 16 * jb * P::kRowQK;
-      ah[n] = sp(isp ? P::oQh : P::oKh);
-      al[n] = sp(isp ? P::oQl : P::oKl);
-      acc[n] = f4{0.f, 0.f, 0.f, 0.f};
-    }
-    int ob[kSl];
-    op_bases(ob);
-    const short* bh = sp(P::oKh);
-    const short* bl = sp(P::oKl);
+  // Block pair (IB, JB), IB >= JB: the K K^T and Q K^T blocks, computed
+  // transposed (A operand K rows JB, B operands K and Q rows IB) so that
+  // each lane holds row r = 16 IB + lr at the four columns 16 JB + 4 lg + v:
+  // they store as one 8-byte (hi, lo) group each.
+  template <int IB, int JB>
+  __device__ __forceinline__ void pair_gram(f4& g, f4& pq, const int (&ob)[kSl]) const {
+    const short* kh = sp(P::oKh);
+    const short* kl = sp(P::oKl);
+    const short* qh = sp(P::oQh);
+    const short* ql = sp(P::oQl);
+    g = f4{0.f, 0.f, 0.f, 0.f};
+    pq = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int sl = 0; sl < kSl; ++sl) {
-      s8 xh[N], xl[N], yh[N], yl[N];
-#pragma unroll
-      for (int n = 0; n < N; ++n) {
-        xh[n] = *reinterpret_cast<const s8*>(ah[n] + ra[n] + ob[sl]);
-        xl[n] = *reinterpret_cast<const s8*>(al[n] + ra[n] + ob[sl]);
-        yh[n] = *reinterpret_cast<const s8*>(bh + rb[n] + ob[sl]);
-        yl[n] = *reinterpret_cast<const s8*>(bl + rb[n] + ob[sl]);
-      }
-#pragma unroll
-      for (int n = 0; n < N; ++n) acc[n] = mma32(xl[n], yh[n], acc[n]);
-#pragma unroll
-      for (int n = 0; n < N; ++n) acc[n] = mma32(xh[n], yl[n], acc[n]);
-#pragma unroll
-      for (int n = 0; n < N; ++n) acc[n] = mma32(xh[n], yh[n], acc[n]);
+      const int oa = 16 * JB * P::kRowQK + ob[sl], obr = 16 * IB * P::kRowQK + ob[sl];
+      const s8 ah = *reinterpret_cast<const s8*>(kh + oa);
+      const s8 al = *reinterpret_cast<const s8*>(kl + oa);
+      const s8 bkh = IB == JB ? ah : *reinterpret_cast<const s8*>(kh + obr);
+      const s8 bkl = IB == JB ? al : *reinterpret_cast<const s8*>(kl + obr);
+      const s8 bqh = *reinterpret_cast<const s8*>(qh + obr);
+      const s8 bql = *reinterpret_cast<const s8*>(ql + obr);
+      g = mma32(al, bkh, g);
+      pq = mma32(al, bqh, pq);
+      g = mma32(ah, bkl, g);
+      pq = mma32(ah, bql, pq);
+      g = mma32(ah, bkh, g);
+      pq = mma32(ah, bqh, pq);
     }
   }
 
-  // Scale and store an off-diagonal A tile or a P tile as (hi, lo).
-  __device__ void store_tile(int q, const f4& acc) const {
+  // Scale a transposed pair and store it: A_ri = b_r e^{g_r - g_i} k_r.k_i
+  // (IB > JB only) and P_ri = e^{g_r - g_i} q_r.k_i (i <= r).
+  template <int IB, int JB>
+  __device__ __forceinline__ void pair_store(const f4& g, const f4& pq) const {
     const int l = lane_now(), lr = l & 15, lg = l >> 4;
-    int ib, jb;
-    bool isp;
-    tile_of(q, ib, jb, isp);
     const float* gt = fp(P::oGate);
-    const int i = 16 * jb + lr;
-    const float gi = gt[i];
-    short* dh = sp(isp ? P::oPh : P::oAh);
-    short* dl = sp(isp ? P::oPl : P::oAl);
+    const int r = 16 * IB + lr;
+    const float gr = gt[r];
+    const f4 gi = *reinterpret_cast<const f4*>(gt + 16 * JB + 4 * lg);
+    f4 dec;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = 16 * ib + 4 * lg + v;
-      const float dec = expf(gt[r] - gi);
-      const float val = isp ? (i <= r ? dec * acc[v] : 0.f) : gt[kC + r] * dec * acc[v];
-      short vh, vl;
-      split(val, vh, vl);
-      dh[r * P::kRowT + slot(i)] = vh;
-      dl[r * P::kRowT + slot(i)] = vl;
+    for (int v = 0; v < 4; ++v) dec[v] = __expf(gr - gi[v]);
+    const int o = r * P::kRowT + slot(16 * JB + 4 * lg);
+    f4 pv = dec * pq;
+    if (IB == JB) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (4 * lg + v > lr) pv[v] = 0.f;
     }
+    s4 h, lo;
+    split4(pv, h, lo);
+    *reinterpret_cast<s4*>(sp(P::oPh) + o) = h;
+    *reinterpret_cast<s4*>(sp(P::oPl) + o) = lo;
+    if (IB > JB) {
+      split4(gt[kC + r] * dec * g, h, lo);
+      *reinterpret_cast<s4*>(sp(P::oAh) + o) = h;
+      *reinterpret_cast<s4*>(sp(P::oAl) + o) = lo;
+    }
+  }
+
+  template <int IB, int JB>
+  __device__ __forceinline__ void pair(const int (&ob)[kSl]) const {
+    f4 g, pq;
+    pair_gram<IB, JB>(g, pq, ob);
+    pair_store<IB, JB>(g, pq);
+  }
+  template <int B>
+  __device__ __forceinline__ void diag_pair(const int (&ob)[kSl]) const {
+    f4 g, pq;
+    pair_gram<B, B>(g, pq, ob);
+    pair_store<B, B>(g, pq);
+    diag_inverse(B, g);
   }
 
   // Bl(X Y) from X in A-operand layout (X[lr][4 lg + v]) and Y in
@@ -591,8 +585,8 @@ struct Prefill {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int rv = 4 * lg + v;
-      nb[v] = lr < rv ? br[v] * expf(gr[v] - gi) * G[v] : 0.f;  // N[rv][lr]
-      na[v] = rv < lr ? bi * expf(gi - gr[v]) * G[v] : 0.f;     // N[lr][rv]
+      nb[v] = lr < rv ? br[v] * __expf(gr[v] - gi) * G[v] : 0.f;  // N[rv][lr]
+      na[v] = rv < lr ? bi * __expf(gi - gr[v]) * G[v] : 0.f;     // N[lr][rv]
       id[v] = rv == lr ? 1.f : 0.f;
     }
     f4 l1[2];                                   // N^2 in B and A layout
@@ -613,19 +607,20 @@ struct Prefill {
     *reinterpret_cast<s4*>(sp(P::oAl) + o) = xl;
   }
 
+  // The 10 block pairs over 8 waves: waves 0-3 a diagonal pair each (with
+  // the inverse of that block of I + A), waves 4-7 the 6 off-diagonal pairs.
   __device__ void gram_phase() const {
-    if (wave < 4) {
-      const int q[2] = {16 + wave, 12 + wave};
-      f4 acc[2];
-      gram<2>(q, acc);
-      store_tile(q[1], acc[1]);
-      diag_inverse(wave, acc[0]);
-    } else {
-      const int q[3] = {(wave - 4) * 3, (wave - 4) * 3 + 1, (wave - 4) * 3 + 2};
-      f4 acc[3];
-      gram<3>(q, acc);
-#pragma unroll
-      for (int n = 0; n < 3; ++n) store_tile(q[n], acc[n]);
+    int ob[kSl];
+    op_bases(ob);
+    switch (wave) {
+      case 0: diag_pair<0>(ob); break;
+      case 1: diag_pair<1>(ob); break;
+      case 2: diag_pair<2>(ob); break;
+      case 3: diag_pair<3>(ob); break;
+      case 4: pair<1, 0>(ob); pair<2, 1>(ob); break;
+      case 5: pair<2, 0>(ob); pair<3, 2>(ob); break;
+      case 6: pair<3, 0>(ob); break;
+      default: pair<3, 1>(ob); break;
     }
   }
 
@@ -813,7 +808,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
   using P = Plan<DK>;
   K k{a, lds_raw};
   k.tid = threadIdx.x;
-  k.wave = k.tid >> 6;
+  k.wave = __builtin_amdgcn_readfirstlane(k.tid >> 6);  // uniform: offsets from it stay scalar
   k.lane = k.tid & 63;
   k.lr = k.lane & 15;
   k.lg = k.lane >> 4;
