@@ -47,6 +47,7 @@ namespace {
 constexpr int kMaxW1 = 3;                 // conv_width <= 4
 constexpr int kBatch = 2;                 // later tokens whose x are loaded together
 constexpr int kMaxUnitsPerCta = 512;      // slot-table entries per workgroup
+constexpr int kRawIt = 6;                 // raw-input copies per lane with precomputed offsets
 constexpr size_t kLdsBytes = 160 * 1024;  // LDS of one gfx950 CU
 
 // Lane layout of a state row of d_k fp32: LPR lanes, each holding CPL 16-byte
@@ -60,13 +61,14 @@ struct RowMap {
 };
 
 // LDS plan of a workgroup, in dwords: per-wave state stages | two raw-input
-// buffers | two activation buffers | slot table.
+// buffers (the next unit's copies land while this unit reads its own) | one
+// activation buffer | slot table of the workgroup's units.
 struct LdsPlan {
   int stage_per_wave, raw_len, act_len;
   int raw, act, slots, total;
 };
 __host__ __device__ inline LdsPlan lds_plan(int dk, int rpw, int waves, int Cg, int W1, int GA,
-                                            int G, int tchunk) {
+                                            int G, int tchunk, int units = kMaxUnitsPerCta) {
   LdsPlan p;
   const int rpp = dk >= 64 ? 4 : 256 / dk;
   const int cpl = dk >= 64 ? dk / 64 : 1;
@@ -75,8 +77,8 @@ __host__ __device__ inline LdsPlan lds_plan(int dk, int rpw, int waves, int Cg, 
   p.act_len = tchunk * (Cg + GA + G + 4);
   p.raw = waves * p.stage_per_wave;
   p.act = p.raw + 2 * p.raw_len;
-  p.slots = p.act + 2 * p.act_len;
-  p.total = p.slots + kMaxUnitsPerCta;
+  p.slots = p.act + p.act_len;
+  p.total = p.slots + units;
   return p;
 }
 
@@ -97,6 +99,9 @@ struct DecodeCta {
   uint32_t lane_off;  // this lane's first state element within a unit
   uint32_t chan;      // global conv channel of this thread (tid < Cg)
   LdsPlan plan;
+  // element offset, within its source block (x row | conv window | gates |
+  // betas), of raw input j*64 + lane for this wave's first kRawIt values of j
+  uint32_t roff[kRawIt];
 
   __device__ __forceinline__ DecodeCta(const DecodeArgs& args) : a(args) {
     tid = threadIdx.x;
@@ -128,6 +133,19 @@ struct DecodeCta {
     lane_off = static_cast<uint32_t>(wave * RPW + lr * NR) * DK + 4 * lc;
     chan = channel(tid < Cg ? tid : 0);
     plan = lds_plan(DK, RPW, nwaves, Cg, W1, GA, G, TC);
+#pragma unroll
+    for (int i = 0; i < kRawIt; ++i) roff[i] = raw_offset((wave + i * nwaves) * 64 + lane);
+  }
+
+  // Offset of raw input d within its source block (see copy_unit).
+  __device__ __forceinline__ uint32_t raw_offset(int d) const {
+    const int nx = Cg * (1 + W1);
+    if (d < Cg) return channel(d);
+    if (d < nx) {
+      const int r = (d - Cg) / Cg;
+      return static_cast<uint32_t>(r) * C + channel(d - Cg - r * Cg);
+    }
+    return d < nx + GA ? d - nx : d - nx - GA;
   }
 
   // global conv channel of local channel c (q | k | v of this key head)
@@ -167,21 +185,17 @@ struct DecodeCta {
     const Act* al = static_cast<const Act*>(a.alpha) + th * DKA;
     const Act* be = static_cast<const Act*>(a.beta) + th;
     const int nx = Cg * (1 + W1);
-    for (int j = wave; j * 64 < plan.raw_len; j += nwaves) {
+    int i = 0;
+    for (int j = wave; j * 64 < plan.raw_len; j += nwaves, ++i) {
       const int d = j * 64 + lane;
       if (d < plan.raw_len) {
-        const Act* p;
-        if (d < Cg) {
-          p = x0 + channel(d);
-        } else if (d < nx) {
-          const int r = (d - Cg) / Cg;
-          p = cs + static_cast<uint32_t>(r) * C + channel(d - Cg - r * Cg);
-        } else if (d < nx + GA) {
-          p = al + (d - nx);
-        } else {
-          p = be + (d - nx - GA);
-        }
-        lds_dma<sizeof(Act)>(p, raw + j * 64);
+        uint32_t off = 0;
+#pragma unroll
+        for (int q = 0; q < kRawIt; ++q)
+          if (q == i) off = roff[q];
+        if (i >= kRawIt) off = raw_offset(d);
+        const Act* base = d < Cg ? x0 : d < nx ? cs : d < nx + GA ? al : be;
+        lds_dma<sizeof(Act)>(base + off, raw + j * 64);
       }
     }
   }
@@ -208,7 +222,7 @@ struct DecodeCta {
 #pragma unroll
     for (int j = 0; j + 1 < kMaxW1; ++j) win[j] = j >= lead ? win[j + 1] : 0.f;
     win[kMaxW1 - 1] = xv;
-    if (a.silu) y = y / (1.0f + expf(-y));
+    if (a.silu) y = y * __builtin_amdgcn_rcpf(1.0f + __expf(-y));
     act[tid] = y;
     Act* wdst = nullptr;
     if (spec)
@@ -393,8 +407,11 @@ struct DecodeCta {
   }
 };
 
+// Units of at most 16 rows per wave (single-head groups such as KDA's) have
+// 64 KiB stages, so two workgroups share a CU when the registers allow four
+// waves per SIMD.
 template <int DK, int RPW, typename Act, bool KDA>
-__global__ void __launch_bounds__(512, 2) decode_kernel(const DecodeArgs a) {
+__global__ void __launch_bounds__(512, RPW <= 16 ? 4 : 2) decode_kernel(const DecodeArgs a) {
   using Cta = DecodeCta<DK, RPW, Act, KDA>;
   const Cta cta(a);
   extern __shared__ __attribute__((aligned(16))) float lds[];
@@ -434,7 +451,9 @@ __global__ void __launch_bounds__(512, 2) decode_kernel(const DecodeArgs a) {
   for (int k = 0; k < mine; ++k) {
     const int b = cta.b0 + k * cta.m;
     uint32_t* const raw = raw0 + (k & 1) * P.raw_len;
-    float* const act = act0 + (k & 1) * P.act_len;
+    // one activation buffer: the barrier above ends every wave's reads of
+    // the previous unit's activations before this unit writes them
+    float* const act = act0;
     // drain: this unit's copies (and the previous unit's stores) are done
     vm_wait<0>();
     if (sl >= 0) {
@@ -450,10 +469,11 @@ __global__ void __launch_bounds__(512, 2) decode_kernel(const DecodeArgs a) {
 }
 
 // Dynamic LDS bytes of the decode kernel for a shape and token chunk.
-size_t decode_lds_bytes(int dk, int rpw, int G, int dv, int W1, int kda, int tchunk) {
+size_t decode_lds_bytes(int dk, int rpw, int G, int dv, int W1, int kda, int tchunk,
+                        int units = kMaxUnitsPerCta) {
   const int waves = G * dv / rpw;
   const int Cg = 2 * dk + G * dv;
-  const LdsPlan p = lds_plan(dk, rpw, waves, Cg, W1, G * (kda ? dk : 1), G, tchunk);
+  const LdsPlan p = lds_plan(dk, rpw, waves, Cg, W1, G * (kda ? dk : 1), G, tchunk, units);
   return sizeof(float) * static_cast<size_t>(p.total);
 }
 
@@ -529,27 +549,38 @@ hipError_t launch_decode(const DecodeArgs& args, int dk, int act_bf16, int kda, 
   const int W1 = args.W - 1;
   const int rpw = decode_rows_per_wave(dk, args.G, args.dv, W1, kda);
   if (!rpw) return hipErrorInvalidValue;
-  // tokens whose activations are staged in LDS at once: what fits next to
-  // the stages, raw buffers and slot table
-  DecodeArgs a = args;
-  int tc = 1;
-  while (tc < args.T && decode_lds_bytes(dk, rpw, args.G, args.dv, W1, kda, tc + 1) <= kLdsBytes)
-    ++tc;
-  a.tchunk = tc;
-  const size_t lds = decode_lds_bytes(dk, rpw, args.G, args.dv, W1, kda, tc);
-  // persistent grid: H_k * m workgroups, m ~ 2 CUs / H_k -- twice what fits
-  // at once, so the dispatcher hands the second half to whichever CUs finish
-  // first (per-XCD bandwidth differs from call to call); at least one
-  // request per workgroup, at most kMaxUnitsPerCta units each
+  // persistent grid: H_k * m workgroups, m ~ 2 * (workgroups per CU) * CUs
+  // / H_k -- twice what fits at once, so the dispatcher hands the second half
+  // to whichever CUs finish first (per-XCD bandwidth differs from call to
+  // call); at least one request per workgroup, at most kMaxUnitsPerCta units
+  // each.  Workgroups per CU: what the LDS plan allows (2 for single-head
+  // units such as KDA's 64 KiB stages, else 1).
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess || cus <= 0) return e != hipSuccess ? e : hipErrorInvalidDevice;
-  int64_t m = 2 * static_cast<int64_t>(cus) / args.Hk;
+  const int per_cu =
+      args.T == 1 && 2 * decode_lds_bytes(dk, rpw, args.G, args.dv, W1, kda, 1,
+                                          (args.B + cus - 1) / cus) <= kLdsBytes
+          ? 2
+          : 1;
+  int64_t m = 2 * per_cu * static_cast<int64_t>(cus) / args.Hk;
   if (m < 1) m = 1;
   const int64_t m_min = (args.B + kMaxUnitsPerCta - 1) / kMaxUnitsPerCta;
   if (m < m_min) m = m_min;
   if (m > args.B) m = args.B;
+  // slot-table entries: the units of the busiest workgroup (a small table
+  // lets two workgroups share a CU when the state stages allow it)
+  const int units = static_cast<int>((args.B + m - 1) / m);
+  // tokens whose activations are staged in LDS at once: what fits next to
+  // the stages, raw buffers and slot table
+  DecodeArgs a = args;
+  int tc = 1;
+  while (tc < args.T &&
+         decode_lds_bytes(dk, rpw, args.G, args.dv, W1, kda, tc + 1, units) <= kLdsBytes)
+    ++tc;
+  a.tchunk = tc;
+  const size_t lds = decode_lds_bytes(dk, rpw, args.G, args.dv, W1, kda, tc, units);
   const int64_t ctas = m * args.Hk;
   if (ctas < 1 || ctas > INT32_MAX) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(ctas));
