@@ -111,3 +111,31 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(gdn, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         gdn.lib()
+
+
+def prefill(L, N=2, dst=FAKE, init=None, cu=FAKE, max_len=64, total=128, chunk=64, inp=None,
+            out=FAKE):
+    pool = GdnPool(FAKE, FAKE, 8)
+    inp = inp or GdnInputs(FAKE, FAKE, FAKE, FAKE, None)
+    return gdn.lib().gdn_prefill_chunked(ct.byref(L), ct.byref(pool), dst, init, N, cu,
+                                         max_len, total, chunk, ct.byref(inp), out, None, 0,
+                                         None)
+
+
+def test_bad_prefill_arguments():
+    L = qwen_layer()
+    assert prefill(L, N=-1) == gdn.GDN_ERR_BAD_SHAPE
+    assert prefill(L, max_len=-1) == gdn.GDN_ERR_BAD_SHAPE
+    assert prefill(L, chunk=32) == gdn.GDN_ERR_UNSUPPORTED
+    assert prefill(qwen_layer(gate="channel")) == gdn.GDN_ERR_UNSUPPORTED
+    assert prefill(qwen_layer(n_k_heads=2, n_v_heads=2, d_k=16, d_v=16)) == \
+        gdn.GDN_ERR_UNSUPPORTED
+    assert prefill(L, dst=None) == gdn.GDN_ERR_NULL_ARG
+    assert prefill(L, cu=None) == gdn.GDN_ERR_NULL_ARG
+    assert prefill(L, inp=GdnInputs(None, FAKE, FAKE, FAKE, None)) == gdn.GDN_ERR_NULL_ARG
+    assert prefill(L, out=None) == gdn.GDN_ERR_NULL_ARG
+    misaligned = GdnInputs(ct.c_void_p(0x10002), FAKE, FAKE, FAKE, None)
+    assert prefill(L, inp=misaligned) == gdn.GDN_ERR_BAD_SHAPE
+    assert prefill(L, N=0) == gdn.GDN_OK                  # nothing to do, nothing enqueued
+    # the fused kernel keeps every intermediate on chip
+    assert gdn.lib().gdn_prefill_workspace_size(ct.byref(L), 4, 8192, 32768, 64) == 0
