@@ -297,8 +297,11 @@ def prefill_counts(shape, seqlens):
     (K K^T, Q K^T, T V, W = T diag(e^g) K: 5.24 M) and the state pass
     (W S0^T, Q S0^T, P U, U^T K: 6.29 M) -- 11.53 MFLOP at d = 128.
     issued: per workgroup (64 value columns) and chunk, 20 Gram tiles and 4
-    waves of K S0^T, Q S0^T, P U and state-update tiles on 16x16x32 MFMAs,
-    the U solve on 16x16x16 MFMAs, each product three times (hi/lo split)."""
+    waves of K S0^T, Q S0^T, P U and state-update tiles on 16x16x32 MFMAs;
+    on 16x16x16 MFMAs the U solve (10 block products per wave) and the four
+    diagonal-block inverses (8 products each); every product three times
+    (hi/lo split).  rocprofv3's SQ_INSTS_VALU_MFMA_MOPS_BF16 (x 512 FLOP)
+    agrees with this count."""
     act = 2 if shape.dtype == "bf16" else 4
     C, Hv, dk, dv = shape.channels, shape.n_v_heads, shape.d_k, shape.d_v
     total = int(sum(seqlens))
@@ -313,7 +316,7 @@ def prefill_counts(shape, seqlens):
     nblk = -(-dv // 64)
     ksl, kdt = dk // 32, dk // 16
     m32 = 20 * ksl * 3 + 4 * (4 * ksl * 2 * 3 + 6 * 3 + kdt * 2 * 3)
-    m16 = 4 * 10 * 3
+    m16 = 4 * 10 * 3 + 4 * 8 * 3
     issued = (m32 * 16 * 16 * 32 * 2 + m16 * 16 * 16 * 16 * 2) * chunks * Hv * nblk
     return nbytes, flops, issued
 
