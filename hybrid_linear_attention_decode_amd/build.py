@@ -21,7 +21,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gdn_api.hip", "gdn_decode.hip", "gdn_prefill.hip", "gdn_slots.hip"]
+SOURCES = ["gdn_api.hip", "gdn_decode.hip", "gdn_prefill.hip", "gdn_slots.hip", "kda_prefill.hip"]
 ARCH = "gfx950"
 
 

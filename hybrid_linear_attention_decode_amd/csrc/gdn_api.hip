@@ -179,13 +179,12 @@ gdn_status gdn_slot_zero(const gdn_layer* L, const gdn_pool* P, const int32_t* i
 
 size_t gdn_prefill_workspace_size(const gdn_layer* L, int32_t N, int32_t max_seqlen,
                                   int32_t total_tokens, int32_t chunk) {
-  // The fused kernel keeps every intermediate in registers and LDS.
-  (void)L;
-  (void)N;
-  (void)max_seqlen;
-  (void)total_tokens;
-  (void)chunk;
-  return 0;
+  if (check_layer(L) != GDN_OK || N < 0 || max_seqlen < 0 || total_tokens < 0 || chunk != 64)
+    return 0;
+  // The scalar-decay kernel keeps every intermediate in registers and LDS;
+  // the per-channel one stores the diagonal blocks of each chunk.
+  if (L->gate != GDN_GATE_CHANNEL) return 0;
+  return gdn::kda_workspace_bytes(L->n_v_heads, N, total_tokens);
 }
 
 gdn_status gdn_prefill_chunked(const gdn_layer* L, const gdn_pool* P, const int32_t* dst,
@@ -193,8 +192,6 @@ gdn_status gdn_prefill_chunked(const gdn_layer* L, const gdn_pool* P, const int3
                                int32_t max_seqlen, int32_t total_tokens, int32_t chunk,
                                const gdn_inputs* in, float* out, void* workspace,
                                size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   gdn_status st = check_layer(L);
   if (st != GDN_OK) return st;
   if ((st = check_pool(L, P)) != GDN_OK) return st;
@@ -209,6 +206,13 @@ gdn_status gdn_prefill_chunked(const gdn_layer* L, const gdn_pool* P, const int3
     return GDN_ERR_NULL_ARG;
   if (in->x && !aligned16(in->x)) return GDN_ERR_BAD_SHAPE;
   if (out && !aligned16(out)) return GDN_ERR_BAD_SHAPE;
+  const bool kda = L->gate == GDN_GATE_CHANNEL;
+  if (kda && total_tokens > 0) {
+    if (in->alpha && !aligned16(in->alpha)) return GDN_ERR_BAD_SHAPE;
+    const size_t need = gdn::kda_workspace_bytes(L->n_v_heads, N, total_tokens);
+    if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255))
+      return GDN_ERR_WORKSPACE;
+  }
 
   gdn::PrefillArgs a{};
   a.Hk = L->n_k_heads;
@@ -236,8 +240,11 @@ gdn_status gdn_prefill_chunked(const gdn_layer* L, const gdn_pool* P, const int3
   a.w = in->conv_w;
   a.bias = in->conv_b;
   a.out = out;
-  return from_hip(gdn::launch_prefill(a, L->d_k, L->act_dtype == GDN_BF16,
-                                      static_cast<hipStream_t>(stream)));
+  a.ws = workspace;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (kda)
+    return from_hip(gdn::launch_prefill_kda(a, L->d_k, L->act_dtype == GDN_BF16, max_seqlen, hs));
+  return from_hip(gdn::launch_prefill(a, L->d_k, L->act_dtype == GDN_BF16, hs));
 }
 
 }  // extern "C"

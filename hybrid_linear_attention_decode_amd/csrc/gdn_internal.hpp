@@ -1,6 +1,6 @@
 // gdn_internal.hpp -- argument blocks shared by the C-ABI entry points
 // (gdn_api.hip) and the kernel launchers (gdn_decode.hip, gdn_slots.hip,
-// gdn_prefill.hip).  Host-visible only; no device code here.
+// gdn_prefill.hip, kda_prefill.hip).  Host-visible only; no device code here.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -62,11 +62,12 @@ struct PrefillArgs {
   const int32_t* init;       // [N] or nullptr (= dst)
   const int32_t* cu;         // [N+1]
   const void* x;             // [total][C]
-  const void* alpha;         // [total][Hv]
+  const void* alpha;         // [total][Hv] or [total][Hv][dk]
   const void* beta;          // [total][Hv]
   const void* w;             // [C][W]
   const void* bias;          // [C] or nullptr
   float* out;                // [total][Hv][dv]
+  void* ws;                  // per-channel decay: diagonal-block records (workspace)
 };
 
 // Launchers: return hipSuccess or the launch error.  The caller has validated
@@ -74,6 +75,10 @@ struct PrefillArgs {
 hipError_t launch_decode(const DecodeArgs& a, int dk, int act_bf16, int kda, hipStream_t s);
 hipError_t launch_slots(const SlotArgs& a, SlotMode mode, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int dk, int act_bf16, hipStream_t s);
+hipError_t launch_prefill_kda(const PrefillArgs& a, int dk, int act_bf16, int max_seqlen,
+                              hipStream_t s);
+// Workspace bytes of the per-channel-decay prefill for N sequences of total tokens.
+size_t kda_workspace_bytes(int Hv, int64_t N, int64_t total);
 
 // Rows of state per wave of the decode kernel for a shape; 0 when unsupported.
 int decode_rows_per_wave(int dk, int G, int dv, int W1, int kda);

@@ -1,0 +1,1001 @@
+// kda_prefill.hip -- chunked prefill of the delta rule with a per-channel
+// decay (Kimi Delta Attention) on gfx950.
+//
+// The recurrence S_t = S_{t-1} diag(a_t) (I - b_t k_t k_t^T) + b_t v_t k_t^T,
+// o_t = S_t q_t, a_t in [0, 1]^{d_k} (one decay per key channel), evaluated
+// 64 tokens at a time in the WY / UT form of the delta rule (Yang et al.,
+// "Parallelizing Linear Transformers with the Delta Rule over Sequence
+// Length", 2024, sec. 3) with the fine-grained gate of Kimi Delta Attention.
+// With g_t = sum_{s <= t} log a_s (per channel, inside the chunk):
+//   A_ri = b_r sum_c k_rc k_ic e^{g_rc - g_ic}          (i < r)
+//   P_ri =     sum_c q_rc k_ic e^{g_rc - g_ic}          (i <= r)
+//   (I + A) U = diag(b) (V - (K o e^g) S0^T)
+//   O = (Q o e^g) S0^T + P U
+//   S^T = diag(e^{g_c}) S0^T + (K o e^{g_c - g})^T U
+// A per-channel decay does not factor out of the products as a row scale,
+// and e^{-g} overflows fp32 after a few strongly decaying tokens, so every
+// factor is taken relative to a 16-token block boundary and stays <= 1:
+// for token t in block R (boundary b_R = the token before the block),
+//   E_t = prod_{b_R < s <= t} a_s,  F_t = prod_{t < s <= last of R} a_s,
+//   Lam_R = prod over the whole block R;
+//   KE = K o E, QE = Q o E, KF = K o F (bf16 hi/lo planes in LDS);
+//   off-diagonal block pair (R, I), I < R:
+//     A_RI = diag(b_R) KE_R diag(D_RI) KF_I^T,  P_RI = QE_R diag(D_RI) KF_I^T,
+//     D_RI = prod_{I < J < R} Lam_J;
+//   K o e^g on block R = KE_R diag(e^{G_R}), e^{G_R} = prod_{J < R} Lam_J,
+//     applied to S0^T instead (a per-channel scale of the contraction);
+//   K o e^{g_c - g} on block I = KF_I diag(f_I), f_I = prod_{J > I} Lam_J,
+//     applied to the block's partial sum of the state update.
+// The four diagonal 16 x 16 blocks need e^{g_r - g_i} inside one block, which
+// has no bounded factorisation; they are formed exactly, with products of
+// the decays, by a first kernel (kda_diag_kernel) that also inverts each
+// block of I + A by forward substitution in fp32.  The second kernel
+// (kda_chunk_kernel) has the work split and pipeline of the scalar-decay
+// kernel (gdn_prefill.hip): producers prepare the next chunk (conv1d, SiLU,
+// L2 norm, the decay products and the three planes), all waves form the six
+// off-diagonal blocks, and four consumer waves carry 16 value columns each.
+#include "prefill_common.hpp"
+
+namespace gdn {
+namespace {
+
+constexpr int kBlk = 16;           // tokens per diagonal block
+constexpr int kWsBlockBytes = 2048;  // one diagonal block: X, P as (hi, lo)
+
+// Workspace block of token block jb of sequence s (start t0): sequences are
+// laid out at floor(t0 / 16) + 4 min(s, t0) blocks, which leaves room for
+// their 4 ceil(T / 64) blocks whatever the lengths; the whole call needs
+// floor(total / 16) + 4 min(N, total) blocks per value head.
+__device__ __forceinline__ int64_t ws_block(int s, int t0, int jb) {
+  return static_cast<int64_t>(t0 / kBlk) + 4 * static_cast<int64_t>(s < t0 ? s : t0) + jb;
+}
+
+// =====================================================================
+// Kernel 1: the diagonal 16 x 16 blocks, one wave per (sequence, value
+// head, token block).  Workspace record (2 KiB): lane l = 4 r + q holds
+// columns 4q..4q+3 of row r as X hi, X lo, P hi, P lo (4 bf16 each), where
+// X = (I + N)^{-1}, N_ri = b_r sum_c k_rc k_ic prod_{i < s <= r} a_sc
+// (i < r), and P_ri = sum_c q_rc k_ic prod_{i < s <= r} a_sc (i <= r).
+// =====================================================================
+template <int DK>
+struct DiagPlan {
+  static constexpr int kRow = DK + 4;            // fp32 per row of q, k, a (padded)
+  static constexpr int oQ = 0;
+  static constexpr int oK = oQ + kBlk * kRow * 4;
+  static constexpr int oA = oK + kBlk * kRow * 4;
+  static constexpr int oN = oA + kBlk * kRow * 4;  // fp32 [16][16]
+  static constexpr int oP = oN + kBlk * kBlk * 4;
+  static constexpr int oX = oP + kBlk * kBlk * 4;
+  static constexpr int oBeta = oX + kBlk * kBlk * 4;
+  static constexpr int kBytes = oBeta + kBlk * 4;
+};
+
+template <int DK, typename Act>
+__global__ void __launch_bounds__(64) kda_diag_kernel(PrefillArgs a) {
+  using DP = DiagPlan<DK>;
+  constexpr int kGrp = DK / 8;       // channel octets per head
+  constexpr int kTpl = kGrp / 2;     // tokens per lane in the conv stage
+  constexpr int kCw = DK / 8;        // channels per lane in the pair stage
+  __shared__ __align__(16) unsigned char lds[DP::kBytes];
+  float* yq = reinterpret_cast<float*>(lds + DP::oQ);
+  float* yk = reinterpret_cast<float*>(lds + DP::oK);
+  float* al = reinterpret_cast<float*>(lds + DP::oA);
+  float* nm = reinterpret_cast<float*>(lds + DP::oN);
+  float* pm = reinterpret_cast<float*>(lds + DP::oP);
+  float* xm = reinterpret_cast<float*>(lds + DP::oX);
+  float* bt = reinterpret_cast<float*>(lds + DP::oBeta);
+
+  const int lane = threadIdx.x;
+  const int s = blockIdx.x / a.Hv, h = blockIdx.x % a.Hv;
+  const int t0 = a.cu[s], t1 = a.cu[s + 1];
+  const int32_t dst = a.dst[s];
+  const int32_t init = a.init ? a.init[s] : dst;
+  if (t0 < 0 || t1 < t0 || t1 > a.total || dst < 0 || dst >= a.num_slots || init >= a.num_slots)
+    return;
+  const int T = t1 - t0;
+  const int nb = 4 * ((T + kC - 1) / kC);
+  if (static_cast<int>(blockIdx.y) >= nb) return;
+
+  PrefillCore<DK, Act> core{a, lds};
+  core.t0 = t0;
+  core.T = T;
+  core.init = init;
+  core.h = h;
+  core.hk = h / a.G;
+
+  // conv stage: lane = (channel octet co of q | k, token group tg)
+  const int co = lane % (2 * kGrp), tg = lane / (2 * kGrp);
+  const bool isk = co >= kGrp;
+  const int oc = isk ? co - kGrp : co;
+  const int ch = (isk ? a.Hk * DK : 0) + core.hk * DK + 8 * oc;
+  f4 wt[8];
+  float bias[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    wt[m] = f4{core.tap(ch + m, 0), core.tap(ch + m, 1), core.tap(ch + m, 2), core.tap(ch + m, 3)};
+    bias[m] = a.bias ? to_f32(static_cast<const Act*>(a.bias)[ch + m]) : 0.f;
+  }
+  // pair stage: lane = (channel group cg, column pair cp): columns cp and
+  // 15 - cp, 17 (row, column) steps in all, channels cg * kCw ..
+  const int cg = lane & 7, cp = lane >> 3;
+  for (int i = lane; i < 2 * kBlk * kBlk; i += 64) nm[i] = 0.f;  // N and P: upper parts stay 0
+
+  for (int jb = blockIdx.y; jb < nb; jb += gridDim.y) {
+    const int tb = jb * kBlk;   // first token of the block
+    // ---- conv1d + SiLU + L2 norm of q and k ----
+    {
+      const rsrc_t rx = core.x_rows(tb);
+      Row8<Act> raw[kTpl + 3];
+#pragma unroll
+      for (int r = 0; r < kTpl + 3; ++r)
+        raw[r].load(rx, core.x_off(tb, tb + kTpl * tg - 3 + r, ch));
+      if (tb == 0) {
+        const rsrc_t rw = core.win_rows();
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+          Row8<Act> wr;
+          wr.load(rw, core.win_off(kTpl * tg - 3 + r, ch));
+          raw[r].merge(wr);
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < kTpl; ++tt) {
+        float y[8], ss = 0.f;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          float v = bias[m];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) v = fmaf(wt[m][jj], raw[tt + jj].get(m), v);
+          v = core.act(v);
+          y[m] = v;
+          ss = fmaf(v, v, ss);
+        }
+        const float sum = group_sum<kGrp>(ss);
+        float sc = a.l2norm ? rsqrtf(sum + a.eps) : 1.0f;
+        if (!isk) sc *= a.q_scale;
+        const int tok = kTpl * tg + tt;
+        if (tb + tok >= T) sc = 0.f;
+        float* row = (isk ? yk : yq) + tok * DP::kRow + 8 * oc;
+        *reinterpret_cast<f4*>(row) = f4{y[0], y[1], y[2], y[3]} * sc;
+        *reinterpret_cast<f4*>(row + 4) = f4{y[4], y[5], y[6], y[7]} * sc;
+      }
+    }
+    // ---- decays (1 past the sequence) and b ----
+    {
+      const int n = T - tb < kBlk ? (T > tb ? T - tb : 0) : kBlk;
+      const int64_t rowe = static_cast<int64_t>(a.Hv) * DK;
+      const rsrc_t ra = make_rsrc(static_cast<const Act*>(a.alpha) + (t0 + static_cast<int64_t>(tb)) * rowe,
+                                  static_cast<uint32_t>(n * rowe * sizeof(Act)));
+      const int r = lane >> 2, q4 = lane & 3;  // token r, channel quarter q4
+#pragma unroll
+      for (int o = 0; o < DK / 32; ++o) {
+        const int c = 8 * (4 * o + q4);
+        Row8<Act> v;
+        v.load(ra, static_cast<int>(((r * a.Hv + h) * DK + c) * sizeof(Act)));
+        float* dstp = al + r * DP::kRow + c;
+        f4 lo4, hi4;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          lo4[m] = r < n ? v.get(m) : 1.f;
+          hi4[m] = r < n ? v.get(m + 4) : 1.f;
+        }
+        *reinterpret_cast<f4*>(dstp) = lo4;
+        *reinterpret_cast<f4*>(dstp + 4) = hi4;
+      }
+      if (lane < kBlk)
+        bt[lane] = lane < n ? to_f32(static_cast<const Act*>(a.beta)[(t0 + static_cast<int64_t>(tb) + lane) * a.Hv + h])
+                            : 0.f;
+    }
+    lds_barrier();
+    // ---- N and P by products of the decays ----
+    {
+      float w[kCw], accn[17], accp[17];
+#pragma unroll
+      for (int st = 0; st < 17; ++st) {
+        const bool first = st < 16 - cp;
+        const int i = first ? cp : 15 - cp;
+        const int r = first ? cp + st : st - 1;
+        const float* kr = yk + r * DP::kRow + cg * kCw;
+        const float* qr = yq + r * DP::kRow + cg * kCw;
+        const float* ar = al + r * DP::kRow + cg * kCw;
+        const bool start = r == i;
+        float sn = 0.f, sp = 0.f;
+#pragma unroll
+        for (int c4 = 0; c4 < kCw; c4 += 4) {
+          const f4 kv = *reinterpret_cast<const f4*>(kr + c4);
+          const f4 qv = *reinterpret_cast<const f4*>(qr + c4);
+          const f4 av = *reinterpret_cast<const f4*>(ar + c4);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            w[c4 + m] = start ? kv[m] : w[c4 + m] * av[m];
+            sn = fmaf(kv[m], w[c4 + m], sn);
+            sp = fmaf(qv[m], w[c4 + m], sp);
+          }
+        }
+        accn[st] = group_sum<8>(sn);
+        accp[st] = group_sum<8>(sp);
+      }
+      if (cg == 0) {
+#pragma unroll
+        for (int st = 0; st < 17; ++st) {
+          const bool first = st < 16 - cp;
+          const int i = first ? cp : 15 - cp;
+          const int r = first ? cp + st : st - 1;
+          if (r > i) nm[r * kBlk + i] = bt[r] * accn[st];
+          pm[r * kBlk + i] = accp[st];
+        }
+      }
+    }
+    lds_barrier();
+    // ---- X = (I + N)^{-1}: lane i < 16 solves for column i ----
+    if (lane < kBlk) {
+      float x[kBlk];
+#pragma unroll
+      for (int r = 0; r < kBlk; ++r) {
+        float v = r == lane ? 1.f : 0.f;
+#pragma unroll
+        for (int j = 0; j < r; ++j) v = fmaf(-nm[r * kBlk + j], x[j], v);
+        x[r] = v;
+        xm[r * kBlk + lane] = v;
+      }
+    }
+    lds_barrier();
+    // ---- write the record ----
+    {
+      const int r = lane >> 2, q4 = lane & 3;
+      const f4 xv = *reinterpret_cast<const f4*>(xm + r * kBlk + 4 * q4);
+      const f4 pv = *reinterpret_cast<const f4*>(pm + r * kBlk + 4 * q4);
+      s4 xh, xl, ph, pl;
+      split4(xv, xh, xl);
+      split4(pv, ph, pl);
+      typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+      const u4 w0 = __builtin_bit_cast(u4, cat(xh, xl));
+      const u4 w1 = __builtin_bit_cast(u4, cat(ph, pl));
+      unsigned char* rec = static_cast<unsigned char*>(a.ws) +
+                           (ws_block(s, t0, jb) * a.Hv + h) * kWsBlockBytes + lane * 32;
+      *reinterpret_cast<u4*>(rec) = w0;
+      *reinterpret_cast<u4*>(rec + 16) = w1;
+    }
+    lds_barrier();  // the next block reuses the LDS
+  }
+}
+
+// =====================================================================
+// Kernel 2: the chunk scan.
+// =====================================================================
+// LDS plan (bytes).  KE, QE, KF planes ([token][d_k] bf16 hi and lo, rows
+// per QkRow, staggered by 64 bytes); P and A ([token][token] bf16 hi and lo,
+// rows padded by 16 bytes); b per token; per-channel fp32 vectors: block
+// decays Lam_0..3, then e^{G_1..3}, e^{G_4} (the chunk's decay), f_0..2;
+// conv taps and bias of the key head's q and k channels.
+template <int DK>
+struct KdaPlan {
+  static constexpr int kRowQK = QkRow<DK>::kElems;
+  static constexpr int kRowT = kC + 8;
+  static constexpr int kQK = 2 * kC * kRowQK + 64;
+  static constexpr int kSq = 2 * kC * kRowT;
+  static constexpr int oEKh = 0, oEKl = oEKh + kQK, oEQh = oEKl + kQK, oEQl = oEQh + kQK;
+  static constexpr int oFKh = oEQl + kQK, oFKl = oFKh + kQK;
+  static constexpr int oPh = oFKl + kQK, oPl = oPh + kSq, oAh = oPl + kSq, oAl = oAh + kSq;
+  static constexpr int oBeta = oAl + kSq;
+  static constexpr int oLam = oBeta + kC * 4;       // fp32 [4][DK]
+  static constexpr int oVec = oLam + 4 * DK * 4;    // fp32 [7][DK]
+  static constexpr int kVecG = 0, kVecC = 3, kVecF = 4;
+  static constexpr int oW = oVec + 7 * DK * 4;
+  static constexpr int oB = oW + 2 * DK * 16;
+  static constexpr int kBytes = oB + 2 * DK * 4;
+};
+
+template <int DK, typename Act>
+struct KdaChunk : PrefillCore<DK, Act> {
+  GDN_PREFILL_CORE(DK, Act);
+  using P = KdaPlan<DK>;
+  static constexpr int kSl = DK / 32;
+  static constexpr int kDt = DK / 16;
+  static constexpr int kNco = DK / 4;
+  static constexpr int kGrp = DK / 8;
+  static constexpr bool kBf = sizeof(Act) == 2;
+
+  int s;   // sequence index (workspace addressing)
+
+  __device__ __forceinline__ static int qk(int r, int sl) { return QkRow<DK>::at(r, sl); }
+  __device__ __forceinline__ static float bfx(short v) {
+    return __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(v)) << 16);
+  }
+
+  // ================= producers =================
+  // Thread (co, tau): channel octet co of q|k (q first), tokens 8 tau..+7.
+  struct Prod {
+    Row8<Act> raw[11];        // rows 8 tau - 3 .. 8 tau + 7 of a chunk
+    Row8<Act> dec[8];         // decays of tokens 8 tau .. +7 at the 8 channels
+    s4 eh[8][2], el[8][2];    // KE (k) or QE (q) rows, not yet stored
+    s4 fh[4][2], fl[4][2];    // KF rows: tokens 0..3 of the octet (k thread), 4..7 (q thread)
+    float lam[8];             // decay over the whole 16-token block
+    uint32_t diag[8];         // this thread's 32 bytes of a diagonal-block record
+    float beta;               // wave 3: b of token = lane
+    int co, tau, ch, oc;
+    bool isk, on;
+  };
+
+  __device__ void prod_init(Prod& p) const {
+    p.on = tid < 8 * kNco;
+    p.co = tid % kNco;
+    p.tau = tid / kNco;
+    p.isk = p.co >= kGrp;
+    p.oc = p.isk ? p.co - kGrp : p.co;
+    p.ch = (p.isk ? a.Hk * DK : 0) + hk * DK + 8 * p.oc;
+  }
+
+  __device__ void load_taps() const {
+    float* wt = fp(P::oW);
+    float* bs = fp(P::oB);
+    for (int i = tid; i < 2 * DK; i += kThreads) {
+      const int ch = i < DK ? hk * DK + i : a.Hk * DK + hk * DK + (i - DK);
+      *reinterpret_cast<f4*>(wt + 4 * i) = f4{tap(ch, 0), tap(ch, 1), tap(ch, 2), tap(ch, 3)};
+      bs[i] = a.bias ? to_f32(static_cast<const Act*>(a.bias)[ch]) : 0.f;
+    }
+  }
+
+  __device__ __forceinline__ void prod_load(Prod& p, int c0) const {
+    const int tau = opaque(p.tau), ch = opaque(p.ch), oc = opaque(p.oc);
+    if (p.on) {
+      const rsrc_t rx = x_rows(c0);
+#pragma unroll
+      for (int r = 0; r < 11; ++r) p.raw[r].load(rx, x_off(c0, c0 + 8 * tau - 3 + r, ch));
+      const int n = T - c0 < kC ? T - c0 : kC;
+      const int64_t rowe = static_cast<int64_t>(a.Hv) * DK;
+      const rsrc_t ra = make_rsrc(static_cast<const Act*>(a.alpha) + (t0 + static_cast<int64_t>(c0)) * rowe,
+                                  static_cast<uint32_t>(n * rowe * sizeof(Act)));
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt)
+        p.dec[tt].load(ra, static_cast<int>((((8 * tau + tt) * a.Hv + h) * DK + 8 * oc) * sizeof(Act)));
+      if (c0 == 0) {
+        const rsrc_t rw = win_rows();
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+          Row8<Act> wr;
+          wr.load(rw, win_off(8 * tau - 3 + r, ch));
+          p.raw[r].merge(wr);
+        }
+      }
+    }
+  }
+
+  // The chunk's diagonal-block records (thread = block R, lane): loaded when
+  // its preparation starts, stored with its planes.
+  __device__ __forceinline__ void load_diag(Prod& p, int c0) const {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    const int R = tid >> 6, l = tid & 63;
+    const unsigned char* rec = static_cast<const unsigned char*>(a.ws) +
+                               (ws_block(s, t0, c0 / kBlk + R) * a.Hv + h) * kWsBlockBytes + l * 32;
+    const u4 w0 = *reinterpret_cast<const u4*>(rec);
+    const u4 w1 = *reinterpret_cast<const u4*>(rec + 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p.diag[i] = w0[i];
+      p.diag[4 + i] = w1[i];
+    }
+  }
+
+  // Decay of token 8 tau + tt at channel m of the thread's octet (1 past the
+  // sequence), re-read from the packed rows at every use: an opaque copy
+  // keeps the compiler from holding 64 unpacked values across the passes.
+  __device__ __forceinline__ float dec(const Prod& p, int tt, int m, bool in) const {
+    Row8<Act> r;
+#pragma unroll
+    for (int i = 0; i < Row8<Act>::kWords; ++i) r.w[i] = 0;
+    r.w[m * Row8<Act>::kWords / 8] = static_cast<uint32_t>(opaque(static_cast<int>(p.dec[tt].w[m * Row8<Act>::kWords / 8])));
+    return in ? r.get(m) : 1.f;
+  }
+
+  // conv + SiLU + L2 norm (+ q scale), the decay products and the planes of
+  // chunk c0.  The octet's total decay and its partner's (the other half of
+  // the 16-token block, kNco lanes away) start a forward pass (conv, the
+  // normalised rows, KE / QE with the running prefix product E) and a
+  // backward pass (KF with the running suffix product F).
+  __device__ void prod_prep(Prod& p, int c0) const {
+    const float* wl = fp(P::oW);
+    const float* bl = fp(P::oB);
+    load_diag(p, c0);
+    if (p.on) {
+      const int tbase = c0 + 8 * p.tau;
+      float tot[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) tot[m] = 1.f;
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) tot[m] = tot[m] * dec(p, tt, m, tbase + tt < T);
+      const bool odd = p.tau & 1;
+      float run[8], pt[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        pt[m] = __shfl_xor(tot[m], kNco);
+        run[m] = odd ? pt[m] : 1.f;
+        p.lam[m] = pt[m] * tot[m];
+      }
+      // k rows for the KF plane: a k thread keeps its own tokens 0..3, its q
+      // partner (kGrp lanes away, same channels and decays) takes 4..7
+      float kf[4][8];
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        const bool in = tbase + tt < T;
+        float y[8], ss = 0.f;
+        const int cw = 8 * opaque(p.co);   // taps re-read per token, not held
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const f4 wt = *reinterpret_cast<const f4*>(wl + 4 * (cw + m));
+          float v = bl[cw + m];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) v = fmaf(wt[jj], p.raw[tt + jj].get(m), v);
+          v = act(v);
+          y[m] = v;
+          ss = fmaf(v, v, ss);
+        }
+        const float sum = group_sum<kGrp>(ss);
+        float sc = a.l2norm ? rsqrtf(sum + a.eps) : 1.0f;
+        if (!p.isk) sc *= a.q_scale;
+        if (!in) sc = 0.f;
+        f4 ve[2];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const float yv = y[m] * sc;
+          if (tt < 4) {
+            kf[tt][m] = yv;
+          } else {
+            const float other = __shfl_xor(yv, kGrp);
+            kf[tt - 4][m] = p.isk ? kf[tt - 4][m] : other;
+          }
+          run[m] = run[m] * dec(p, tt, m, in);
+          ve[m >> 2][m & 3] = yv * run[m];
+        }
+        split4(ve[0], p.eh[tt][0], p.el[tt][0]);
+        split4(ve[1], p.eh[tt][1], p.el[tt][1]);
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m) run[m] = odd ? 1.f : pt[m];
+#pragma unroll
+      for (int tt = 7; tt >= 0; --tt) {
+        const int jx = tt & 3;
+        f4 vf[2];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) vf[m >> 2][m & 3] = kf[jx][m] * run[m];
+        s4 h0, l0, h1, l1;
+        split4(vf[0], h0, l0);
+        split4(vf[1], h1, l1);
+        if (tt >= 4 || p.isk) {
+          p.fh[jx][0] = h0;
+          p.fh[jx][1] = h1;
+          p.fl[jx][0] = l0;
+          p.fl[jx][1] = l1;
+        }
+        if (tt > 0) {
+          const bool in = tbase + tt < T;
+#pragma unroll
+          for (int m = 0; m < 8; ++m) run[m] = run[m] * dec(p, tt, m, in);
+        }
+      }
+    }
+    if (wave == 3)
+      p.beta = c0 + lane < T ? to_f32(static_cast<const Act*>(a.beta)[(static_cast<int64_t>(t0) + c0 + lane) * a.Hv + h])
+                             : 0.f;
+  }
+
+  __device__ void prod_store(const Prod& p) const {
+    if (p.on) {
+      short* eh = sp(p.isk ? P::oEKh : P::oEQh);
+      short* el = sp(p.isk ? P::oEKl : P::oEQl);
+      const int tau = opaque(p.tau);
+      const int sb = slot(8 * opaque(p.oc));
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        const int o0 = qk(8 * tau + tt, sb), o1 = qk(8 * tau + tt, sb + 8);
+        *reinterpret_cast<s4*>(eh + o0) = p.eh[tt][0];
+        *reinterpret_cast<s4*>(eh + o1) = p.eh[tt][1];
+        *reinterpret_cast<s4*>(el + o0) = p.el[tt][0];
+        *reinterpret_cast<s4*>(el + o1) = p.el[tt][1];
+      }
+      {
+        short* fh = sp(P::oFKh);
+        short* fl = sp(P::oFKl);
+        const int t4 = 8 * tau + (p.isk ? 0 : 4);
+#pragma unroll
+        for (int jx = 0; jx < 4; ++jx) {
+          const int o0 = qk(t4 + jx, sb), o1 = qk(t4 + jx, sb + 8);
+          *reinterpret_cast<s4*>(fh + o0) = p.fh[jx][0];
+          *reinterpret_cast<s4*>(fh + o1) = p.fh[jx][1];
+          *reinterpret_cast<s4*>(fl + o0) = p.fl[jx][0];
+          *reinterpret_cast<s4*>(fl + o1) = p.fl[jx][1];
+        }
+      }
+      if (p.isk) {
+        if (tau & 1) {
+          float* lam = fp(P::oLam) + (tau >> 1) * DK + 8 * opaque(p.oc);
+          *reinterpret_cast<f4*>(lam) = f4{p.lam[0], p.lam[1], p.lam[2], p.lam[3]};
+          *reinterpret_cast<f4*>(lam + 4) = f4{p.lam[4], p.lam[5], p.lam[6], p.lam[7]};
+        }
+      }
+    }
+    {
+      const int l = lane_now();
+      const int R = wave, r = 16 * R + (l >> 2), q4 = l & 3;
+      const int o = r * P::kRowT + slot(16 * R + 4 * q4);
+      typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+      *reinterpret_cast<u2*>(sp(P::oAh) + o) = u2{p.diag[0], p.diag[1]};
+      *reinterpret_cast<u2*>(sp(P::oAl) + o) = u2{p.diag[2], p.diag[3]};
+      *reinterpret_cast<u2*>(sp(P::oPh) + o) = u2{p.diag[4], p.diag[5]};
+      *reinterpret_cast<u2*>(sp(P::oPl) + o) = u2{p.diag[6], p.diag[7]};
+    }
+    if (wave == 3) fp(P::oBeta)[lane] = p.beta;
+  }
+
+  // ================= all waves: the off-diagonal blocks of A and P =====
+  __device__ __forceinline__ void op_bases(int (&ob)[kSl]) const {
+    const int l = lane_now(), r = l & 15, g = l >> 4;
+#pragma unroll
+    for (int sl = 0; sl < kSl; ++sl) ob[sl] = qk(r, 32 * sl + 8 * g);
+  }
+
+  // Block pair (IB, JB), IB > JB + 0, computed transposed: A operand KF rows
+  // JB (times D = prod_{JB < J < IB} Lam_J on its channels), B operands KE
+  // and QE rows IB; lane holds row r = 16 IB + lr at columns 16 JB + 4 lg + v.
+  template <int IB, int JB>
+  __device__ __forceinline__ void pair(const int (&ob)[kSl]) const {
+    const short* fh = sp(P::oFKh);
+    const short* fl = sp(P::oFKl);
+    const short* kh = sp(P::oEKh);
+    const short* kl = sp(P::oEKl);
+    const short* qh = sp(P::oEQh);
+    const short* ql = sp(P::oEQl);
+    const int l = lane_now(), lr = l & 15, lg = l >> 4;
+    f4 g = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sl = 0; sl < kSl; ++sl) {
+      const int oa = 16 * JB * P::kRowQK + ob[sl], obr = 16 * IB * P::kRowQK + ob[sl];
+      s8 ah = *reinterpret_cast<const s8*>(fh + oa);
+      s8 al = *reinterpret_cast<const s8*>(fl + oa);
+      if constexpr (IB - JB > 1) {
+        // channels 32 sl + 4 lg + j (slots 0..3) and 32 sl + 16 + 4 lg + j (4..7)
+        const float* lam = fp(P::oLam);
+        f4 d0 = *reinterpret_cast<const f4*>(lam + (JB + 1) * DK + 32 * sl + 4 * lg);
+        f4 d1 = *reinterpret_cast<const f4*>(lam + (JB + 1) * DK + 32 * sl + 16 + 4 * lg);
+        if constexpr (IB - JB > 2) {
+          d0 = d0 * *reinterpret_cast<const f4*>(lam + (JB + 2) * DK + 32 * sl + 4 * lg);
+          d1 = d1 * *reinterpret_cast<const f4*>(lam + (JB + 2) * DK + 32 * sl + 16 + 4 * lg);
+        }
+        f4 x0, x1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x0[j] = (bfx(ah[j]) + bfx(al[j])) * d0[j];
+          x1[j] = (bfx(ah[4 + j]) + bfx(al[4 + j])) * d1[j];
+        }
+        s4 h0, l0, h1, l1;
+        split4(x0, h0, l0);
+        split4(x1, h1, l1);
+        ah = cat(h0, h1);
+        al = cat(l0, l1);
+      }
+      const s8 bkh = *reinterpret_cast<const s8*>(kh + obr);
+      const s8 bkl = *reinterpret_cast<const s8*>(kl + obr);
+      const s8 bqh = *reinterpret_cast<const s8*>(qh + obr);
+      const s8 bql = *reinterpret_cast<const s8*>(ql + obr);
+      g = mma32(al, bkh, g);
+      pq = mma32(al, bqh, pq);
+      g = mma32(ah, bkl, g);
+      pq = mma32(ah, bql, pq);
+      g = mma32(ah, bkh, g);
+      pq = mma32(ah, bqh, pq);
+    }
+    const int r = 16 * IB + lr;
+    const int o = r * P::kRowT + slot(16 * JB + 4 * lg);
+    s4 h, lo;
+    split4(pq, h, lo);
+    *reinterpret_cast<s4*>(sp(P::oPh) + o) = h;
+    *reinterpret_cast<s4*>(sp(P::oPl) + o) = lo;
+    split4(fp(P::oBeta)[r] * g, h, lo);
+    *reinterpret_cast<s4*>(sp(P::oAh) + o) = h;
+    *reinterpret_cast<s4*>(sp(P::oAl) + o) = lo;
+  }
+
+  // Per-channel chunk vectors from the block decays: e^{G_R} = prod_{J<R}
+  // Lam_J (R = 1..3), e^{G_4}, and f_I = prod_{J>I} Lam_J (I = 0..2).
+  __device__ void vectors() const {
+    const int c = (wave - 6) * 64 + lane_now();
+    if (c >= DK) return;
+    const float* lam = fp(P::oLam);
+    float* vec = fp(P::oVec);
+    const float l0 = lam[c], l1 = lam[DK + c], l2 = lam[2 * DK + c], l3 = lam[3 * DK + c];
+    const float g1 = l0, g2 = g1 * l1, g3 = g2 * l2;
+    vec[(P::kVecG + 0) * DK + c] = g1;
+    vec[(P::kVecG + 1) * DK + c] = g2;
+    vec[(P::kVecG + 2) * DK + c] = g3;
+    vec[P::kVecC * DK + c] = g3 * l3;
+    const float f2 = l3, f1 = l2 * f2, f0 = l1 * f1;
+    vec[(P::kVecF + 0) * DK + c] = f0;
+    vec[(P::kVecF + 1) * DK + c] = f1;
+    vec[(P::kVecF + 2) * DK + c] = f2;
+  }
+
+  __device__ void gram_phase() const {
+    int ob[kSl];
+    op_bases(ob);
+    switch (wave) {
+      case 0: pair<1, 0>(ob); break;
+      case 1: pair<2, 1>(ob); break;
+      case 2: pair<3, 2>(ob); break;
+      case 3: pair<2, 0>(ob); break;
+      case 4: pair<3, 1>(ob); break;
+      case 5: pair<3, 0>(ob); break;
+      default: vectors(); break;
+    }
+  }
+
+  // ================= consumers =================
+  // The value conv of the wave's 16 columns: lane (lr, lg) needs tokens
+  // 16 b + 4 lg + v (v < 4), i.e. raw rows 16 b + 4 lg - 3 .. + 3.
+  struct Cons {
+    uint32_t vx[4][7];
+    float vw[4], vb;
+    int vch;
+    bool von;
+  };
+
+  __device__ void cons_init(Cons& c) const {
+    c.vch = 2 * a.Hk * DK + h * a.dv + e0 + lr;
+    c.von = e0 + lr < a.dv;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) c.vw[jj] = c.von ? tap(c.vch, jj) : 0.f;
+    c.vb = (c.von && a.bias) ? to_f32(static_cast<const Act*>(a.bias)[c.vch]) : 0.f;
+  }
+
+  __device__ __forceinline__ void cons_load(Cons& c, int c0) const {
+    const rsrc_t rx = x_rows(c0);
+    const int l = lane_now(), lgg = l >> 4, vch = opaque(c.vch);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < 7; ++i) {
+        const int off = x_off(c0, c0 + 16 * b + 4 * lgg - 3 + i, vch);
+        if constexpr (kBf)
+          c.vx[b][i] = __builtin_amdgcn_raw_buffer_load_b16(rx, off, 0, 0);
+        else
+          c.vx[b][i] = __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0);
+      }
+    if (c0 == 0) {
+      const rsrc_t rw = win_rows();
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int off = win_off(4 * lgg - 3 + i, vch);
+        if constexpr (kBf)
+          c.vx[0][i] |= __builtin_amdgcn_raw_buffer_load_b16(rw, off, 0, 0);
+        else
+          c.vx[0][i] |= __builtin_amdgcn_raw_buffer_load_b32(rw, off, 0, 0);
+      }
+    }
+  }
+
+  __device__ __forceinline__ float vraw(uint32_t u) const {
+    return kBf ? __uint_as_float(u << 16) : __uint_as_float(u);
+  }
+
+  // The wave's 16 value columns for chunk c0.  S[d] holds rows
+  // 16d + 4 lg + v (key index) of S^T at column e0 + lr (value index).
+  __device__ void columns(int c0, f4 (&S)[kDt], Cons& cv, bool next) const {
+    const int l = lane_now(), lr = l & 15, lg = l >> 4;
+    // value conv of this chunk, then the next chunk's raw rows
+    f4 V[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float y = cv.vb;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) y = fmaf(cv.vw[jj], vraw(cv.vx[b][v + jj]), y);
+        V[b][v] = c0 + 16 * b + 4 * lg + v < T ? act(y) : 0.f;
+      }
+    if (next) cons_load(cv, c0 + kC);
+    const float* vec = fp(P::oVec);
+    const short* kh = sp(P::oEKh);
+    const short* kl = sp(P::oEKl);
+    const short* qh = sp(P::oEQh);
+    const short* ql = sp(P::oEQl);
+    // K E_b diag(e^{G_b}) S0^T and the same for Q, rows 16 tb + 4 lg + v
+    f4 ks[4], qs[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      ks[tb] = f4{0.f, 0.f, 0.f, 0.f};
+      qs[tb] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+    int ob[kSl];
+    op_bases(ob);
+#pragma unroll
+    for (int sl = 0; sl < kSl; ++sl) {
+      s8 xh[4], xl[4], yh[4], yl[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const int ra = 16 * tb * P::kRowQK + ob[sl];
+        xh[tb] = *reinterpret_cast<const s8*>(kh + ra);
+        xl[tb] = *reinterpret_cast<const s8*>(kl + ra);
+        yh[tb] = *reinterpret_cast<const s8*>(qh + ra);
+        yl[tb] = *reinterpret_cast<const s8*>(ql + ra);
+      }
+      s8 sbh[4], sbl[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        f4 s0 = S[2 * sl], s1 = S[2 * sl + 1];
+        if (tb > 0) {
+          const float* gv = vec + (P::kVecG + tb - 1) * DK + 32 * sl + 4 * lg;
+          s0 = s0 * *reinterpret_cast<const f4*>(gv);
+          s1 = s1 * *reinterpret_cast<const f4*>(gv + 16);
+        }
+        s4 h0, l0, h1, l1;
+        split4(s0, h0, l0);
+        split4(s1, h1, l1);
+        sbh[tb] = cat(h0, h1);
+        sbl[tb] = cat(l0, l1);
+      }
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        ks[tb] = mma32(xl[tb], sbh[tb], ks[tb]);
+        qs[tb] = mma32(yl[tb], sbh[tb], qs[tb]);
+      }
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        ks[tb] = mma32(xh[tb], sbl[tb], ks[tb]);
+        qs[tb] = mma32(yh[tb], sbl[tb], qs[tb]);
+      }
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        ks[tb] = mma32(xh[tb], sbh[tb], ks[tb]);
+        qs[tb] = mma32(yh[tb], sbh[tb], qs[tb]);
+      }
+    }
+    // U_b = X_bb (b_b R_b - sum_{j<b} A_bj U_j),  R = V - (K o e^g) S0^T
+    const float* bt = fp(P::oBeta);
+    f4 U[4];
+    s4 uh[4], ul[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int row = (16 * b + lr) * P::kRowT;
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (b > 0) {
+        s4 ah[3], al[3];
+#pragma unroll
+        for (int jb = 0; jb < b; ++jb) {
+          const int o = row + slot(16 * jb + 4 * lg);
+          ah[jb] = *reinterpret_cast<const s4*>(sp(P::oAh) + o);
+          al[jb] = *reinterpret_cast<const s4*>(sp(P::oAl) + o);
+        }
+#pragma unroll
+        for (int jb = 0; jb < b; ++jb) acc = mma16(al[jb], uh[jb], acc);
+#pragma unroll
+        for (int jb = 0; jb < b; ++jb) acc = mma16(ah[jb], ul[jb], acc);
+#pragma unroll
+        for (int jb = 0; jb < b; ++jb) acc = mma16(ah[jb], uh[jb], acc);
+      }
+      const int o = row + slot(16 * b + 4 * lg);
+      const s4 xh = *reinterpret_cast<const s4*>(sp(P::oAh) + o);
+      const s4 xl = *reinterpret_cast<const s4*>(sp(P::oAl) + o);
+      const f4 bb = *reinterpret_cast<const f4*>(bt + 16 * b + 4 * lg);
+      s4 zh, zl;
+      split4(bb * (V[b] - ks[b]) - acc, zh, zl);
+      U[b] = mma16x3(xh, xl, zh, zl, f4{0.f, 0.f, 0.f, 0.f});
+      split4(U[b], uh[b], ul[b]);
+    }
+    // O = (Q o e^g) S0^T + P U
+    {
+      constexpr int kB[6] = {0, 1, 2, 2, 3, 3}, kU[6] = {0, 0, 0, 1, 0, 1};
+      s8 ph[6], pl[6];
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        const int off = (16 * kB[i] + lr) * P::kRowT + 32 * kU[i] + 8 * lg;
+        ph[i] = *reinterpret_cast<const s8*>(sp(P::oPh) + off);
+        pl[i] = *reinterpret_cast<const s8*>(sp(P::oPl) + off);
+      }
+      f4 o[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) o[b] = qs[b];
+      const s8 u0h = cat(uh[0], uh[1]), u0l = cat(ul[0], ul[1]);
+      const s8 u1h = cat(uh[2], uh[3]), u1l = cat(ul[2], ul[3]);
+#pragma unroll
+      for (int i = 0; i < 6; ++i) o[kB[i]] = mma32(pl[i], kU[i] ? u1h : u0h, o[kB[i]]);
+#pragma unroll
+      for (int i = 0; i < 6; ++i) o[kB[i]] = mma32(ph[i], kU[i] ? u1l : u0l, o[kB[i]]);
+#pragma unroll
+      for (int i = 0; i < 6; ++i) o[kB[i]] = mma32(ph[i], kU[i] ? u1h : u0h, o[kB[i]]);
+      const int rs = a.Hv * a.dv;
+      const int n = T - c0 < kC ? T - c0 : kC;
+      const rsrc_t ro =
+          make_rsrc(a.out + ((static_cast<int64_t>(t0) + c0) * a.Hv + h) * a.dv + e0,
+                    static_cast<uint32_t>(n) * static_cast<uint32_t>(rs) * 4u);
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[b][v]), ro,
+                                                ((16 * b + 4 * lg + v) * rs + lr) * 4, 0, 0);
+    }
+    // S^T <- diag(e^{G_4}) S^T + sum_I diag(f_I) KF_I^T U_I: per key tile d,
+    // one 16-token product per block I from transposing reads of the KF rows.
+    int tb0[kSl];
+    {
+      const int r = l & 15, g = l >> 4;
+#pragma unroll
+      for (int D = 0; D < kSl; ++D) tb0[D] = qk(4 * g + (r >> 2), 32 * D + 8 * (r & 3));
+    }
+    const short* fh = sp(P::oFKh);
+    const short* fl = sp(P::oFKl);
+#pragma unroll
+    for (int d = 0; d < kDt; ++d) {
+      s4 th[4], tl[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        const int r0 = tb0[d >> 1] + (16 * I) * P::kRowQK + 4 * (d & 1);
+        th[I] = ld_tr(fh + r0);
+        tl[I] = ld_tr(fl + r0);
+      }
+      f4 acc[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) acc[I] = mma16(tl[I], uh[I], f4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int I = 0; I < 4; ++I) acc[I] = mma16(th[I], ul[I], acc[I]);
+#pragma unroll
+      for (int I = 0; I < 4; ++I) acc[I] = mma16(th[I], uh[I], acc[I]);
+      const int key = 16 * d + 4 * lg;
+      f4 s = *reinterpret_cast<const f4*>(vec + P::kVecC * DK + key) * S[d] + acc[3];
+#pragma unroll
+      for (int I = 0; I < 3; ++I)
+        s = s + *reinterpret_cast<const f4*>(vec + (P::kVecF + I) * DK + key) * acc[I];
+      S[d] = s;
+    }
+  }
+};
+
+template <int DK, typename Act>
+__global__ void __launch_bounds__(kThreads, 1) kda_chunk_kernel(PrefillArgs a) {
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  using K = KdaChunk<DK, Act>;
+  using P = KdaPlan<DK>;
+  K k{{a, lds_raw}};
+  k.tid = threadIdx.x;
+  k.wave = __builtin_amdgcn_readfirstlane(k.tid >> 6);
+  k.lane = k.tid & 63;
+  k.lr = k.lane & 15;
+  k.lg = k.lane >> 4;
+
+  // Units (sequence, value head, column block), value heads of one key head
+  // consecutive, dealt so that consecutive units share an XCD.
+  const int nb = gridDim.x;
+  const int bid = blockIdx.x;
+  const int u = (nb % 8 == 0) ? (bid % 8) * (nb / 8) + bid / 8 : bid;
+  const int j = u % a.nblk;
+  k.h = (u / a.nblk) % a.Hv;
+  const int s = u / a.nblk / a.Hv;
+  k.s = s;
+  k.hk = k.h / a.G;
+
+  const int t0 = a.cu[s], t1 = a.cu[s + 1];
+  const int32_t dst = a.dst[s];
+  k.init = a.init ? a.init[s] : dst;
+  if (t0 < 0 || t1 < t0 || t1 > a.total || dst < 0 || dst >= a.num_slots ||
+      k.init >= a.num_slots)
+    return;
+  k.t0 = t0;
+  k.T = t1 - t0;
+  const int nch = (k.T + kC - 1) / kC;
+
+  // P and A planes: the blocks above the diagonal stay zero.
+  for (int i = k.tid; i < 4 * P::kSq / 16; i += kThreads)
+    reinterpret_cast<uint4*>(lds_raw + P::oPh)[i] = uint4{0u, 0u, 0u, 0u};
+  k.e0 = j * kCols;
+  k.load_taps();
+
+  if (k.tid < kProd) {
+    typename K::Prod p;
+    k.prod_init(p);
+    if (nch > 0) k.prod_load(p, 0);
+    lds_barrier();            // planes zeroed, taps loaded
+    if (nch > 0) {
+      k.prod_prep(p, 0);
+      if (nch > 1) k.prod_load(p, kC);
+      k.prod_store(p);
+      lds_barrier();
+      k.gram_phase();
+      lds_barrier();
+    }
+    for (int c = 0; c < nch; ++c) {
+      const bool next = c + 1 < nch;
+      if (next) {
+        k.prod_prep(p, (c + 1) * kC);
+        if (c + 2 < nch) k.prod_load(p, (c + 2) * kC);
+      }
+      lds_barrier();          // consumers are done with chunk c
+      if (next) {
+        k.prod_store(p);
+        lds_barrier();
+        k.gram_phase();
+        lds_barrier();
+      }
+    }
+  } else {
+    k.e0 = j * kCols + (k.wave - 4) * 16;
+    const bool cols = k.e0 < a.dv;
+    typename K::Cons cv;
+    k.cons_init(cv);
+    if (cols && nch > 0) k.cons_load(cv, 0);
+    f4 S[K::kDt];
+    const int64_t head = static_cast<int64_t>(k.h) * a.dv * DK;
+    const int64_t slot_elems = static_cast<int64_t>(a.Hv) * a.dv * DK;
+#pragma unroll
+    for (int d = 0; d < K::kDt; ++d) {
+      S[d] = f4{0.f, 0.f, 0.f, 0.f};
+      if (cols && k.init >= 0)
+        S[d] = *reinterpret_cast<const f4*>(a.ssm + k.init * slot_elems + head +
+                                           static_cast<int64_t>(k.e0 + k.lr) * DK + 16 * d +
+                                           4 * k.lg);
+    }
+    lds_barrier();            // planes zeroed, taps loaded
+    if (nch > 0) {
+      lds_barrier();          // producers stored chunk 0
+      k.gram_phase();
+      lds_barrier();
+    }
+    for (int c = 0; c < nch; ++c) {
+      const bool next = c + 1 < nch;
+      if (cols) k.columns(c * kC, S, cv, next);
+      lds_barrier();          // chunk c consumed
+      if (next) {
+        lds_barrier();        // producers stored chunk c + 1
+        k.gram_phase();
+        lds_barrier();
+      }
+    }
+    if (cols) {
+      float* out = a.ssm + dst * slot_elems + head + static_cast<int64_t>(k.e0 + k.lr) * DK;
+#pragma unroll
+      for (int d = 0; d < K::kDt; ++d) *reinterpret_cast<f4*>(out + 16 * d + 4 * k.lg) = S[d];
+    }
+  }
+}
+
+template <int DK, typename Act>
+hipError_t launch_kda(const PrefillArgs& a, int max_seqlen, hipStream_t st) {
+  // diagonal blocks: grid x strides over the token blocks of a sequence
+  const int64_t want = 4 * ((static_cast<int64_t>(max_seqlen) + kC - 1) / kC);
+  const int gy = static_cast<int>(want < 1 ? 1 : (want > 65535 ? 65535 : want));
+  hipLaunchKernelGGL((kda_diag_kernel<DK, Act>), dim3(a.N * a.Hv, gy), dim3(64), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int bytes = KdaPlan<DK>::kBytes;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_chunk_kernel<DK, Act>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((kda_chunk_kernel<DK, Act>), dim3(a.N * a.Hv * a.nblk), dim3(kThreads),
+                     bytes, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.W < 2) return e;
+  hipLaunchKernelGGL((prefill_conv_tail<Act>), dim3((a.C + 255) / 256, a.N), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+static_assert(KdaPlan<128>::kBytes <= 160 * 1024, "LDS plan exceeds 160 KiB");
+
+}  // namespace
+
+size_t kda_workspace_bytes(int Hv, int64_t N, int64_t total) {
+  const int64_t blocks = total / kBlk + 4 * (N < total ? N : total);
+  return static_cast<size_t>(blocks) * static_cast<size_t>(Hv) * kWsBlockBytes;
+}
+
+hipError_t launch_prefill_kda(const PrefillArgs& a, int dk, int act_bf16, int max_seqlen,
+                              hipStream_t s) {
+  if (a.N == 0) return hipSuccess;
+  switch (dk) {
+    case 32: return act_bf16 ? launch_kda<32, bf16>(a, max_seqlen, s) : launch_kda<32, float>(a, max_seqlen, s);
+    case 64: return act_bf16 ? launch_kda<64, bf16>(a, max_seqlen, s) : launch_kda<64, float>(a, max_seqlen, s);
+    case 128: return act_bf16 ? launch_kda<128, bf16>(a, max_seqlen, s) : launch_kda<128, float>(a, max_seqlen, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

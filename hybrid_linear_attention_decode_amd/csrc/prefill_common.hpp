@@ -1,0 +1,242 @@
+// prefill_common.hpp -- device pieces shared by the chunked prefill kernels
+// (scalar decay: gdn_prefill.hip; per-channel decay: kda_prefill.hip):
+// bf16 (hi, lo) operand splitting, the MFMA wrappers, the permuted
+// contraction order of K / Q planes, raw buffer descriptors, 8-channel raw
+// input rows, the per-unit addressing, and the destination conv-window copy.
+#pragma once
+
+#include "gdn_device.hpp"
+#include "gdn_internal.hpp"
+
+namespace gdn {
+namespace {
+
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef short s8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+
+constexpr int kC = 64;         // chunk length
+constexpr int kThreads = 512;  // 4 producer + 4 consumer waves
+constexpr int kProd = 256;     // producer threads
+constexpr int kCols = 64;      // value columns per workgroup (16 per consumer wave)
+
+// x ~= hi + lo with hi = bf16(x), lo = bf16(x - hi) (round to nearest even).
+__device__ __forceinline__ void split(float x, short& hi, short& lo) {
+  const __bf16 h = static_cast<__bf16>(x);
+  const __bf16 l = static_cast<__bf16>(x - static_cast<float>(h));
+  hi = __builtin_bit_cast(short, h);
+  lo = __builtin_bit_cast(short, l);
+}
+__device__ __forceinline__ void split4(f4 x, s4& hi, s4& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    short h, l;
+    split(x[i], h, l);
+    hi[i] = h;
+    lo[i] = l;
+  }
+}
+
+__device__ __forceinline__ f4 mma32(s8 a, s8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a),
+                                                 __builtin_bit_cast(b8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mma16(s4 a, s4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+// c + a*b with both operands given as (hi, lo) pairs.
+__device__ __forceinline__ f4 mma32x3(s8 ah, s8 al, s8 bh, s8 bl, f4 c) {
+  c = mma32(al, bh, c);
+  c = mma32(ah, bl, c);
+  return mma32(ah, bh, c);
+}
+__device__ __forceinline__ f4 mma16x3(s4 ah, s4 al, s4 bh, s4 bl, f4 c) {
+  c = mma16(al, bh, c);
+  c = mma16(ah, bl, c);
+  return mma16(ah, bh, c);
+}
+__device__ __forceinline__ s8 cat(s4 x, s4 y) {
+  return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Storage slot of contraction index i: inside each block of 32, index
+// 16h + 4g + j (h < 2, g < 4, j < 4) sits at 8g + 4h + j.  Lane group g of a
+// 16x16x32 operand then reads 8 consecutive slots holding rows 4g..4g+3 of
+// the two 16-row tiles of the block.
+__device__ __forceinline__ int slot(int i) {
+  return (i & ~31) | (((i >> 2) & 3) << 3) | (((i >> 4) & 1) << 2) | (i & 3);
+}
+
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane j receives element
+// (j mod 4) of the 64-bit words read by lanes 4e + j/4, e = 0..3.  Lanes
+// 4e + q reading row r0 + e, columns c0 + 4q..4q+3 thus hand lane j the
+// column c0 + j of rows r0..r0+3.
+__device__ __forceinline__ s4 ld_tr(const short* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s4*)(const_cast<short*>(p)));
+}
+
+// Raw buffer accesses (gfx9 descriptor, no stride): an access whose 32-bit
+// byte offset lies at or past num_records reads zero or is dropped, which
+// masks rows outside a sequence without branches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// SiLU with the hardware exp2 / reciprocal.
+__device__ __forceinline__ float silu(float y) {
+  return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y));
+}
+
+// Raw 8-channel rows: 16 bytes of bf16 or 32 bytes of fp32.
+template <typename Act>
+struct Row8 {
+  static constexpr int kWords = sizeof(Act) == 2 ? 4 : 8;
+  uint32_t w[kWords];
+  __device__ __forceinline__ void load(rsrc_t r, int off) {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    const u4 u = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    w[0] = u[0], w[1] = u[1], w[2] = u[2], w[3] = u[3];
+    if constexpr (kWords == 8) {
+      const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
+      w[4] = v[0], w[5] = v[1], w[6] = v[2], w[7] = v[3];
+    }
+  }
+  __device__ __forceinline__ void merge(const Row8& o) {
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) w[i] |= o.w[i];
+  }
+  __device__ __forceinline__ float get(int m) const {
+    if constexpr (kWords == 4)
+      return __uint_as_float((m & 1) ? (w[m >> 1] & 0xffff0000u) : (w[m >> 1] << 16));
+    else
+      return __uint_as_float(w[m]);
+  }
+};
+
+// Element offset of storage slot sl of row r in a [token][d_k] bf16 plane.
+// Rows of d_k = 128 (256 bytes, all 64 banks) are swizzled: 16-byte chunk c
+// of row r sits at chunk c ^ (((r & 3) << 2) | ((r >> 2) & 3)), so both the
+// 16-rows-at-one-chunk reads of MFMA operands and the 4-rows-by-4-chunks
+// transposing reads touch 16 distinct chunks.  Narrower rows are padded by
+// 16 bytes instead.
+template <int DK>
+struct QkRow {
+  static constexpr bool kSwz = DK == 128;
+  static constexpr int kElems = kSwz ? DK : DK + 8;   // bf16 per row
+  __device__ __forceinline__ static int at(int r, int sl) {
+    if constexpr (kSwz)
+      return r * DK + (((sl >> 3) ^ (((r & 3) << 2) | ((r >> 2) & 3))) << 3) + (sl & 7);
+    else
+      return r * kElems + sl;
+  }
+};
+
+// What every prefill workgroup knows about its unit (sequence, value head,
+// 64 value columns) and the raw-input addressing both kernels share.
+template <int DK, typename Act>
+struct PrefillCore {
+  const PrefillArgs& a;
+  unsigned char* lds;
+  int tid, wave, lane, lr, lg;
+  int h, hk, e0;
+  int t0, T;
+  int32_t init;
+
+  __device__ short* sp(int off) const { return reinterpret_cast<short*>(lds + off); }
+  __device__ float* fp(int off) const { return reinterpret_cast<float*>(lds + off); }
+  // The lane id, opaque to the compiler: offsets derived from it inside a
+  // phase are recomputed there (a few VALU ops) instead of being hoisted
+  // out of the chunk loop and kept live (or spilled) across all phases.
+  __device__ __forceinline__ static int opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+  }
+  __device__ __forceinline__ int lane_now() const { return opaque(lane); }
+
+  // Raw input rows for chunk c0: a descriptor over rows b0.. of the
+  // sequence (b0 = c0 - 8, or 0), ending at the sequence's last row (empty
+  // when b0 lies past it), so rows past the end (and before row 0) read zero.  The initial conv window
+  // (W-1 rows before row 0) has its own descriptor, empty when the sequence
+  // starts from zeros.
+  __device__ __forceinline__ int chunk_base(int c0) const { return c0 >= 8 ? c0 - 8 : 0; }
+  __device__ __forceinline__ rsrc_t x_rows(int c0) const {
+    const int b0 = chunk_base(c0);
+    const int64_t rowb = static_cast<int64_t>(a.C) * sizeof(Act);
+    const int64_t n = T - b0 < 80 ? (T > b0 ? T - b0 : 0) : 80;
+    return make_rsrc(static_cast<const Act*>(a.x) + (static_cast<int64_t>(t0) + b0) * a.C,
+                     static_cast<uint32_t>(n * rowb));
+  }
+  __device__ __forceinline__ rsrc_t win_rows() const {
+    const int W1 = a.W - 1;
+    const bool on = init >= 0 && W1 > 0;
+    return make_rsrc(on ? static_cast<const Act*>(a.conv) + static_cast<int64_t>(init) * W1 * a.C
+                        : a.x,
+                     on ? static_cast<uint32_t>(W1 * a.C * sizeof(Act)) : 0u);
+  }
+  // Byte offsets of row rho at channel ch in the two descriptors.
+  __device__ __forceinline__ int x_off(int c0, int rho, int ch) const {
+    return (rho - chunk_base(c0)) * a.C * static_cast<int>(sizeof(Act)) +
+           ch * static_cast<int>(sizeof(Act));
+  }
+  __device__ __forceinline__ int win_off(int rho, int ch) const {
+    return (a.W - 1 + rho) * a.C * static_cast<int>(sizeof(Act)) +
+           ch * static_cast<int>(sizeof(Act));
+  }
+  // Conv tap jj (0..3, the last on the current token) of channel ch; taps of
+  // a narrower conv are left-padded with zeros.
+  __device__ __forceinline__ float tap(int ch, int jj) const {
+    const int lead = 4 - a.W;
+    return jj >= lead ? to_f32(static_cast<const Act*>(a.w)[static_cast<int64_t>(ch) * a.W + jj - lead])
+                      : 0.f;
+  }
+  __device__ __forceinline__ float act(float y) const { return a.silu ? silu(y) : y; }
+};
+
+// The using-declarations a kernel struct deriving from PrefillCore needs.
+#define GDN_PREFILL_CORE(DK, Act)                                                         \
+  using Core = PrefillCore<DK, Act>;                                                      \
+  using Core::a; using Core::lds; using Core::tid; using Core::wave; using Core::lane;    \
+  using Core::lr; using Core::lg; using Core::h; using Core::hk; using Core::e0;          \
+  using Core::t0; using Core::T; using Core::init; using Core::sp; using Core::fp;        \
+  using Core::opaque; using Core::lane_now; using Core::chunk_base; using Core::x_rows;  \
+  using Core::win_rows; using Core::x_off; using Core::win_off; using Core::tap;          \
+  using Core::act
+
+// The destination conv window: the last W-1 inputs of the sequence (taken
+// from the initial window when the sequence is shorter).  Runs after the
+// main kernel, so an in-place sequence (init == dst) has read its window.
+// Each thread reads its channel's rows before writing any.
+template <typename Act>
+__global__ void __launch_bounds__(256) prefill_conv_tail(PrefillArgs a) {
+  const int s = blockIdx.y;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= a.C) return;
+  const int t0 = a.cu[s], t1 = a.cu[s + 1];
+  const int32_t dst = a.dst[s];
+  const int32_t init = a.init ? a.init[s] : dst;
+  if (t0 < 0 || t1 < t0 || t1 > a.total || dst < 0 || dst >= a.num_slots || init >= a.num_slots)
+    return;
+  const int T = t1 - t0, W1 = a.W - 1;
+  const Act* x = static_cast<const Act*>(a.x);
+  Act* conv = static_cast<Act*>(a.conv);
+  Act v[3];
+#pragma unroll
+  for (int jj = 0; jj < 3; ++jj) {
+    v[jj] = from_exact<Act>(0.f);
+    if (jj < W1) {
+      const int rho = T - W1 + jj;
+      if (rho >= 0)
+        v[jj] = x[(static_cast<int64_t>(t0) + rho) * a.C + c];
+      else if (init >= 0)
+        v[jj] = conv[(static_cast<int64_t>(init) * W1 + W1 + rho) * a.C + c];
+    }
+  }
+#pragma unroll
+  for (int jj = 0; jj < 3; ++jj)
+    if (jj < W1) conv[(static_cast<int64_t>(dst) * W1 + jj) * a.C + c] = v[jj];
+}
+
+}  // namespace
+}  // namespace gdn

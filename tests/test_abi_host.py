@@ -114,12 +114,12 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 
 
 def prefill(L, N=2, dst=FAKE, init=None, cu=FAKE, max_len=64, total=128, chunk=64, inp=None,
-            out=FAKE):
+            out=FAKE, ws=None, ws_bytes=0):
     pool = GdnPool(FAKE, FAKE, 8)
     inp = inp or GdnInputs(FAKE, FAKE, FAKE, FAKE, None)
     return gdn.lib().gdn_prefill_chunked(ct.byref(L), ct.byref(pool), dst, init, N, cu,
-                                         max_len, total, chunk, ct.byref(inp), out, None, 0,
-                                         None)
+                                         max_len, total, chunk, ct.byref(inp), out, ws,
+                                         ws_bytes, None)
 
 
 def test_bad_prefill_arguments():
@@ -127,7 +127,6 @@ def test_bad_prefill_arguments():
     assert prefill(L, N=-1) == gdn.GDN_ERR_BAD_SHAPE
     assert prefill(L, max_len=-1) == gdn.GDN_ERR_BAD_SHAPE
     assert prefill(L, chunk=32) == gdn.GDN_ERR_UNSUPPORTED
-    assert prefill(qwen_layer(gate="channel")) == gdn.GDN_ERR_UNSUPPORTED
     assert prefill(qwen_layer(n_k_heads=2, n_v_heads=2, d_k=16, d_v=16)) == \
         gdn.GDN_ERR_UNSUPPORTED
     assert prefill(L, dst=None) == gdn.GDN_ERR_NULL_ARG
@@ -137,5 +136,25 @@ def test_bad_prefill_arguments():
     misaligned = GdnInputs(ct.c_void_p(0x10002), FAKE, FAKE, FAKE, None)
     assert prefill(L, inp=misaligned) == gdn.GDN_ERR_BAD_SHAPE
     assert prefill(L, N=0) == gdn.GDN_OK                  # nothing to do, nothing enqueued
-    # the fused kernel keeps every intermediate on chip
+    # the scalar-decay kernel keeps every intermediate on chip
     assert gdn.lib().gdn_prefill_workspace_size(ct.byref(L), 4, 8192, 32768, 64) == 0
+
+
+def test_per_channel_prefill_workspace():
+    """The per-channel-decay prefill stores one 2 KiB record per (16-token
+    block, value head): floor(total / 16) + 4 min(N, total) blocks."""
+    K = qwen_layer(gate="channel", n_k_heads=32, n_v_heads=32)
+    size = gdn.lib().gdn_prefill_workspace_size
+    assert size(ct.byref(K), 4, 8192, 32768, 64) == (2048 + 16) * 32 * 2048
+    assert size(ct.byref(K), 3, 100, 130, 64) == (8 + 12) * 32 * 2048
+    assert size(ct.byref(K), 1000, 1, 5, 64) == (0 + 20) * 32 * 2048   # empty sequences cost nothing
+    assert size(ct.byref(K), 0, 0, 0, 64) == 0
+    assert size(ct.byref(K), 4, 8192, 32768, 32) == 0                   # bad chunk
+    assert size(ct.byref(K), -1, 8192, 32768, 64) == 0
+    need = size(ct.byref(K), 2, 64, 128, 64)
+    # missing, short or misaligned workspace is refused before any launch
+    assert prefill(K) == gdn.GDN_ERR_WORKSPACE
+    assert prefill(K, ws=FAKE, ws_bytes=need - 1) == gdn.GDN_ERR_WORKSPACE
+    assert prefill(K, ws=ct.c_void_p(0x10080), ws_bytes=need) == gdn.GDN_ERR_WORKSPACE
+    assert prefill(K, N=0) == gdn.GDN_OK
+    assert prefill(K, chunk=32) == gdn.GDN_ERR_UNSUPPORTED
