@@ -288,26 +288,34 @@ def bench_kda_stack(torch, gdn, synth, K=20, W=3, layers=48):
 
 def prefill_counts(shape, seqlens):
     """Algorithmic bytes and FLOPs of one chunked prefill call, and the bf16
-    MFMA FLOPs the kernel issues.
+    MFMA FLOPs the kernels issue.
 
-    bytes: x read, o written (fp32), alpha/beta read, taps, and per sequence
-    the final state + conv window written and the initial ones read (zero
-    starts read nothing; counted as if every start were a copy).
+    bytes: x read, o written (fp32), alpha (per value head, or per value head
+    and key channel for the per-channel decay) and beta read, taps, and per
+    sequence the final state + conv window written and the initial ones read
+    (zero starts read nothing; counted as if every start were a copy).
     flops (dense, per (64-token chunk, value head)): the UT transform
     (K K^T, Q K^T, T V, W = T diag(e^g) K: 5.24 M) and the state pass
-    (W S0^T, Q S0^T, P U, U^T K: 6.29 M) -- 11.53 MFLOP at d = 128.
-    issued: per workgroup (64 value columns) and chunk, 20 Gram tiles and 4
-    waves of K S0^T, Q S0^T, P U and state-update tiles on 16x16x32 MFMAs;
-    on 16x16x16 MFMAs the U solve (10 block products per wave) and the four
-    diagonal-block inverses (8 products each); every product three times
-    (hi/lo split).  rocprofv3's SQ_INSTS_VALU_MFMA_MOPS_BF16 (x 512 FLOP)
-    agrees with this count."""
+    (W S0^T, Q S0^T, P U, U^T K: 6.29 M) -- 11.53 MFLOP at d = 128; the
+    per-channel decay changes elementwise factors only.
+    issued, scalar decay: per workgroup (64 value columns) and chunk, 20 Gram
+    tiles and 4 waves of K S0^T, Q S0^T, P U and state-update tiles on
+    16x16x32 MFMAs; on 16x16x16 MFMAs the U solve (10 block products per
+    wave) and the four diagonal-block inverses (8 products each).
+    issued, per-channel decay: 12 off-diagonal Gram tiles (the diagonal
+    blocks are formed without MFMA), the same K S0^T, Q S0^T and P U tiles,
+    and the state update as one 16x16x16 product per 16-token block.  Every
+    product runs three times (hi/lo split).  rocprofv3's
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 (x 512 FLOP) agrees with the scalar-decay
+    count."""
     act = 2 if shape.dtype == "bf16" else 4
     C, Hv, dk, dv = shape.channels, shape.n_v_heads, shape.d_k, shape.d_v
+    kda = shape.gate == "channel"
     total = int(sum(seqlens))
     state = Hv * dv * dk * 4 + (shape.conv_width - 1) * C * act
-    nbytes = total * (C * act + 2 * Hv * act + Hv * dv * 4) + C * shape.conv_width * act \
-        + 2 * state * len(seqlens)
+    gate_elems = Hv * dk if kda else Hv
+    nbytes = total * (C * act + (gate_elems + Hv) * act + Hv * dv * 4) \
+        + C * shape.conv_width * act + 2 * state * len(seqlens)
     chunks = sum(-(-L // 64) for L in seqlens)
     c, dense = 64, 0
     dense += 2 * c * c * dk * 2 + c * c * dv * 2 + c * c * dk * 2     # KK^T, QK^T, TV, TK
@@ -315,16 +323,22 @@ def prefill_counts(shape, seqlens):
     flops = dense * chunks * Hv
     nblk = -(-dv // 64)
     ksl, kdt = dk // 32, dk // 16
-    m32 = 20 * ksl * 3 + 4 * (4 * ksl * 2 * 3 + 6 * 3 + kdt * 2 * 3)
-    m16 = 4 * 10 * 3 + 4 * 8 * 3
+    if kda:
+        m32 = 12 * ksl * 3 + 4 * (4 * ksl * 2 * 3 + 6 * 3)
+        m16 = 4 * 10 * 3 + 4 * kdt * 4 * 3
+    else:
+        m32 = 20 * ksl * 3 + 4 * (4 * ksl * 2 * 3 + 6 * 3 + kdt * 2 * 3)
+        m16 = 4 * 10 * 3 + 4 * 8 * 3
     issued = (m32 * 16 * 16 * 32 * 2 + m16 * 16 * 16 * 16 * 2) * chunks * Hv * nblk
     return nbytes, flops, issued
 
 
-def bench_prefill(torch, gdn, synth, K=10, W=2, seqlens=(8192,) * 4):
-    """Chunked prefill, Qwen3.5 shape, 4 x 8192 tokens, chunk 64: sequences
-    alternate a zero start and a copy-on-write start from checkpoint slots."""
-    shape = synth.QWEN35
+def bench_prefill(torch, gdn, synth, K=10, W=2, seqlens=(8192,) * 4, shape=None):
+    """Chunked prefill, 4 x 8192 tokens, chunk 64, of the Qwen3.5 layer (scalar
+    decay) or the KDA layer (per-channel decay): sequences alternate a zero
+    start and a copy-on-write start from checkpoint slots."""
+    shape = shape or synth.QWEN35
+    kda = shape.gate == "channel"
     case = synth.prefill_case(shape, list(seqlens), 64, seed=17)
     dev = _dev(torch)
     g = gdn.Layer(shape.n_k_heads, shape.n_v_heads, shape.d_k, shape.d_v, shape.conv_width,
@@ -334,21 +348,28 @@ def bench_prefill(torch, gdn, synth, K=10, W=2, seqlens=(8192,) * 4):
     x, al, be, w = dev(case.x), dev(case.alpha), dev(case.beta), dev(case.conv_w)
     total = int(case.cu_seqlens[-1])
     out = torch.empty((total, shape.n_v_heads, shape.d_v), dtype=torch.float32, device="cuda")
+    need = gdn.gdn_prefill_workspace_size(g, len(seqlens), max(seqlens), total)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
 
     def call(_c):
-        gdn.gdn_prefill_chunked(g, ssm, conv, dst, init, cu, max(seqlens), x, al, be, w, out=out)
+        gdn.gdn_prefill_chunked(g, ssm, conv, dst, init, cu, max(seqlens), x, al, be, w, out=out,
+                                workspace=ws)
     for c in range(W):
         call(c)
     ms = time_calls(torch, call, W, K) / K
     nbytes, flops, issued = prefill_counts(shape, seqlens)
-    rec = path_record(ms, nbytes, total, "chunked prefill, Qwen3.5 shape, 4 x 8192 tokens, "
-                                         "chunk 64, zero / copy-on-write starts")
+    what = ("chunked prefill, KDA layer (32 heads, d=128, per-channel decay)" if kda else
+            "chunked prefill, Qwen3.5 shape") + \
+        ", 4 x 8192 tokens, chunk 64, zero / copy-on-write starts"
+    rec = path_record(ms, nbytes, total, what)
     rec["algorithmic_tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
     rec["algorithmic_flops"] = int(flops)
     rec["mfma_issued_bf16_flops"] = int(issued)
     rec["mfma_issued_tflops"] = round(issued / (ms * 1e-3) / 1e12, 1)
     rec["mfma_issued_frac_of_bf16_peak"] = round(issued / (ms * 1e-3) / 1e12 /
                                                  MFMA_BF16_PEAK_TFLOPS, 4)
+    if kda:
+        rec["workspace_bytes"] = int(need)
     return rec
 
 
@@ -371,7 +392,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "decode", "paths", "prefill", "copy"],
+    ap.add_argument("--only", choices=["all", "decode", "paths", "prefill", "prefill_kda",
+                                       "copy"],
                     default="all",
                     help="profiling runs: just the headline decode, the other paths, or a "
                          "plain copy of known size")
@@ -397,11 +419,15 @@ def main():
         return
     if args.only == "paths":
         for r in (bench_decode_b16(torch, gdn, synth), *bench_spec(torch, gdn, synth),
-                  bench_kda_stack(torch, gdn, synth), bench_prefill(torch, gdn, synth)):
+                  bench_kda_stack(torch, gdn, synth), bench_prefill(torch, gdn, synth),
+                  bench_prefill(torch, gdn, synth, shape=synth.KDA)):
             print(json.dumps(r), flush=True)
         return
     if args.only == "prefill":
         print(json.dumps(bench_prefill(torch, gdn, synth)), flush=True)
+        return
+    if args.only == "prefill_kda":
+        print(json.dumps(bench_prefill(torch, gdn, synth, shape=synth.KDA)), flush=True)
         return
 
     shape = synth.QWEN35
@@ -430,14 +456,15 @@ def main():
     paths = None
     if args.only == "all":
         log("bench: other paths (B=16 decode, speculative draft + commit, KDA 48-layer stack, "
-            "chunked prefill)")
+            "chunked prefill of both layers)")
         d16 = bench_decode_b16(torch, gdn, synth)
         draft, commit = bench_spec(torch, gdn, synth)
         kda = bench_kda_stack(torch, gdn, synth)
         pf = bench_prefill(torch, gdn, synth)
+        pfk = bench_prefill(torch, gdn, synth, shape=synth.KDA)
         paths = {"decode_qwen35_b16": d16, "spec_draft_qwen35_b64_t7": draft,
                  "spec_commit_qwen35_b64": commit, "kda_stack_b64_48layers": kda,
-                 "prefill_qwen35_4x8192": pf}
+                 "prefill_qwen35_4x8192": pf, "prefill_kda_4x8192": pfk}
 
     cpu = None
     if not args.no_cpu_baseline and args.only == "all":

@@ -381,56 +381,23 @@ struct Prefill : PrefillCore<DK, Act> {
     diag_inverse(B, g);
   }
 
-  // Bl(X Y) from X in A-operand layout (X[lr][4 lg + v]) and Y in
-  // B-operand layout (Y[4 lg + v][lr]); the result is in B layout.  N
-  // independent products at once, their MFMAs interleaved.
-  template <int N>
-  __device__ __forceinline__ void mm(const f4 (&x)[N], const f4 (&y)[N], f4 (&r)[N]) const {
-    s4 xh[N], xl[N], yh[N], yl[N];
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-      split4(x[n], xh[n], xl[n]);
-      split4(y[n], yh[n], yl[n]);
-      r[n] = f4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int n = 0; n < N; ++n) r[n] = mma16(xl[n], yh[n], r[n]);
-#pragma unroll
-    for (int n = 0; n < N; ++n) r[n] = mma16(xh[n], yl[n], r[n]);
-#pragma unroll
-    for (int n = 0; n < N; ++n) r[n] = mma16(xh[n], yh[n], r[n]);
-  }
-
   // Diagonal block b from its raw K K^T tile G: N = the strictly lower block
   // of A, X = (I + N)^{-1}, stored in A layout (X[lr][4 lg + v]) in the
-  // diagonal block of the A planes.  All factors are polynomials in N and
-  // commute, so X^T is built in B layout: X^T = Q2 + (N^8)^T Q2,
-  // Q2 = Q1 + (N^4)^T Q1, Q1 = I - N^T + (N^2)^T - N^T (N^2)^T.
+  // diagonal block of the A planes.
   __device__ void diag_inverse(int b, const f4& G) const {
     const int l = lane_now(), lr = l & 15, lg = l >> 4;
     const float* gt = fp(P::oGate);
     const float gi = gt[16 * b + lr], bi = gt[kC + 16 * b + lr];
     const f4 gr = *reinterpret_cast<const f4*>(gt + 16 * b + 4 * lg);
     const f4 br = *reinterpret_cast<const f4*>(gt + kC + 16 * b + 4 * lg);
-    f4 nb, na, id;
+    f4 nb, na;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int rv = 4 * lg + v;
       nb[v] = lr < rv ? br[v] * __expf(gr[v] - gi) * G[v] : 0.f;  // N[rv][lr]
       na[v] = rv < lr ? bi * __expf(gi - gr[v]) * G[v] : 0.f;     // N[lr][rv]
-      id[v] = rv == lr ? 1.f : 0.f;
     }
-    f4 l1[2];                                   // N^2 in B and A layout
-    mm<2>({na, nb}, {nb, na}, l1);
-    f4 l2[3];                                   // N^4 (B, A), N^T (N^2)^T
-    mm<3>({l1[1], l1[0], nb}, {l1[0], l1[1], l1[1]}, l2);
-    const f4 q1 = id - na + l1[1] - l2[2];
-    f4 l3[2];                                   // N^8 (B), (N^4)^T Q1
-    mm<2>({l2[1], l2[0]}, {l2[0], q1}, l3);
-    const f4 q2 = q1 + l3[1];
-    f4 l4[1];
-    mm<1>({l3[0]}, {q2}, l4);
-    const f4 xt = q2 + l4[0];
+    const f4 xt = unit_lower_inverse(na, nb, lr, lg);
     s4 xh, xl;
     split4(xt, xh, xl);
     const int o = (16 * b + lr) * P::kRowT + slot(16 * b + 4 * lg);

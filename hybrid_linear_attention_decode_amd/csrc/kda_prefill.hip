@@ -65,24 +65,23 @@ struct DiagPlan {
   static constexpr int oA = oK + kBlk * kRow * 4;
   static constexpr int oN = oA + kBlk * kRow * 4;  // fp32 [16][16]
   static constexpr int oP = oN + kBlk * kBlk * 4;
-  static constexpr int oX = oP + kBlk * kBlk * 4;
-  static constexpr int oBeta = oX + kBlk * kBlk * 4;
+  static constexpr int oBeta = oP + kBlk * kBlk * 4;
   static constexpr int kBytes = oBeta + kBlk * 4;
 };
 
 template <int DK, typename Act>
-__global__ void __launch_bounds__(64) kda_diag_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(64, 4) kda_diag_kernel(PrefillArgs a) {
   using DP = DiagPlan<DK>;
   constexpr int kGrp = DK / 8;       // channel octets per head
   constexpr int kTpl = kGrp / 2;     // tokens per lane in the conv stage
   constexpr int kCw = DK / 8;        // channels per lane in the pair stage
+  constexpr int kAo = DK / 32;       // decay octets per lane
   __shared__ __align__(16) unsigned char lds[DP::kBytes];
   float* yq = reinterpret_cast<float*>(lds + DP::oQ);
   float* yk = reinterpret_cast<float*>(lds + DP::oK);
   float* al = reinterpret_cast<float*>(lds + DP::oA);
   float* nm = reinterpret_cast<float*>(lds + DP::oN);
   float* pm = reinterpret_cast<float*>(lds + DP::oP);
-  float* xm = reinterpret_cast<float*>(lds + DP::oX);
   float* bt = reinterpret_cast<float*>(lds + DP::oBeta);
 
   const int lane = threadIdx.x;
@@ -115,6 +114,8 @@ __global__ void __launch_bounds__(64) kda_diag_kernel(PrefillArgs a) {
     wt[m] = f4{core.tap(ch + m, 0), core.tap(ch + m, 1), core.tap(ch + m, 2), core.tap(ch + m, 3)};
     bias[m] = a.bias ? to_f32(static_cast<const Act*>(a.bias)[ch + m]) : 0.f;
   }
+  // decay stage: lane = (token r, channel quarter q4)
+  const int ar = lane >> 2, aq = lane & 3;
   // pair stage: lane = (channel group cg, column pair cp): columns cp and
   // 15 - cp, 17 (row, column) steps in all, channels cg * kCw ..
   const int cg = lane & 7, cp = lane >> 3;
@@ -122,10 +123,13 @@ __global__ void __launch_bounds__(64) kda_diag_kernel(PrefillArgs a) {
 
   for (int jb = blockIdx.y; jb < nb; jb += gridDim.y) {
     const int tb = jb * kBlk;   // first token of the block
-    // ---- conv1d + SiLU + L2 norm of q and k ----
+    const int n = T - tb < kBlk ? (T > tb ? T - tb : 0) : kBlk;
+    // ---- loads: raw q / k rows (and the initial window), decays, b ----
+    Row8<Act> raw[kTpl + 3];
+    Row8<Act> dv[kAo];
+    float bv = 0.f;
     {
       const rsrc_t rx = core.x_rows(tb);
-      Row8<Act> raw[kTpl + 3];
 #pragma unroll
       for (int r = 0; r < kTpl + 3; ++r)
         raw[r].load(rx, core.x_off(tb, tb + kTpl * tg - 3 + r, ch));
@@ -138,82 +142,81 @@ __global__ void __launch_bounds__(64) kda_diag_kernel(PrefillArgs a) {
           raw[r].merge(wr);
         }
       }
-#pragma unroll
-      for (int tt = 0; tt < kTpl; ++tt) {
-        float y[8], ss = 0.f;
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          float v = bias[m];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) v = fmaf(wt[m][jj], raw[tt + jj].get(m), v);
-          v = core.act(v);
-          y[m] = v;
-          ss = fmaf(v, v, ss);
-        }
-        const float sum = group_sum<kGrp>(ss);
-        float sc = a.l2norm ? rsqrtf(sum + a.eps) : 1.0f;
-        if (!isk) sc *= a.q_scale;
-        const int tok = kTpl * tg + tt;
-        if (tb + tok >= T) sc = 0.f;
-        float* row = (isk ? yk : yq) + tok * DP::kRow + 8 * oc;
-        *reinterpret_cast<f4*>(row) = f4{y[0], y[1], y[2], y[3]} * sc;
-        *reinterpret_cast<f4*>(row + 4) = f4{y[4], y[5], y[6], y[7]} * sc;
-      }
-    }
-    // ---- decays (1 past the sequence) and b ----
-    {
-      const int n = T - tb < kBlk ? (T > tb ? T - tb : 0) : kBlk;
       const int64_t rowe = static_cast<int64_t>(a.Hv) * DK;
       const rsrc_t ra = make_rsrc(static_cast<const Act*>(a.alpha) + (t0 + static_cast<int64_t>(tb)) * rowe,
                                   static_cast<uint32_t>(n * rowe * sizeof(Act)));
-      const int r = lane >> 2, q4 = lane & 3;  // token r, channel quarter q4
 #pragma unroll
-      for (int o = 0; o < DK / 32; ++o) {
-        const int c = 8 * (4 * o + q4);
-        Row8<Act> v;
-        v.load(ra, static_cast<int>(((r * a.Hv + h) * DK + c) * sizeof(Act)));
-        float* dstp = al + r * DP::kRow + c;
-        f4 lo4, hi4;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          lo4[m] = r < n ? v.get(m) : 1.f;
-          hi4[m] = r < n ? v.get(m + 4) : 1.f;
-        }
-        *reinterpret_cast<f4*>(dstp) = lo4;
-        *reinterpret_cast<f4*>(dstp + 4) = hi4;
-      }
-      if (lane < kBlk)
-        bt[lane] = lane < n ? to_f32(static_cast<const Act*>(a.beta)[(t0 + static_cast<int64_t>(tb) + lane) * a.Hv + h])
-                            : 0.f;
+      for (int o = 0; o < kAo; ++o)
+        dv[o].load(ra, static_cast<int>(((ar * a.Hv + h) * DK + 8 * (4 * o + aq)) * sizeof(Act)));
+      if (lane < n)
+        bv = to_f32(static_cast<const Act*>(a.beta)[(t0 + static_cast<int64_t>(tb) + lane) * a.Hv + h]);
     }
+    // ---- conv1d + SiLU + L2 norm of q and k ----
+#pragma unroll
+    for (int tt = 0; tt < kTpl; ++tt) {
+      float y[8], ss = 0.f;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        float v = bias[m];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) v = fmaf(wt[m][jj], raw[tt + jj].get(m), v);
+        v = core.act(v);
+        y[m] = v;
+        ss = fmaf(v, v, ss);
+      }
+      const float sum = group_sum<kGrp>(ss);
+      float sc = a.l2norm ? rsqrtf(sum + a.eps) : 1.0f;
+      if (!isk) sc *= a.q_scale;
+      const int tok = kTpl * tg + tt;
+      if (tb + tok >= T) sc = 0.f;
+      float* row = (isk ? yk : yq) + tok * DP::kRow + 8 * oc;
+      *reinterpret_cast<f4*>(row) = f4{y[0], y[1], y[2], y[3]} * sc;
+      *reinterpret_cast<f4*>(row + 4) = f4{y[4], y[5], y[6], y[7]} * sc;
+    }
+    // decays (1 past the sequence) and b
+#pragma unroll
+    for (int o = 0; o < kAo; ++o) {
+      float* dstp = al + ar * DP::kRow + 8 * (4 * o + aq);
+      f4 lo4, hi4;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        lo4[m] = ar < n ? dv[o].get(m) : 1.f;
+        hi4[m] = ar < n ? dv[o].get(m + 4) : 1.f;
+      }
+      *reinterpret_cast<f4*>(dstp) = lo4;
+      *reinterpret_cast<f4*>(dstp + 4) = hi4;
+    }
+    if (lane < kBlk) bt[lane] = bv;
     lds_barrier();
-    // ---- N and P by products of the decays ----
+    // ---- N and P by products of the decays, 4 channels at a time ----
     {
-      float w[kCw], accn[17], accp[17];
+      float accn[17], accp[17];
 #pragma unroll
-      for (int st = 0; st < 17; ++st) {
-        const bool first = st < 16 - cp;
-        const int i = first ? cp : 15 - cp;
-        const int r = first ? cp + st : st - 1;
-        const float* kr = yk + r * DP::kRow + cg * kCw;
-        const float* qr = yq + r * DP::kRow + cg * kCw;
-        const float* ar = al + r * DP::kRow + cg * kCw;
-        const bool start = r == i;
-        float sn = 0.f, sp = 0.f;
+      for (int st = 0; st < 17; ++st) accn[st] = accp[st] = 0.f;
+      for (int c4 = 0; c4 < kCw; c4 += 4) {
+        f4 w = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c4 = 0; c4 < kCw; c4 += 4) {
-          const f4 kv = *reinterpret_cast<const f4*>(kr + c4);
-          const f4 qv = *reinterpret_cast<const f4*>(qr + c4);
-          const f4 av = *reinterpret_cast<const f4*>(ar + c4);
+        for (int st = 0; st < 17; ++st) {
+          const bool first = st < 16 - cp;
+          const int i = first ? cp : 15 - cp;
+          const int r = first ? cp + st : st - 1;
+          const int off = r * DP::kRow + cg * kCw + c4;
+          const f4 kv = *reinterpret_cast<const f4*>(yk + off);
+          const f4 qv = *reinterpret_cast<const f4*>(yq + off);
+          const f4 av = *reinterpret_cast<const f4*>(al + off);
+          const bool start = r == i;
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
-            w[c4 + m] = start ? kv[m] : w[c4 + m] * av[m];
-            sn = fmaf(kv[m], w[c4 + m], sn);
-            sp = fmaf(qv[m], w[c4 + m], sp);
+            w[m] = start ? kv[m] : w[m] * av[m];
+            accn[st] = fmaf(kv[m], w[m], accn[st]);
+            accp[st] = fmaf(qv[m], w[m], accp[st]);
           }
         }
-        accn[st] = group_sum<8>(sn);
-        accp[st] = group_sum<8>(sp);
+      }
+#pragma unroll
+      for (int st = 0; st < 17; ++st) {
+        accn[st] = group_sum<8>(accn[st]);
+        accp[st] = group_sum<8>(accp[st]);
       }
       if (cg == 0) {
 #pragma unroll
@@ -227,34 +230,25 @@ __global__ void __launch_bounds__(64) kda_diag_kernel(PrefillArgs a) {
       }
     }
     lds_barrier();
-    // ---- X = (I + N)^{-1}: lane i < 16 solves for column i ----
-    if (lane < kBlk) {
-      float x[kBlk];
-#pragma unroll
-      for (int r = 0; r < kBlk; ++r) {
-        float v = r == lane ? 1.f : 0.f;
-#pragma unroll
-        for (int j = 0; j < r; ++j) v = fmaf(-nm[r * kBlk + j], x[j], v);
-        x[r] = v;
-        xm[r * kBlk + lane] = v;
-      }
-    }
-    lds_barrier();
-    // ---- write the record ----
+    // ---- X = (I + N)^{-1} on MFMA, and the record ----
     {
-      const int r = lane >> 2, q4 = lane & 3;
-      const f4 xv = *reinterpret_cast<const f4*>(xm + r * kBlk + 4 * q4);
-      const f4 pv = *reinterpret_cast<const f4*>(pm + r * kBlk + 4 * q4);
+      const int lr = lane & 15, lg = lane >> 4;
+      f4 na, nb;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        na[v] = nm[lr * kBlk + 4 * lg + v];
+        nb[v] = nm[(4 * lg + v) * kBlk + lr];
+      }
+      const f4 xv = unit_lower_inverse(na, nb, lr, lg);      // X[lr][4 lg + v]
+      const f4 pv = *reinterpret_cast<const f4*>(pm + lr * kBlk + 4 * lg);
       s4 xh, xl, ph, pl;
       split4(xv, xh, xl);
       split4(pv, ph, pl);
       typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-      const u4 w0 = __builtin_bit_cast(u4, cat(xh, xl));
-      const u4 w1 = __builtin_bit_cast(u4, cat(ph, pl));
       unsigned char* rec = static_cast<unsigned char*>(a.ws) +
-                           (ws_block(s, t0, jb) * a.Hv + h) * kWsBlockBytes + lane * 32;
-      *reinterpret_cast<u4*>(rec) = w0;
-      *reinterpret_cast<u4*>(rec + 16) = w1;
+                           (ws_block(s, t0, jb) * a.Hv + h) * kWsBlockBytes + (4 * lr + lg) * 32;
+      *reinterpret_cast<u4*>(rec) = __builtin_bit_cast(u4, cat(xh, xl));
+      *reinterpret_cast<u4*>(rec + 16) = __builtin_bit_cast(u4, cat(ph, pl));
     }
     lds_barrier();  // the next block reuses the LDS
   }
@@ -377,46 +371,61 @@ struct KdaChunk : PrefillCore<DK, Act> {
     }
   }
 
-  // Decay of token 8 tau + tt at channel m of the thread's octet (1 past the
-  // sequence), re-read from the packed rows at every use: an opaque copy
-  // keeps the compiler from holding 64 unpacked values across the passes.
-  __device__ __forceinline__ float dec(const Prod& p, int tt, int m, bool in) const {
+  // Decay of token 8 tau + tt at channel m of the thread's octet, unpacked
+  // from an opaque copy of its word: the backward pass's 64 unpacked values
+  // are then not held until the forward pass unpacks them again.
+  __device__ __forceinline__ float dec(const Prod& p, int tt, int m) const {
     Row8<Act> r;
 #pragma unroll
     for (int i = 0; i < Row8<Act>::kWords; ++i) r.w[i] = 0;
     r.w[m * Row8<Act>::kWords / 8] = static_cast<uint32_t>(opaque(static_cast<int>(p.dec[tt].w[m * Row8<Act>::kWords / 8])));
-    return in ? r.get(m) : 1.f;
+    return r.get(m);
   }
 
   // conv + SiLU + L2 norm (+ q scale), the decay products and the planes of
-  // chunk c0.  The octet's total decay and its partner's (the other half of
-  // the 16-token block, kNco lanes away) start a forward pass (conv, the
-  // normalised rows, KE / QE with the running prefix product E) and a
-  // backward pass (KF with the running suffix product F).
+  // chunk c0, in one forward pass over the octet's tokens.  A backward pass
+  // over the decays first gives the octet's total and the suffix products
+  // F the thread needs (a k thread keeps tokens 0..3 of the KF rows, its q
+  // partner kGrp lanes away -- same channels, same decays -- takes 4..7 and
+  // receives those k rows by shuffle); the partner octet of the 16-token
+  // block (kNco lanes away) supplies the missing factor of E and F.
   __device__ void prod_prep(Prod& p, int c0) const {
     const float* wl = fp(P::oW);
     const float* bl = fp(P::oB);
     load_diag(p, c0);
     if (p.on) {
       const int tbase = c0 + 8 * p.tau;
-      float tot[8];
+      if (tbase + 8 > T) {      // decays of tokens past the sequence read 1
+        constexpr uint32_t kOne = sizeof(Act) == 2 ? 0x3F803F80u : 0x3F800000u;
 #pragma unroll
-      for (int m = 0; m < 8; ++m) tot[m] = 1.f;
+        for (int tt = 0; tt < 8; ++tt)
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt)
+          for (int i = 0; i < Row8<Act>::kWords; ++i)
+            p.dec[tt].w[i] = tbase + tt < T ? p.dec[tt].w[i] : kOne;
+      }
+      float fs[4][8], run[8];
 #pragma unroll
-        for (int m = 0; m < 8; ++m) tot[m] = tot[m] * dec(p, tt, m, tbase + tt < T);
+      for (int m = 0; m < 8; ++m) run[m] = 1.f;
+#pragma unroll
+      for (int tt = 7; tt >= 0; --tt) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          if (tt >= 4)
+            fs[tt - 4][m] = run[m];
+          else
+            fs[tt][m] = p.isk ? run[m] : fs[tt][m];
+          run[m] = run[m] * dec(p, tt, m);
+        }
+      }
       const bool odd = p.tau & 1;
-      float run[8], pt[8];
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        pt[m] = __shfl_xor(tot[m], kNco);
-        run[m] = odd ? pt[m] : 1.f;
-        p.lam[m] = pt[m] * tot[m];
+        const float pt = __shfl_xor(run[m], kNco);   // the partner octet's total
+        p.lam[m] = pt * run[m];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fs[j][m] = odd ? fs[j][m] : fs[j][m] * pt;
+        run[m] = odd ? pt : 1.f;                      // E starts at the partner's total
       }
-      // k rows for the KF plane: a k thread keeps its own tokens 0..3, its q
-      // partner (kGrp lanes away, same channels and decays) takes 4..7
-      float kf[4][8];
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
         const bool in = tbase + tt < T;
@@ -436,43 +445,25 @@ struct KdaChunk : PrefillCore<DK, Act> {
         float sc = a.l2norm ? rsqrtf(sum + a.eps) : 1.0f;
         if (!p.isk) sc *= a.q_scale;
         if (!in) sc = 0.f;
-        f4 ve[2];
+        f4 ve[2], vf[2];
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
           const float yv = y[m] * sc;
-          if (tt < 4) {
-            kf[tt][m] = yv;
-          } else {
-            const float other = __shfl_xor(yv, kGrp);
-            kf[tt - 4][m] = p.isk ? kf[tt - 4][m] : other;
-          }
-          run[m] = run[m] * dec(p, tt, m, in);
+          run[m] = run[m] * p.dec[tt].get(m);
           ve[m >> 2][m & 3] = yv * run[m];
+          const float kv = tt < 4 ? yv : __shfl_xor(yv, kGrp);
+          vf[m >> 2][m & 3] = kv * fs[tt & 3][m];
         }
         split4(ve[0], p.eh[tt][0], p.el[tt][0]);
         split4(ve[1], p.eh[tt][1], p.el[tt][1]);
-      }
-#pragma unroll
-      for (int m = 0; m < 8; ++m) run[m] = odd ? 1.f : pt[m];
-#pragma unroll
-      for (int tt = 7; tt >= 0; --tt) {
-        const int jx = tt & 3;
-        f4 vf[2];
-#pragma unroll
-        for (int m = 0; m < 8; ++m) vf[m >> 2][m & 3] = kf[jx][m] * run[m];
         s4 h0, l0, h1, l1;
         split4(vf[0], h0, l0);
         split4(vf[1], h1, l1);
-        if (tt >= 4 || p.isk) {
-          p.fh[jx][0] = h0;
-          p.fh[jx][1] = h1;
-          p.fl[jx][0] = l0;
-          p.fl[jx][1] = l1;
-        }
-        if (tt > 0) {
-          const bool in = tbase + tt < T;
-#pragma unroll
-          for (int m = 0; m < 8; ++m) run[m] = run[m] * dec(p, tt, m, in);
+        if (tt < 4 || !p.isk) {
+          p.fh[tt & 3][0] = h0;
+          p.fh[tt & 3][1] = h1;
+          p.fl[tt & 3][0] = l0;
+          p.fl[tt & 3][1] = l1;
         }
       }
     }
@@ -895,23 +886,24 @@ __global__ void __launch_bounds__(kThreads, 1) kda_chunk_kernel(PrefillArgs a) {
     k.prod_init(p);
     if (nch > 0) k.prod_load(p, 0);
     lds_barrier();            // planes zeroed, taps loaded
+    // The next chunk's raw rows and decays are fetched right after a chunk's
+    // planes are stored (into the registers the stored results free), and
+    // land during the off-diagonal blocks and the wait for the consumers.
     if (nch > 0) {
       k.prod_prep(p, 0);
-      if (nch > 1) k.prod_load(p, kC);
       k.prod_store(p);
+      if (nch > 1) k.prod_load(p, kC);
       lds_barrier();
       k.gram_phase();
       lds_barrier();
     }
     for (int c = 0; c < nch; ++c) {
       const bool next = c + 1 < nch;
-      if (next) {
-        k.prod_prep(p, (c + 1) * kC);
-        if (c + 2 < nch) k.prod_load(p, (c + 2) * kC);
-      }
+      if (next) k.prod_prep(p, (c + 1) * kC);
       lds_barrier();          // consumers are done with chunk c
       if (next) {
         k.prod_store(p);
+        if (c + 2 < nch) k.prod_load(p, (c + 2) * kC);
         lds_barrier();
         k.gram_phase();
         lds_barrier();

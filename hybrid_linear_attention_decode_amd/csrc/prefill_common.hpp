@@ -115,6 +115,50 @@ struct Row8 {
   }
 };
 
+// Bl(X Y) from X in A-operand layout (X[lr][4 lg + v]) and Y in B-operand
+// layout (Y[4 lg + v][lr]) of 16x16 tiles; the result is in B layout.  N
+// independent products at once, their MFMAs interleaved, each on (hi, lo)
+// split operands.
+template <int N>
+__device__ __forceinline__ void mm_split(const f4 (&x)[N], const f4 (&y)[N], f4 (&r)[N]) {
+  s4 xh[N], xl[N], yh[N], yl[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    split4(x[n], xh[n], xl[n]);
+    split4(y[n], yh[n], yl[n]);
+    r[n] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int n = 0; n < N; ++n) r[n] = mma16(xl[n], yh[n], r[n]);
+#pragma unroll
+  for (int n = 0; n < N; ++n) r[n] = mma16(xh[n], yl[n], r[n]);
+#pragma unroll
+  for (int n = 0; n < N; ++n) r[n] = mma16(xh[n], yh[n], r[n]);
+}
+
+// X = (I + N)^{-1} for a strictly lower triangular 16x16 N given in both
+// layouts (na[v] = N[lr][4 lg + v], nb[v] = N[4 lg + v][lr]); returns
+// X[lr][4 lg + v].  N is nilpotent (N^16 = 0), so
+// X = (I - N)(I + N^2)(I + N^4)(I + N^8); all factors are polynomials in N
+// and commute, so X^T is built in B layout: X^T = Q2 + (N^8)^T Q2,
+// Q2 = Q1 + (N^4)^T Q1, Q1 = I - N^T + (N^2)^T - N^T (N^2)^T.
+__device__ __forceinline__ f4 unit_lower_inverse(const f4& na, const f4& nb, int lr, int lg) {
+  f4 id;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) id[v] = 4 * lg + v == lr ? 1.f : 0.f;
+  f4 l1[2];                                   // N^2 in B and A layout
+  mm_split<2>({na, nb}, {nb, na}, l1);
+  f4 l2[3];                                   // N^4 (B, A), N^T (N^2)^T
+  mm_split<3>({l1[1], l1[0], nb}, {l1[0], l1[1], l1[1]}, l2);
+  const f4 q1 = id - na + l1[1] - l2[2];
+  f4 l3[2];                                   // N^8 (B), (N^4)^T Q1
+  mm_split<2>({l2[1], l2[0]}, {l2[0], q1}, l3);
+  const f4 q2 = q1 + l3[1];
+  f4 l4[1];
+  mm_split<1>({l3[0]}, {q2}, l4);
+  return q2 + l4[0];
+}
+
 // Element offset of storage slot sl of row r in a [token][d_k] bf16 plane.
 // Rows of d_k = 128 (256 bytes, all 64 banks) are swizzled: 16-byte chunk c
 // of row r sits at chunk c ^ (((r & 3) << 2) | ((r >> 2) & 3)), so both the
