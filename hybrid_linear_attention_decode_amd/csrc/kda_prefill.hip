@@ -320,13 +320,17 @@ struct KdaChunk : PrefillCore<DK, Act> {
     p.ch = (p.isk ? a.Hk * DK : 0) + hk * DK + 8 * p.oc;
   }
 
+  // Taps and bias of the key head's q and k channels, stored [m][octet] (m =
+  // channel within the octet) so that the lanes of one wave, one octet each,
+  // read 16 consecutive bytes apiece at every m.
   __device__ void load_taps() const {
     float* wt = fp(P::oW);
     float* bs = fp(P::oB);
     for (int i = tid; i < 2 * DK; i += kThreads) {
       const int ch = i < DK ? hk * DK + i : a.Hk * DK + hk * DK + (i - DK);
-      *reinterpret_cast<f4*>(wt + 4 * i) = f4{tap(ch, 0), tap(ch, 1), tap(ch, 2), tap(ch, 3)};
-      bs[i] = a.bias ? to_f32(static_cast<const Act*>(a.bias)[ch]) : 0.f;
+      const int at = (i & 7) * kNco + (i >> 3);
+      *reinterpret_cast<f4*>(wt + 4 * at) = f4{tap(ch, 0), tap(ch, 1), tap(ch, 2), tap(ch, 3)};
+      bs[at] = a.bias ? to_f32(static_cast<const Act*>(a.bias)[ch]) : 0.f;
     }
   }
 
@@ -430,11 +434,11 @@ struct KdaChunk : PrefillCore<DK, Act> {
       for (int tt = 0; tt < 8; ++tt) {
         const bool in = tbase + tt < T;
         float y[8], ss = 0.f;
-        const int cw = 8 * opaque(p.co);   // taps re-read per token, not held
+        const int cw = opaque(p.co);   // taps re-read per token, not held
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-          const f4 wt = *reinterpret_cast<const f4*>(wl + 4 * (cw + m));
-          float v = bl[cw + m];
+          const f4 wt = *reinterpret_cast<const f4*>(wl + 4 * (m * kNco + cw));
+          float v = bl[m * kNco + cw];
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) v = fmaf(wt[jj], p.raw[tt + jj].get(m), v);
           v = act(v);

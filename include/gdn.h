@@ -156,18 +156,26 @@ gdn_status gdn_spec_decode_commit(const gdn_layer* layer, const gdn_pool* pool,
 /*
  * Chunked prefill of N variable-length sequences ("Scheduler dual": prefill
  * populates the initial state; "Riesgo de correctitud": a fresh working slot
- * starts from a clean checkpoint copy or from zeros).
+ * starts from a clean checkpoint copy or from zeros).  Both gate kinds: the
+ * scalar decay (GDN) and the per-channel decay (KDA, the fine-grained gate of
+ * the Kimi K3 layers the pages name).
  *   dst_slots [N] int32 (device): the working slot each sequence writes.
  *   init_slot [N] int32 (device) or NULL: -1 = start from zero state and zero
  *     conv window; s >= 0 = start from slot s (s == dst continues in place,
  *     any other s is a copy-on-write source that is only read).  NULL means
  *     init_slot == dst_slots.  No init slot may be another sequence's dst.
  *   cu_seqlens [N+1] int32 (device), cu_seqlens[0] == 0, non-decreasing;
- *     max_seqlen (host) >= every length; total_tokens (host) == cu_seqlens[N].
- *   chunk: 64 (the only chunk length built).
+ *     max_seqlen (host) >= every length (it sizes a launch grid; a smaller
+ *     value stays correct, only slower); total_tokens (host) == cu_seqlens[N].
+ *   chunk: 64 (the only chunk length built).  d_k in {32, 64, 128}.
+ *   in->alpha: [total][H_v] (scalar decay) or [total][H_v][d_k] (per-channel
+ *     decay, 16-byte aligned).
  *   out [total][H_v][d_v] fp32.
  *   workspace: device scratch of at least gdn_prefill_workspace_size() bytes,
- *     256-byte aligned.
+ *     256-byte aligned, owned by the caller and free again when the call's
+ *     stream work has finished (the scalar decay needs none; the per-channel
+ *     decay stores its diagonal blocks there).  Missing, short or misaligned:
+ *     GDN_ERR_WORKSPACE, nothing enqueued.
  */
 gdn_status gdn_prefill_chunked(const gdn_layer* layer, const gdn_pool* pool,
                                const int32_t* dst_slots, const int32_t* init_slot, int32_t N,
@@ -176,7 +184,9 @@ gdn_status gdn_prefill_chunked(const gdn_layer* layer, const gdn_pool* pool,
                                float* out, void* workspace, size_t workspace_bytes,
                                void* stream);
 
-/* Bytes of workspace gdn_prefill_chunked needs for these sizes (0 on bad args). */
+/* Bytes of workspace gdn_prefill_chunked needs for these sizes: 0 for the
+ * scalar decay; for the per-channel decay 2048 * H_v * (floor(total/16) +
+ * 4 * min(N, total)).  0 on bad arguments. */
 size_t gdn_prefill_workspace_size(const gdn_layer* layer, int32_t N, int32_t max_seqlen,
                                   int32_t total_tokens, int32_t chunk);
 
