@@ -83,7 +83,7 @@ class DecodeBench:
     states replicated over all slots (values do not change the traffic)."""
 
     def __init__(self, torch, gdn, synth, shape, B, slots, n_calls, seed, n_inputs=64,
-                 n_distinct_slots=64, T=1, spec=False):
+                 n_distinct_slots=64, T=1, spec=False, spec_pool=False):
         self.torch = torch
         rs = synth.streams(seed)
         base = synth.make_pool(shape, n_distinct_slots, np.arange(n_distinct_slots), rs)
@@ -117,7 +117,21 @@ class DecodeBench:
         self.Lref, self.Pref = ct.byref(self.L), ct.byref(self.P)
         self.inref = [ct.byref(i) for i in self.inputs]
         self.spec = None
-        if spec:
+        self.specs = None
+        if spec and spec_pool:
+            # per call, B*T snapshot slots drawn from the slots no request of
+            # that call works on
+            g = np.random.default_rng(seed)
+            tab = np.empty((n_calls, B, T), np.int32)
+            for c in range(n_calls):
+                free = np.setdiff1d(np.arange(slots, dtype=np.int32), self.idx_host[c])
+                tab[c] = g.permutation(free)[:B * T].reshape(B, T)
+            self.spec_slots_host = tab
+            self.spec_slots = dev(tab)
+            self.S_list = [gdn.GdnSpecCache(None, None, T, self.spec_slots[c].data_ptr())
+                           for c in range(n_calls)]
+            self.specs = [ct.byref(x) for x in self.S_list]
+        elif spec:
             self.spec_ssm = torch.empty((B, T) + tuple(self.ssm.shape[1:]), dtype=torch.float32,
                                         device="cuda")
             self.spec_conv = torch.empty((B, T) + tuple(self.conv.shape[1:]),
@@ -126,8 +140,9 @@ class DecodeBench:
             self.spec = ct.byref(self.S)
 
     def call(self, c: int):
-        st = self.fn(self.Lref, self.Pref, self.idx_ptrs[c], self.B, self.T,
-                     self.inref[c % self.n_inputs], self.out_ptr, self.spec, self.stream)
+        spec = self.specs[c] if self.specs is not None else self.spec
+        st = self.fn(self.Lref, self.Pref, self.idx_ptrs[c], None, self.B, self.T,
+                     self.inref[c % self.n_inputs], self.out_ptr, spec, self.stream)
         if st != 0:
             raise RuntimeError(f"gdn_decode_step failed with status {st}")
 
@@ -233,6 +248,42 @@ def bench_spec(torch, gdn, synth, K=100, W=10):
     return draft, rec
 
 
+def bench_spec_pool(torch, gdn, synth, K=100, W=10):
+    """The same draft with each snapshot written to a pool slot of its own
+    (448 distinct slots per call, none a working slot), then the commit by
+    index: the accepted snapshot's slot becomes the request's working slot,
+    no state is copied."""
+    shape = synth.QWEN35
+    B, T = 64, 7
+    b = DecodeBench(torch, gdn, synth, shape, B, 1024, W + K, seed=2, n_inputs=8, T=T, spec=True,
+                    spec_pool=True)
+    for c in range(W):
+        b.call(c)
+    ms_draft = time_calls(torch, b.call, W, K) / K
+    draft = path_record(ms_draft, decode_bytes(shape, B, T, spec=True), B * T,
+                        "speculative draft, Qwen3.5 shape, B=64, 7 tokens, snapshots into pool "
+                        "slots")
+    acc = torch.from_numpy(synth.accepted_lengths(B, T, seed=2)).cuda()
+    idx = b.idx[0].clone()
+    released = torch.empty_like(idx)
+    fn = gdn.lib().gdn_spec_commit_index
+    P = ct.byref(b.P)
+    args = [(b.specs[c], ct.c_void_p(acc.data_ptr()), ct.c_void_p(idx.data_ptr()),
+             ct.c_void_p(released.data_ptr())) for c in range(W + K)]
+
+    def commit(c):
+        st = fn(P, *args[c], B, b.stream)
+        if st != 0:
+            raise RuntimeError(f"gdn_spec_commit_index failed with status {st}")
+    for c in range(W):
+        commit(c)
+    ms_commit = time_calls(torch, commit, W, K) / K
+    rec = path_record(ms_commit, 16 * B, int(acc.sum().item()),
+                      "commit by index of accepted lengths ~U{0..7}, B=64 (tokens = accepted; "
+                      "bytes: indices only)")
+    return draft, rec
+
+
 def bench_kda_stack(torch, gdn, synth, K=20, W=3, layers=48):
     """KDA-style decode (per-channel gate), B=64, 32/32 heads, d=128, 48
     layers each with its own 1024-slot pool.  A step: slot preparation in
@@ -269,7 +320,7 @@ def bench_kda_stack(torch, gdn, synth, K=20, W=3, layers=48):
             assert lib.gdn_slot_zero(Lr, Pr[l], fr_p[c], 16, stream) == 0
             assert lib.gdn_slot_copy(Lr, Pr[l], src_p[c], dst_p[c], 16, stream) == 0
         for l in range(layers):
-            assert lib.gdn_decode_step(Lr, Pr[l], idx_p[c], B, 1, base.inref[(c + l) % 4],
+            assert lib.gdn_decode_step(Lr, Pr[l], idx_p[c], None, B, 1, base.inref[(c + l) % 4],
                                        base.out_ptr, None, stream) == 0
     for c in range(W):
         step(c)
@@ -282,8 +333,33 @@ def bench_kda_stack(torch, gdn, synth, K=20, W=3, layers=48):
                                      "per step 16 zeroed + 16 copied slots per layer")
     rec["ms_per_step"] = rec.pop("us_per_call") / 1e3
     rec["prep_bytes"] = int(prep_bytes)
+
+    # the same step with the preparation fused into the decode call: fresh
+    # rows start from zeros (no state or window read), copy-on-write rows read
+    # their checkpoint and write their working slot
+    init_host = np.stack([r[:64] for r in roles]).copy()
+    init_host[:, :16] = -1
+    init_host[:, 16:32] = np.stack([r[64:80] for r in roles])
+    init = dev(init_host)
+    init_p = [ptr(init[c]) for c in range(W + K)]
+
+    def fused(c):
+        for l in range(layers):
+            assert lib.gdn_decode_step(Lr, Pr[l], idx_p[c], init_p[c], B, 1,
+                                       base.inref[(c + l) % 4], base.out_ptr, None, stream) == 0
+    for c in range(W):
+        fused(c)
+    ms_f = time_calls(torch, fused, W, K) / K
+    window = (shape.conv_width - 1) * shape.channels * 2
+    state = shape.n_v_heads * shape.d_v * shape.d_k * 4
+    nbytes_f = layers * (decode_bytes(shape, B) - 16 * (state + window))
+    fused_rec = path_record(ms_f, nbytes_f, B, "KDA decode stack as above with the slot "
+                                               "preparation fused into each decode call (16 "
+                                               "zero starts read nothing, 16 copy-on-write "
+                                               "rows read their checkpoint)")
+    fused_rec["ms_per_step"] = fused_rec.pop("us_per_call") / 1e3
     del pools, convs
-    return rec
+    return rec, fused_rec
 
 
 def prefill_counts(shape, seqlens):
@@ -419,7 +495,8 @@ def main():
         return
     if args.only == "paths":
         for r in (bench_decode_b16(torch, gdn, synth), *bench_spec(torch, gdn, synth),
-                  bench_kda_stack(torch, gdn, synth), bench_prefill(torch, gdn, synth),
+                  *bench_spec_pool(torch, gdn, synth), *bench_kda_stack(torch, gdn, synth),
+                  bench_prefill(torch, gdn, synth),
                   bench_prefill(torch, gdn, synth, shape=synth.KDA)):
             print(json.dumps(r), flush=True)
         return
@@ -455,15 +532,20 @@ def main():
 
     paths = None
     if args.only == "all":
-        log("bench: other paths (B=16 decode, speculative draft + commit, KDA 48-layer stack, "
-            "chunked prefill of both layers)")
+        log("bench: other paths (B=16 decode, speculative draft + commit with snapshots in "
+            "spec buffers and in pool slots, KDA 48-layer stack with separate and fused slot "
+            "preparation, chunked prefill of both layers)")
         d16 = bench_decode_b16(torch, gdn, synth)
         draft, commit = bench_spec(torch, gdn, synth)
-        kda = bench_kda_stack(torch, gdn, synth)
+        pdraft, pcommit = bench_spec_pool(torch, gdn, synth)
+        kda, kda_fused = bench_kda_stack(torch, gdn, synth)
         pf = bench_prefill(torch, gdn, synth)
         pfk = bench_prefill(torch, gdn, synth, shape=synth.KDA)
         paths = {"decode_qwen35_b16": d16, "spec_draft_qwen35_b64_t7": draft,
-                 "spec_commit_qwen35_b64": commit, "kda_stack_b64_48layers": kda,
+                 "spec_commit_qwen35_b64": commit,
+                 "spec_draft_pool_slots_qwen35_b64_t7": pdraft,
+                 "spec_commit_index_b64": pcommit,
+                 "kda_stack_b64_48layers": kda, "kda_stack_b64_48layers_fused_prep": kda_fused,
                  "prefill_qwen35_4x8192": pf, "prefill_kda_4x8192": pfk}
 
     cpu = None

@@ -7,7 +7,7 @@ status.  There is no fallback: if the library is not built, every call fails
 loudly.  Build it with ``python -m hybrid_linear_attention_decode_amd.build``.
 
 Entry points (same names as the C ABI):
-    gdn_decode_step, gdn_spec_decode_commit, gdn_prefill_chunked,
+    gdn_decode_step, gdn_spec_decode_commit, gdn_spec_commit_index, gdn_prefill_chunked,
     gdn_prefill_workspace_size, gdn_slot_copy, gdn_slot_zero, gdn_status_string
 """
 from __future__ import annotations
@@ -30,8 +30,9 @@ GDN_F32, GDN_BF16 = 0, 1
 GDN_GATE_SCALAR, GDN_GATE_CHANNEL = 0, 1
 GDN_F_CONV_SILU, GDN_F_L2NORM_QK = 1, 2
 
-EXPORTED = ("gdn_decode_step", "gdn_spec_decode_commit", "gdn_prefill_chunked",
-            "gdn_prefill_workspace_size", "gdn_slot_copy", "gdn_slot_zero", "gdn_status_string")
+EXPORTED = ("gdn_decode_step", "gdn_spec_decode_commit", "gdn_spec_commit_index",
+            "gdn_prefill_chunked", "gdn_prefill_workspace_size", "gdn_slot_copy",
+            "gdn_slot_zero", "gdn_status_string")
 
 
 class GdnError(RuntimeError):
@@ -52,7 +53,8 @@ class GdnPool(ct.Structure):
 
 
 class GdnSpecCache(ct.Structure):
-    _fields_ = [("ssm", ct.c_void_p), ("conv", ct.c_void_p), ("t_max", ct.c_int32)]
+    _fields_ = [("ssm", ct.c_void_p), ("conv", ct.c_void_p), ("t_max", ct.c_int32),
+                ("slots", ct.c_void_p)]
 
 
 class GdnInputs(ct.Structure):
@@ -76,8 +78,9 @@ def lib() -> ct.CDLL:
         pp = ct.POINTER(GdnPool)
         sp = ct.POINTER(GdnSpecCache)
         ip = ct.POINTER(GdnInputs)
-        L.gdn_decode_step.argtypes = [lp, pp, P, i32, i32, ip, P, sp, P]
+        L.gdn_decode_step.argtypes = [lp, pp, P, P, i32, i32, ip, P, sp, P]
         L.gdn_spec_decode_commit.argtypes = [lp, pp, P, sp, P, i32, P]
+        L.gdn_spec_commit_index.argtypes = [pp, sp, P, P, P, i32, P]
         L.gdn_prefill_chunked.argtypes = [lp, pp, P, P, i32, P, i32, i32, i32, ip, P, P,
                                           ct.c_size_t, P]
         L.gdn_prefill_workspace_size.argtypes = [lp, i32, i32, i32, i32]
@@ -86,8 +89,8 @@ def lib() -> ct.CDLL:
         L.gdn_slot_zero.argtypes = [lp, pp, P, i32, P]
         L.gdn_status_string.argtypes = [ct.c_int]
         L.gdn_status_string.restype = ct.c_char_p
-        for f in ("gdn_decode_step", "gdn_spec_decode_commit", "gdn_prefill_chunked",
-                  "gdn_slot_copy", "gdn_slot_zero"):
+        for f in ("gdn_decode_step", "gdn_spec_decode_commit", "gdn_spec_commit_index",
+                  "gdn_prefill_chunked", "gdn_slot_copy", "gdn_slot_zero"):
             getattr(L, f).restype = ct.c_int
         _lib = L
     return _lib
@@ -155,30 +158,61 @@ def _pool(ssm, conv) -> GdnPool:
     return GdnPool(_ptr(ssm), _ptr(conv), ssm.shape[0])
 
 
-def _spec(spec_ssm, spec_conv):
+def _spec(spec_ssm, spec_conv, spec_slots=None):
+    if spec_slots is not None:
+        return ct.byref(GdnSpecCache(None, None, spec_slots.shape[1], _ptr(spec_slots)))
     if spec_ssm is None:
         return None
-    return ct.byref(GdnSpecCache(_ptr(spec_ssm), _ptr(spec_conv), spec_ssm.shape[1]))
+    return ct.byref(GdnSpecCache(_ptr(spec_ssm), _ptr(spec_conv), spec_ssm.shape[1], None))
+
+
+def _i32(t, n, what):
+    import torch
+    if t is not None and (t.dtype != torch.int32 or t.numel() != n):
+        raise ValueError(f"{what} must be int32 [{n}]")
 
 
 def gdn_decode_step(layer: Layer, ssm, conv, mamba_pool_indices, x, alpha, beta, conv_w,
-                    conv_b=None, out=None, spec_ssm=None, spec_conv=None, stream=None):
-    """x [B, T, C]; returns out [B, T, H_v, d_v] fp32.  See include/gdn.h."""
+                    conv_b=None, out=None, spec_ssm=None, spec_conv=None, init_slot=None,
+                    spec_slots=None, stream=None):
+    """x [B, T, C]; returns out [B, T, H_v, d_v] fp32.  init_slot [B] int32:
+    fused slot preparation (-1 zero start, s copy-on-write source); spec_slots
+    [B, t_max] int32: snapshots into pool slots.  See include/gdn.h."""
     import torch
-    _dev(ssm, conv, mamba_pool_indices, x, alpha, beta, conv_w, conv_b, out, spec_ssm, spec_conv)
+    _dev(ssm, conv, mamba_pool_indices, x, alpha, beta, conv_w, conv_b, out, spec_ssm, spec_conv,
+         init_slot, spec_slots)
     B, T = x.shape[0], x.shape[1]
-    if mamba_pool_indices.dtype != torch.int32 or mamba_pool_indices.numel() != B:
-        raise ValueError("mamba_pool_indices must be int32 [B]")
+    _i32(mamba_pool_indices, B, "mamba_pool_indices")
+    _i32(init_slot, B, "init_slot")
+    if spec_slots is not None and (spec_slots.dtype != torch.int32 or spec_slots.dim() != 2
+                                   or spec_slots.shape[0] != B):
+        raise ValueError("spec_slots must be int32 [B, t_max]")
     if out is None:
         out = torch.empty((B, T, layer.n_v_heads, layer.d_v), dtype=torch.float32, device=x.device)
     L = layer.c_struct()
     P = _pool(ssm, conv)
     inp = GdnInputs(_ptr(x), _ptr(alpha), _ptr(beta), _ptr(conv_w), _ptr(conv_b))
-    st = lib().gdn_decode_step(ct.byref(L), ct.byref(P), _ptr(mamba_pool_indices), B, T,
-                               ct.byref(inp), _ptr(out), _spec(spec_ssm, spec_conv),
-                               _stream(stream))
+    st = lib().gdn_decode_step(ct.byref(L), ct.byref(P), _ptr(mamba_pool_indices),
+                               _ptr(init_slot), B, T, ct.byref(inp), _ptr(out),
+                               _spec(spec_ssm, spec_conv, spec_slots), _stream(stream))
     _check(st, "gdn_decode_step")
     return out
+
+
+def gdn_spec_commit_index(ssm, conv, spec_slots, accepted_len, mamba_pool_indices,
+                          released=None, stream=None):
+    """Commit by index: mamba_pool_indices[b] <- spec_slots[b, L-1] for L =
+    accepted_len[b] >= 1; released [B] int32 gets each request's previous slot
+    (-1 where unchanged).  See include/gdn.h."""
+    _dev(ssm, conv, spec_slots, accepted_len, mamba_pool_indices, released)
+    B = mamba_pool_indices.numel()
+    _i32(accepted_len, B, "accepted_len")
+    _i32(released, B, "released")
+    P = _pool(ssm, conv)
+    st = lib().gdn_spec_commit_index(ct.byref(P), _spec(None, None, spec_slots),
+                                     _ptr(accepted_len), _ptr(mamba_pool_indices),
+                                     _ptr(released), B, _stream(stream))
+    _check(st, "gdn_spec_commit_index")
 
 
 def gdn_spec_decode_commit(layer: Layer, ssm, conv, mamba_pool_indices, spec_ssm, spec_conv,

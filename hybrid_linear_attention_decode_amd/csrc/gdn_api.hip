@@ -45,9 +45,10 @@ gdn_status check_pool(const gdn_layer* L, const gdn_pool* P) {
 }
 
 gdn_status check_spec(const gdn_layer* L, const gdn_spec_cache* S) {
+  if (S->t_max < 1) return GDN_ERR_BAD_SHAPE;
+  if (S->slots) return GDN_OK;  // snapshots in pool slots
   if (!S->ssm) return GDN_ERR_NULL_ARG;
   if (L->conv_width > 1 && !S->conv) return GDN_ERR_NULL_ARG;
-  if (S->t_max < 1) return GDN_ERR_BAD_SHAPE;
   if (!aligned16(S->ssm) || (S->conv && !aligned16(S->conv))) return GDN_ERR_BAD_SHAPE;
   return GDN_OK;
 }
@@ -83,9 +84,9 @@ const char* gdn_status_string(gdn_status s) {
   return "unknown status";
 }
 
-gdn_status gdn_decode_step(const gdn_layer* L, const gdn_pool* P, const int32_t* idx, int32_t B,
-                           int32_t T, const gdn_inputs* in, float* out,
-                           const gdn_spec_cache* spec, void* stream) {
+gdn_status gdn_decode_step(const gdn_layer* L, const gdn_pool* P, const int32_t* idx,
+                           const int32_t* init_slot, int32_t B, int32_t T, const gdn_inputs* in,
+                           float* out, const gdn_spec_cache* spec, void* stream) {
   gdn_status st = check_layer(L);
   if (st != GDN_OK) return st;
   if ((st = check_pool(L, P)) != GDN_OK) return st;
@@ -120,14 +121,16 @@ gdn_status gdn_decode_step(const gdn_layer* L, const gdn_pool* P, const int32_t*
   a.ssm = P->ssm;
   a.conv = P->conv;
   a.idx = idx;
+  a.init = init_slot;
   a.x = in->x;
   a.alpha = in->alpha;
   a.beta = in->beta;
   a.w = in->conv_w;
   a.bias = in->conv_b;
   a.out = out;
-  a.spec_ssm = spec ? spec->ssm : nullptr;
-  a.spec_conv = spec ? spec->conv : nullptr;
+  a.spec_slots = spec ? spec->slots : nullptr;
+  a.spec_ssm = spec && !spec->slots ? spec->ssm : nullptr;
+  a.spec_conv = spec && !spec->slots ? spec->conv : nullptr;
   a.t_max = spec ? spec->t_max : 0;
   return from_hip(gdn::launch_decode(a, L->d_k, L->act_dtype == GDN_BF16,
                                      L->gate == GDN_GATE_CHANNEL,
@@ -142,6 +145,7 @@ gdn_status gdn_spec_decode_commit(const gdn_layer* L, const gdn_pool* P, const i
   if ((st = check_pool(L, P)) != GDN_OK) return st;
   if (!spec || !idx || !accepted_len) return GDN_ERR_NULL_ARG;
   if ((st = check_spec(L, spec)) != GDN_OK) return st;
+  if (spec->slots) return GDN_ERR_BAD_SHAPE;  // pool-slot snapshots commit by index
   if (B < 0 || B > 65535) return GDN_ERR_BAD_SHAPE;
   SlotArgs a = slot_args(L, P, B);
   a.a = idx;
@@ -150,6 +154,23 @@ gdn_status gdn_spec_decode_commit(const gdn_layer* L, const gdn_pool* P, const i
   a.spec_conv = spec->conv;
   a.t_max = spec->t_max;
   return from_hip(gdn::launch_slots(a, gdn::kSlotCommit, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_spec_commit_index(const gdn_pool* P, const gdn_spec_cache* spec,
+                                 const int32_t* accepted_len, int32_t* idx, int32_t* released,
+                                 int32_t B, void* stream) {
+  if (!P || !spec || !accepted_len || !idx) return GDN_ERR_NULL_ARG;
+  if (!spec->slots) return GDN_ERR_NULL_ARG;
+  if (spec->t_max < 1 || B < 0 || B > 65535 || P->num_slots < 1) return GDN_ERR_BAD_SHAPE;
+  gdn::CommitIndexArgs a{};
+  a.B = B;
+  a.t_max = spec->t_max;
+  a.num_slots = P->num_slots;
+  a.spec_slots = spec->slots;
+  a.accepted_len = accepted_len;
+  a.idx = idx;
+  a.released = released;
+  return from_hip(gdn::launch_commit_index(a, static_cast<hipStream_t>(stream)));
 }
 
 gdn_status gdn_slot_copy(const gdn_layer* L, const gdn_pool* P, const int32_t* src,

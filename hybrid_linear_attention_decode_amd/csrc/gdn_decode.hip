@@ -62,7 +62,8 @@ struct RowMap {
 
 // LDS plan of a workgroup, in dwords: per-wave state stages | two raw-input
 // buffers (the next unit's copies land while this unit reads its own) | one
-// activation buffer | slot table of the workgroup's units.
+// activation buffer | slot table of the workgroup's units (destination and
+// source slot of each).
 struct LdsPlan {
   int stage_per_wave, raw_len, act_len;
   int raw, act, slots, total;
@@ -78,7 +79,7 @@ __host__ __device__ inline LdsPlan lds_plan(int dk, int rpw, int waves, int Cg, 
   p.raw = waves * p.stage_per_wave;
   p.act = p.raw + 2 * p.raw_len;
   p.slots = p.act + p.act_len;
-  p.total = p.slots + units;
+  p.total = p.slots + 2 * units;
   return p;
 }
 
@@ -94,7 +95,8 @@ struct DecodeCta {
   int tid, lane, wave, nwaves, NT, lr, lc;
   int dv, G, R, Cg, GA, W, W1, lead, C, T, TC, Hv, Hk, per_tok;
   int kh, b0, m;  // this workgroup's key head, first request, request stride
-  bool spec;
+  bool spec;        // snapshots per token instead of an in-place update
+  bool spec_pool;   // ... into pool slots named by a.spec_slots
   int64_t slot_elems;
   uint32_t lane_off;  // this lane's first state element within a unit
   uint32_t chan;      // global conv channel of this thread (tid < Cg)
@@ -128,7 +130,8 @@ struct DecodeCta {
     kh = static_cast<int>(blockIdx.x) % Hk;
     b0 = static_cast<int>(blockIdx.x) / Hk;
     m = static_cast<int>(gridDim.x) / Hk;
-    spec = a.spec_ssm != nullptr;
+    spec_pool = a.spec_slots != nullptr;
+    spec = spec_pool || a.spec_ssm != nullptr;
     slot_elems = static_cast<int64_t>(Hv) * dv * DK;
     lane_off = static_cast<uint32_t>(wave * RPW + lr * NR) * DK + 4 * lc;
     chan = channel(tid < Cg ? tid : 0);
@@ -165,22 +168,26 @@ struct DecodeCta {
       return __uint_as_float(d);
   }
 
-  // Issue the copies of unit (b, slot) into LDS: this wave's state rows into
-  // its stage -- instruction (p, n) as 64 lanes x 16 B at stage + (p*CPL +
-  // n)*256, lane i's bytes at 16*i, exactly what a register load would give
-  // -- and, shared by the waves, the raw first-token inputs into raw:
-  //   [x: Cg][window: W1 x Cg][gates: GA][betas: G], one dword per element.
+  // Issue the copies of unit (b, source slot) into LDS: this wave's state
+  // rows into its stage -- instruction (p, n) as 64 lanes x 16 B at stage +
+  // (p*CPL + n)*256, lane i's bytes at 16*i, exactly what a register load
+  // would give -- and, shared by the waves, the raw first-token inputs into
+  // raw: [x: Cg][window: W1 x Cg][gates: GA][betas: G], one dword per element.
+  // A negative source (a fresh start) copies no state and zeroes the window.
   __device__ __forceinline__ void copy_unit(int b, int32_t slot, float* stage,
                                             uint32_t* raw) const {
-    const float* src = state(a.ssm, slot) + lane_off;
+    if (slot >= 0) {
+      const float* src = state(a.ssm, slot) + lane_off;
 #pragma unroll
-    for (int p = 0; p < NR; ++p)
+      for (int p = 0; p < NR; ++p)
 #pragma unroll
-      for (int n = 0; n < CPL; ++n)
-        lds_dma16(src + p * DK + 4 * n * LPR, stage + (p * CPL + n) * 256);
+        for (int n = 0; n < CPL; ++n)
+          lds_dma16(src + p * DK + 4 * n * LPR, stage + (p * CPL + n) * 256);
+    }
 
     const Act* x0 = static_cast<const Act*>(a.x) + static_cast<int64_t>(b) * T * C;
-    const Act* cs = static_cast<const Act*>(a.conv) + static_cast<int64_t>(slot) * W1 * C;
+    const Act* cs =
+        static_cast<const Act*>(a.conv) + static_cast<int64_t>(slot >= 0 ? slot : 0) * W1 * C;
     const int64_t th = static_cast<int64_t>(b) * T * Hv + static_cast<int64_t>(kh) * G;
     const Act* al = static_cast<const Act*>(a.alpha) + th * DKA;
     const Act* be = static_cast<const Act*>(a.beta) + th;
@@ -195,7 +202,10 @@ struct DecodeCta {
           if (q == i) off = roff[q];
         if (i >= kRawIt) off = raw_offset(d);
         const Act* base = d < Cg ? x0 : d < nx ? cs : d < nx + GA ? al : be;
-        lds_dma<sizeof(Act)>(base + off, raw + j * 64);
+        if (slot < 0 && d >= Cg && d < nx)
+          raw[j * 64 + lane] = 0u;
+        else
+          lds_dma<sizeof(Act)>(base + off, raw + j * 64);
       }
     }
   }
@@ -208,13 +218,35 @@ struct DecodeCta {
         s[p][n] = *reinterpret_cast<const f4*>(stage + (p * CPL + n) * 256 + 4 * lane);
   }
 
+  // Where token t's snapshot goes (null: nowhere): a row of the spec cache,
+  // or the pool slot the spec slot table names for it (skipped when outside
+  // the pool).
+  __device__ __forceinline__ int32_t spec_slot(int b, int t) const {
+    const int32_t sl = a.spec_slots[static_cast<int64_t>(b) * a.t_max + t];
+    return (sl < 0 || static_cast<int64_t>(sl) >= a.num_slots) ? -1 : sl;
+  }
+  __device__ __forceinline__ Act* snap_conv(int b, int t) const {
+    if (spec_pool) {
+      const int32_t sl = spec_slot(b, t);
+      return sl < 0 ? nullptr : static_cast<Act*>(a.conv) + static_cast<int64_t>(sl) * W1 * C;
+    }
+    return static_cast<Act*>(a.spec_conv) + (static_cast<int64_t>(b) * a.t_max + t) * W1 * C;
+  }
+  __device__ __forceinline__ float* snap_ssm(int b, int t) const {
+    if (spec_pool) {
+      const int32_t sl = spec_slot(b, t);
+      return sl < 0 ? nullptr : state(a.ssm, sl);
+    }
+    return state(a.spec_ssm, static_cast<int64_t>(b) * a.t_max + t);
+  }
+
   // D1 for one token t of this thread's channel: conv over the window and
   // x, window shift, SiLU; the activation goes to act[tid]; the shifted
   // window goes to the snapshot of token t (spec) or, after the last token,
   // back to the slot.
-  __device__ __forceinline__ void conv_token(int t, float xv, const float (&wt)[kMaxW1 + 1],
+  __device__ __forceinline__ void conv_token(int b, int t, float xv, const float (&wt)[kMaxW1 + 1],
                                              float (&win)[kMaxW1], float bias, float* act,
-                                             Act* conv_slot, Act* spec_conv_req) const {
+                                             Act* conv_slot) const {
     float y = bias;
 #pragma unroll
     for (int j = 0; j < kMaxW1; ++j) y = fmaf(wt[j], win[j], y);
@@ -226,7 +258,7 @@ struct DecodeCta {
     act[tid] = y;
     Act* wdst = nullptr;
     if (spec)
-      wdst = spec_conv_req + static_cast<uint32_t>(t) * W1 * C;
+      wdst = snap_conv(b, t);
     else if (t == T - 1)
       wdst = conv_slot;
     if (wdst) {
@@ -244,9 +276,6 @@ struct DecodeCta {
     const int64_t tok0 = static_cast<int64_t>(b) * T;
     const Act* const x_req = static_cast<const Act*>(a.x) + tok0 * C;
     Act* const conv_slot = static_cast<Act*>(a.conv) + static_cast<int64_t>(slot) * W1 * C;
-    Act* const spec_conv_req =
-        spec ? static_cast<Act*>(a.spec_conv) + static_cast<int64_t>(b) * a.t_max * W1 * C
-             : nullptr;
     const Act* const al_req =
         static_cast<const Act*>(a.alpha) + (tok0 * Hv + static_cast<int64_t>(kh) * G) * DKA;
     const Act* const be_req =
@@ -269,7 +298,7 @@ struct DecodeCta {
       const int first = t0 == 0 ? 1 : 0;
       if (first) {
         if (tid < Cg)
-          conv_token(0, raw_f32(raw[tid]), wt, win, bias, act, conv_slot, spec_conv_req);
+          conv_token(b, 0, raw_f32(raw[tid]), wt, win, bias, act, conv_slot);
         if (tid < GA + G) act[Cg + tid] = raw_f32(raw[nx + tid]);
       }
       // later tokens of the chunk from global memory
@@ -284,8 +313,7 @@ struct DecodeCta {
 #pragma unroll
           for (int k = 0; k < kBatch; ++k) {
             if (tb + k >= nt) break;
-            conv_token(t0 + tb + k, xr[k], wt, win, bias, act + (tb + k) * per_tok, conv_slot,
-                       spec_conv_req);
+            conv_token(b, t0 + tb + k, xr[k], wt, win, bias, act + (tb + k) * per_tok, conv_slot);
           }
         }
       }
@@ -387,11 +415,14 @@ struct DecodeCta {
           if (lc == 0) out_req[static_cast<uint32_t>(t) * Hv * dv + hl * dv + i] = o;
         }
         if (spec) {
-          float* dst = state(a.spec_ssm, static_cast<int64_t>(b) * a.t_max + t) + lane_off;
+          float* dst = snap_ssm(b, t);
+          if (dst) {
+            dst += lane_off;
 #pragma unroll
-          for (int p = 0; p < NR; ++p)
+            for (int p = 0; p < NR; ++p)
 #pragma unroll
-            for (int n = 0; n < CPL; ++n) st_stream(dst + p * DK + 4 * n * LPR, s[p][n]);
+              for (int n = 0; n < CPL; ++n) st_stream(dst + p * DK + 4 * n * LPR, s[p][n]);
+          }
         }
       }
       if (t0 + TC < T) lds_barrier();  // the next chunk rewrites this buffer
@@ -425,11 +456,19 @@ __global__ void __launch_bounds__(512, RPW <= 16 ? 4 : 2) decode_kernel(const De
   const int mine = (a.B - cta.b0 + cta.m - 1) / cta.m;
   if (mine <= 0) return;
 
-  // Once per workgroup: the slots of its units (an index outside the pool
-  // marks a unit as skipped) and the conv taps and bias of its channels.
+  // Once per workgroup: the slots of its units -- destination (an index
+  // outside the pool marks a unit as skipped) and source (the destination
+  // itself, a copy-on-write source, or negative for a zero start; a source
+  // past the pool skips the unit) -- and the conv taps and bias of its
+  // channels.
   for (int k = cta.tid; k < mine; k += cta.NT) {
-    const int32_t sl = a.idx[cta.b0 + k * cta.m];
-    slot_tab[k] = (sl < 0 || static_cast<int64_t>(sl) >= a.num_slots) ? -1 : sl;
+    const int bk = cta.b0 + k * cta.m;
+    int32_t sl = a.idx[bk];
+    int32_t sr = a.init ? a.init[bk] : sl;
+    if (sl < 0 || static_cast<int64_t>(sl) >= a.num_slots || static_cast<int64_t>(sr) >= a.num_slots)
+      sl = -1;
+    slot_tab[2 * k] = sl;
+    slot_tab[2 * k + 1] = sr < 0 ? -1 : sr;
   }
   float wt[kMaxW1 + 1];
   float bias = 0.f;
@@ -445,8 +484,8 @@ __global__ void __launch_bounds__(512, RPW <= 16 ? 4 : 2) decode_kernel(const De
   }
   lds_barrier();
 
-  int32_t sl = uniform(slot_tab[0]);
-  if (sl >= 0) cta.copy_unit(cta.b0, sl, stage, raw0);
+  int32_t sl = uniform(slot_tab[0]), sr = uniform(slot_tab[1]);
+  if (sl >= 0) cta.copy_unit(cta.b0, sr, stage, raw0);
   f4 s[Cta::NR][Cta::CPL];
   for (int k = 0; k < mine; ++k) {
     const int b = cta.b0 + k * cta.m;
@@ -457,14 +496,26 @@ __global__ void __launch_bounds__(512, RPW <= 16 ? 4 : 2) decode_kernel(const De
     // drain: this unit's copies (and the previous unit's stores) are done
     vm_wait<0>();
     if (sl >= 0) {
-      cta.stage_read(stage, s);
-      lgkm_wait();  // the stage is read before the next copy overwrites it
+      if (sr >= 0) {
+        cta.stage_read(stage, s);
+        lgkm_wait();  // the stage is read before the next copy overwrites it
+      } else {
+#pragma unroll
+        for (int p = 0; p < Cta::NR; ++p)
+#pragma unroll
+          for (int n = 0; n < Cta::CPL; ++n) s[p][n] = f4{0.f, 0.f, 0.f, 0.f};
+      }
     }
     lds_barrier();  // every wave's copies of the shared raw inputs have landed
-    const int32_t sn = k + 1 < mine ? uniform(slot_tab[k + 1]) : -1;
-    if (sn >= 0) cta.copy_unit(b + cta.m, sn, stage, raw0 + ((k + 1) & 1) * P.raw_len);
+    int32_t sn = -1, srn = -1;
+    if (k + 1 < mine) {
+      sn = uniform(slot_tab[2 * (k + 1)]);
+      srn = uniform(slot_tab[2 * (k + 1) + 1]);
+    }
+    if (sn >= 0) cta.copy_unit(b + cta.m, srn, stage, raw0 + ((k + 1) & 1) * P.raw_len);
     if (sl >= 0) cta.run(b, sl, s, wt, bias, raw, act);
     sl = sn;
+    sr = srn;
   }
 }
 

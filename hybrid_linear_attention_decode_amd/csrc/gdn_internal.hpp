@@ -19,6 +19,7 @@ struct DecodeArgs {
   float* ssm;                // [slots][Hv][dv][dk]
   void* conv;                // [slots][W-1][C]
   const int32_t* idx;        // [B]
+  const int32_t* init;       // [B] or nullptr (= idx): source slot, < 0 = zero start
   const void* x;             // [B*T][C]
   const void* alpha;         // [B*T][Hv] or [B*T][Hv][dk]
   const void* beta;          // [B*T][Hv]
@@ -27,6 +28,7 @@ struct DecodeArgs {
   float* out;                // [B*T][Hv][dv]
   float* spec_ssm;           // [B][t_max][Hv][dv][dk] or nullptr
   void* spec_conv;           // [B][t_max][W-1][C]
+  const int32_t* spec_slots; // [B][t_max] pool slots taking the snapshots, or nullptr
   int32_t t_max;
 };
 
@@ -46,6 +48,16 @@ struct SlotArgs {
 };
 
 enum SlotMode { kSlotCopy = 0, kSlotZero = 1, kSlotCommit = 2 };
+
+// Commit by index (snapshots in pool slots).
+struct CommitIndexArgs {
+  int32_t B, t_max;
+  int64_t num_slots;
+  const int32_t* spec_slots;    // [B][t_max]
+  const int32_t* accepted_len;  // [B]
+  int32_t* idx;                 // [B] mamba_pool_indices, updated
+  int32_t* released;            // [B] or nullptr
+};
 
 // One chunked prefill call over N sequences.
 struct PrefillArgs {
@@ -74,6 +86,7 @@ struct PrefillArgs {
 // every host-checkable argument.
 hipError_t launch_decode(const DecodeArgs& a, int dk, int act_bf16, int kda, hipStream_t s);
 hipError_t launch_slots(const SlotArgs& a, SlotMode mode, hipStream_t s);
+hipError_t launch_commit_index(const CommitIndexArgs& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int dk, int act_bf16, hipStream_t s);
 hipError_t launch_prefill_kda(const PrefillArgs& a, int dk, int act_bf16, int max_seqlen,
                               hipStream_t s);

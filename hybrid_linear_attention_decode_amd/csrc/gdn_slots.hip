@@ -2,7 +2,8 @@
 // (dst <- src), explicit zeroing, and the speculative commit (slot <- the
 // snapshot of the last accepted draft token).  All are bitwise 16-byte
 // streaming copies; one workgroup moves a contiguous 16 KiB piece of one
-// item's ssm slot followed by its conv slot.
+// item's ssm slot followed by its conv slot.  When the snapshots themselves
+// live in pool slots, the commit is an index update (commit_index_kernel).
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
@@ -74,7 +75,31 @@ __global__ void __launch_bounds__(kThreads) slot_kernel(const SlotArgs a) {
   }
 }
 
+// Commit by index: request b's working slot becomes the pool slot holding
+// the snapshot of its last accepted draft token; nothing is copied.
+__global__ void __launch_bounds__(kThreads) commit_index_kernel(const CommitIndexArgs a) {
+  const int b = blockIdx.x * kThreads + threadIdx.x;
+  if (b >= a.B) return;
+  const int32_t L = a.accepted_len[b];
+  int32_t out = -1;
+  if (L >= 1 && L <= a.t_max) {
+    const int32_t ns = a.spec_slots[static_cast<int64_t>(b) * a.t_max + (L - 1)];
+    if (ns >= 0 && ns < a.num_slots) {
+      out = a.idx[b];
+      a.idx[b] = ns;
+    }
+  }
+  if (a.released) a.released[b] = out;
+}
+
 }  // namespace
+
+hipError_t launch_commit_index(const CommitIndexArgs& a, hipStream_t s) {
+  if (a.B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(commit_index_kernel, dim3((a.B + kThreads - 1) / kThreads), dim3(kThreads),
+                     0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_slots(const SlotArgs& a, SlotMode mode, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;

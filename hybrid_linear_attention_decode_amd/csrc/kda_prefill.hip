@@ -70,7 +70,7 @@ struct DiagPlan {
 };
 
 template <int DK, typename Act>
-__global__ void __launch_bounds__(64, 4) kda_diag_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(64) kda_diag_kernel(PrefillArgs a) {
   using DP = DiagPlan<DK>;
   constexpr int kGrp = DK / 8;       // channel octets per head
   constexpr int kTpl = kGrp / 2;     // tokens per lane in the conv stage

@@ -110,11 +110,18 @@ typedef struct {
   int64_t num_slots;
 } gdn_pool;
 
-/* (host) struct of device pointers: per-draft-token snapshots */
+/* (host) struct of device pointers: per-draft-token snapshots, either in
+ * their own buffers (ssm [B][t_max][H_v][d_v][d_k], conv [B][t_max][W-1][C])
+ * or, when slots != NULL, in pool slots: slots [B][t_max] int32 names the
+ * pool slot (both pools) that receives the snapshot of request b after draft
+ * token t (ssm and conv are then ignored; an entry outside the pool drops
+ * that snapshot).  Snapshot slots must be distinct and must not be any
+ * request's working or source slot. */
 typedef struct {
   float* ssm;
   void* conv;
   int32_t t_max;
+  const int32_t* slots;
 } gdn_spec_cache;
 
 /* (host) struct of device pointers: per-token inputs */
@@ -131,15 +138,22 @@ typedef struct {
  * named by mamba_pool_indices is updated in place every decode step; with a
  * spec cache, per-speculative-step Conv/SSM snapshots are kept for rollback).
  *   mamba_pool_indices [B] int32 (device); B >= 0; 1 <= T.
+ *   init_slot [B] int32 (device) or NULL -- slot preparation fused into the
+ *     step ("Riesgo de correctitud": a fresh working slot must start clean):
+ *     NULL or init_slot[b] == mamba_pool_indices[b]: start from the slot
+ *     itself; init_slot[b] < 0: start from zero state and zero conv window
+ *     (nothing read); any other s: copy-on-write, start from slot s (only
+ *     read) and write the working slot.  s >= num_slots skips the row.
  *   out [B][T][H_v][d_v] fp32: o_t for every token.
- *   spec == NULL: conv and ssm of each slot are updated in place after T tokens.
+ *   spec == NULL: conv and ssm of each working slot are written after T tokens.
  *   spec != NULL: T <= spec->t_max; the state after token t (0-based) goes to
- *     spec->ssm[b][t] and spec->conv[b][t]; the pool is only read.
+ *     snapshot t of request b (see gdn_spec_cache); working slots are not
+ *     written.
  */
 gdn_status gdn_decode_step(const gdn_layer* layer, const gdn_pool* pool,
-                           const int32_t* mamba_pool_indices, int32_t B, int32_t T,
-                           const gdn_inputs* in, float* out, const gdn_spec_cache* spec,
-                           void* stream);
+                           const int32_t* mamba_pool_indices, const int32_t* init_slot,
+                           int32_t B, int32_t T, const gdn_inputs* in, float* out,
+                           const gdn_spec_cache* spec, void* stream);
 
 /*
  * Rollback / commit after verification ("Scheduler dual": rollback from the
@@ -147,6 +161,7 @@ gdn_status gdn_decode_step(const gdn_layer* layer, const gdn_pool* pool,
  * L > 0 copies snapshot L-1 (ssm and conv) into slot mamba_pool_indices[b];
  * L == 0 leaves the slot as it was before the draft.  Bitwise copy.
  *   accepted_len [B] int32 (device), each in [0, spec->t_max].
+ *   spec->slots must be NULL (snapshots in pool slots commit by index).
  */
 gdn_status gdn_spec_decode_commit(const gdn_layer* layer, const gdn_pool* pool,
                                   const int32_t* mamba_pool_indices,
@@ -189,6 +204,20 @@ gdn_status gdn_prefill_chunked(const gdn_layer* layer, const gdn_pool* pool,
  * 4 * min(N, total)).  0 on bad arguments. */
 size_t gdn_prefill_workspace_size(const gdn_layer* layer, int32_t N, int32_t max_seqlen,
                                   int32_t total_tokens, int32_t chunk);
+
+/*
+ * Commit by index, for snapshots kept in pool slots (talk page, section
+ * "Kernel：让 MLA 真正跑满 GPU", on linear models: at a cut-off an index moves,
+ * not the state block): for each b with L =
+ * accepted_len[b] in [1, t_max] and s = spec->slots[b][L-1] inside the pool,
+ * mamba_pool_indices[b] <- s; nothing is copied.  released [B] (device) or
+ * NULL receives the slot each request no longer references (its previous
+ * working slot), or -1 where nothing changed; the caller returns released
+ * and rejected snapshot slots to its free list.
+ */
+gdn_status gdn_spec_commit_index(const gdn_pool* pool, const gdn_spec_cache* spec,
+                                 const int32_t* accepted_len, int32_t* mamba_pool_indices,
+                                 int32_t* released, int32_t B, void* stream);
 
 /*
  * Copy-on-write of n slots ("Riesgo de correctitud": a fresh working slot is

@@ -45,8 +45,8 @@ def qwen_layer(**kw):
 def decode(L, pool=None, idx=FAKE, B=4, T=1, inp=None, out=FAKE, spec=None):
     pool = pool or GdnPool(FAKE, FAKE, 8)
     inp = inp or GdnInputs(FAKE, FAKE, FAKE, FAKE, None)
-    return gdn.lib().gdn_decode_step(ct.byref(L), ct.byref(pool), idx, B, T, ct.byref(inp),
-                                     out, spec, None)
+    return gdn.lib().gdn_decode_step(ct.byref(L), ct.byref(pool), idx, None, B, T,
+                                     ct.byref(inp), out, spec, None)
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -69,7 +69,7 @@ def test_bad_layer(field, value, status):
 
 def test_bad_decode_arguments():
     L = qwen_layer()
-    assert gdn.lib().gdn_decode_step(None, None, FAKE, 1, 1, None, FAKE, None, None) == \
+    assert gdn.lib().gdn_decode_step(None, None, FAKE, None, 1, 1, None, FAKE, None, None) == \
         gdn.GDN_ERR_NULL_ARG
     assert decode(L, pool=GdnPool(None, FAKE, 8)) == gdn.GDN_ERR_NULL_ARG
     assert decode(L, pool=GdnPool(FAKE, None, 8)) == gdn.GDN_ERR_NULL_ARG
@@ -84,9 +84,36 @@ def test_bad_decode_arguments():
     assert decode(L, T=4, spec=ct.byref(spec)) == gdn.GDN_ERR_BAD_SHAPE   # T > t_max
     spec0 = GdnSpecCache(None, FAKE, 7)
     assert decode(L, T=4, spec=ct.byref(spec0)) == gdn.GDN_ERR_NULL_ARG
+    # snapshots in pool slots need no spec buffers, but t_max still bounds T
+    pooled = GdnSpecCache(None, None, 3, FAKE)
+    assert decode(L, T=4, spec=ct.byref(pooled)) == gdn.GDN_ERR_BAD_SHAPE
+    assert decode(L, T=2, spec=ct.byref(pooled), B=0) == gdn.GDN_OK
     # a conv-less layer (W = 1) needs no conv pool; B = 0 enqueues nothing
     L1 = qwen_layer(conv_width=1)
     assert decode(L1, pool=GdnPool(FAKE, None, 8), B=0) == gdn.GDN_OK
+
+
+def test_bad_commit_index_arguments():
+    pool = GdnPool(FAKE, FAKE, 8)
+    lib = gdn.lib()
+    pooled = GdnSpecCache(None, None, 7, FAKE)
+    assert lib.gdn_spec_commit_index(ct.byref(pool), ct.byref(pooled), None, FAKE, None, 4,
+                                     None) == gdn.GDN_ERR_NULL_ARG
+    assert lib.gdn_spec_commit_index(ct.byref(pool), ct.byref(pooled), FAKE, None, None, 4,
+                                     None) == gdn.GDN_ERR_NULL_ARG
+    buffers = GdnSpecCache(FAKE, FAKE, 7, None)     # snapshots not in pool slots
+    assert lib.gdn_spec_commit_index(ct.byref(pool), ct.byref(buffers), FAKE, FAKE, None, 4,
+                                     None) == gdn.GDN_ERR_NULL_ARG
+    assert lib.gdn_spec_commit_index(ct.byref(pool), ct.byref(GdnSpecCache(None, None, 0, FAKE)),
+                                     FAKE, FAKE, None, 4, None) == gdn.GDN_ERR_BAD_SHAPE
+    assert lib.gdn_spec_commit_index(ct.byref(pool), ct.byref(pooled), FAKE, FAKE, None, -1,
+                                     None) == gdn.GDN_ERR_BAD_SHAPE
+    assert lib.gdn_spec_commit_index(ct.byref(pool), ct.byref(pooled), FAKE, FAKE, None, 0,
+                                     None) == gdn.GDN_OK
+    # the copy commit refuses snapshots kept in pool slots
+    L = qwen_layer()
+    assert lib.gdn_spec_decode_commit(ct.byref(L), ct.byref(pool), FAKE, ct.byref(pooled), FAKE,
+                                      4, None) == gdn.GDN_ERR_BAD_SHAPE
 
 
 def test_bad_slot_and_commit_arguments():
