@@ -284,6 +284,37 @@ def bench_spec_pool(torch, gdn, synth, K=100, W=10):
     return draft, rec
 
 
+def bench_slot_pack(torch, gdn, synth, K=50, W=5, n=64):
+    """Pack 64 working slots of the Qwen3.5 layer into a contiguous buffer and
+    unpack them into 64 other slots (the local half of moving state between
+    engines); bytes = 2 x 64 packed items each way."""
+    shape = synth.QWEN35
+    b = DecodeBench(torch, gdn, synth, shape, n, 1024, 1, seed=6, n_inputs=1)
+    g = b.g
+    src = torch.arange(0, 2 * n, 2, dtype=torch.int32, device="cuda")
+    dst = torch.arange(1, 2 * n, 2, dtype=torch.int32, device="cuda")
+    item = gdn.gdn_slot_bytes(g)
+    buf = torch.empty(n * item, dtype=torch.uint8, device="cuda")
+    lib = gdn.lib()
+    ptr = lambda t: ct.c_void_p(t.data_ptr())
+
+    def pack(_c):
+        assert lib.gdn_slot_pack(b.Lref, b.Pref, ptr(src), n, ptr(buf), n * item, b.stream) == 0
+
+    def unpack(_c):
+        assert lib.gdn_slot_unpack(b.Lref, b.Pref, ptr(buf), n * item, ptr(dst), n,
+                                   b.stream) == 0
+    out = []
+    for fn, what in ((pack, "pack"), (unpack, "unpack")):
+        for c in range(W):
+            fn(c)
+        ms = time_calls(torch, fn, W, K) / K
+        rec = path_record(ms, 2 * n * item, n, f"slot {what}: 64 Qwen3.5 working slots "
+                                               f"({item} B each) <-> contiguous buffer")
+        out.append(rec)
+    return out
+
+
 def bench_kda_stack(torch, gdn, synth, K=20, W=3, layers=48):
     """KDA-style decode (per-channel gate), B=64, 32/32 heads, d=128, 48
     layers each with its own 1024-slot pool.  A step: slot preparation in
@@ -496,6 +527,7 @@ def main():
     if args.only == "paths":
         for r in (bench_decode_b16(torch, gdn, synth), *bench_spec(torch, gdn, synth),
                   *bench_spec_pool(torch, gdn, synth), *bench_kda_stack(torch, gdn, synth),
+                  *bench_slot_pack(torch, gdn, synth),
                   bench_prefill(torch, gdn, synth),
                   bench_prefill(torch, gdn, synth, shape=synth.KDA)):
             print(json.dumps(r), flush=True)
@@ -539,6 +571,7 @@ def main():
         draft, commit = bench_spec(torch, gdn, synth)
         pdraft, pcommit = bench_spec_pool(torch, gdn, synth)
         kda, kda_fused = bench_kda_stack(torch, gdn, synth)
+        pack, unpack = bench_slot_pack(torch, gdn, synth)
         pf = bench_prefill(torch, gdn, synth)
         pfk = bench_prefill(torch, gdn, synth, shape=synth.KDA)
         paths = {"decode_qwen35_b16": d16, "spec_draft_qwen35_b64_t7": draft,
@@ -546,6 +579,7 @@ def main():
                  "spec_draft_pool_slots_qwen35_b64_t7": pdraft,
                  "spec_commit_index_b64": pcommit,
                  "kda_stack_b64_48layers": kda, "kda_stack_b64_48layers_fused_prep": kda_fused,
+                 "slot_pack_qwen35_64": pack, "slot_unpack_qwen35_64": unpack,
                  "prefill_qwen35_4x8192": pf, "prefill_kda_4x8192": pfk}
 
     cpu = None

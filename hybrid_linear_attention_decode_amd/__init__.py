@@ -8,7 +8,8 @@ loudly.  Build it with ``python -m hybrid_linear_attention_decode_amd.build``.
 
 Entry points (same names as the C ABI):
     gdn_decode_step, gdn_spec_decode_commit, gdn_spec_commit_index, gdn_prefill_chunked,
-    gdn_prefill_workspace_size, gdn_slot_copy, gdn_slot_zero, gdn_status_string
+    gdn_prefill_workspace_size, gdn_slot_copy, gdn_slot_zero, gdn_slot_bytes, gdn_slot_pack,
+    gdn_slot_unpack, gdn_status_string
 """
 from __future__ import annotations
 
@@ -32,7 +33,8 @@ GDN_F_CONV_SILU, GDN_F_L2NORM_QK = 1, 2
 
 EXPORTED = ("gdn_decode_step", "gdn_spec_decode_commit", "gdn_spec_commit_index",
             "gdn_prefill_chunked", "gdn_prefill_workspace_size", "gdn_slot_copy",
-            "gdn_slot_zero", "gdn_status_string")
+            "gdn_slot_zero", "gdn_slot_bytes", "gdn_slot_pack", "gdn_slot_unpack",
+            "gdn_status_string")
 
 
 class GdnError(RuntimeError):
@@ -87,10 +89,15 @@ def lib() -> ct.CDLL:
         L.gdn_prefill_workspace_size.restype = ct.c_size_t
         L.gdn_slot_copy.argtypes = [lp, pp, P, P, i32, P]
         L.gdn_slot_zero.argtypes = [lp, pp, P, i32, P]
+        L.gdn_slot_bytes.argtypes = [lp]
+        L.gdn_slot_bytes.restype = ct.c_size_t
+        L.gdn_slot_pack.argtypes = [lp, pp, P, i32, P, ct.c_size_t, P]
+        L.gdn_slot_unpack.argtypes = [lp, pp, P, ct.c_size_t, P, i32, P]
         L.gdn_status_string.argtypes = [ct.c_int]
         L.gdn_status_string.restype = ct.c_char_p
         for f in ("gdn_decode_step", "gdn_spec_decode_commit", "gdn_spec_commit_index",
-                  "gdn_prefill_chunked", "gdn_slot_copy", "gdn_slot_zero"):
+                  "gdn_prefill_chunked", "gdn_slot_copy", "gdn_slot_zero", "gdn_slot_pack",
+                  "gdn_slot_unpack"):
             getattr(L, f).restype = ct.c_int
         _lib = L
     return _lib
@@ -243,6 +250,38 @@ def gdn_slot_zero(layer: Layer, ssm, conv, idx, stream=None):
     P = _pool(ssm, conv)
     st = lib().gdn_slot_zero(ct.byref(L), ct.byref(P), _ptr(idx), idx.numel(), _stream(stream))
     _check(st, "gdn_slot_zero")
+
+
+def gdn_slot_bytes(layer: Layer) -> int:
+    L = layer.c_struct()
+    return int(lib().gdn_slot_bytes(ct.byref(L)))
+
+
+def gdn_slot_pack(layer: Layer, ssm, conv, idx, buffer=None, stream=None):
+    """Slots idx [n] int32 -> a contiguous uint8 buffer of n packed items
+    (allocated when not given); returns the buffer.  See include/gdn.h."""
+    import torch
+    _dev(ssm, conv, idx, buffer)
+    n = idx.numel()
+    if buffer is None:
+        buffer = torch.empty(max(n * gdn_slot_bytes(layer), 16), dtype=torch.uint8,
+                             device=ssm.device)
+    L = layer.c_struct()
+    P = _pool(ssm, conv)
+    st = lib().gdn_slot_pack(ct.byref(L), ct.byref(P), _ptr(idx), n, _ptr(buffer),
+                             buffer.numel() * buffer.element_size(), _stream(stream))
+    _check(st, "gdn_slot_pack")
+    return buffer
+
+
+def gdn_slot_unpack(layer: Layer, ssm, conv, buffer, idx, stream=None):
+    _dev(ssm, conv, idx, buffer)
+    L = layer.c_struct()
+    P = _pool(ssm, conv)
+    st = lib().gdn_slot_unpack(ct.byref(L), ct.byref(P), _ptr(buffer),
+                               buffer.numel() * buffer.element_size(), _ptr(idx), idx.numel(),
+                               _stream(stream))
+    _check(st, "gdn_slot_unpack")
 
 
 def gdn_prefill_workspace_size(layer: Layer, N: int, max_seqlen: int, total_tokens: int,

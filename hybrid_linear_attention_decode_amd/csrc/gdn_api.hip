@@ -67,6 +67,28 @@ SlotArgs slot_args(const gdn_layer* L, const gdn_pool* P, int32_t n) {
   return a;
 }
 
+size_t slot_bytes(const gdn_layer* L) {
+  const gdn_pool dummy{nullptr, nullptr, 1};
+  const SlotArgs a = slot_args(L, &dummy, 0);
+  return static_cast<size_t>((a.ssm_vec + a.conv_vec) * 16);
+}
+
+gdn_status pack_common(const gdn_layer* L, const gdn_pool* P, const int32_t* idx, int32_t n,
+                       const void* buffer, size_t buffer_bytes, gdn::SlotMode mode, void* stream) {
+  gdn_status st = check_layer(L);
+  if (st != GDN_OK) return st;
+  if ((st = check_pool(L, P)) != GDN_OK) return st;
+  if (n < 0 || n > 65535) return GDN_ERR_BAD_SHAPE;
+  if (n == 0) return GDN_OK;
+  if (!idx || !buffer) return GDN_ERR_NULL_ARG;
+  if (!aligned16(buffer)) return GDN_ERR_BAD_SHAPE;
+  if (buffer_bytes / static_cast<size_t>(n) < slot_bytes(L)) return GDN_ERR_BAD_SHAPE;
+  SlotArgs a = slot_args(L, P, n);
+  a.a = idx;
+  a.buf = const_cast<void*>(buffer);
+  return from_hip(gdn::launch_slots(a, mode, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -184,6 +206,22 @@ gdn_status gdn_slot_copy(const gdn_layer* L, const gdn_pool* P, const int32_t* s
   a.a = src;
   a.b = dst;
   return from_hip(gdn::launch_slots(a, gdn::kSlotCopy, static_cast<hipStream_t>(stream)));
+}
+
+size_t gdn_slot_bytes(const gdn_layer* L) {
+  if (check_layer(L) != GDN_OK) return 0;
+  return slot_bytes(L);
+}
+
+
+gdn_status gdn_slot_pack(const gdn_layer* L, const gdn_pool* P, const int32_t* idx, int32_t n,
+                         void* buffer, size_t buffer_bytes, void* stream) {
+  return pack_common(L, P, idx, n, buffer, buffer_bytes, gdn::kSlotPack, stream);
+}
+
+gdn_status gdn_slot_unpack(const gdn_layer* L, const gdn_pool* P, const void* buffer,
+                           size_t buffer_bytes, const int32_t* idx, int32_t n, void* stream) {
+  return pack_common(L, P, idx, n, buffer, buffer_bytes, gdn::kSlotUnpack, stream);
 }
 
 gdn_status gdn_slot_zero(const gdn_layer* L, const gdn_pool* P, const int32_t* idx, int32_t n,

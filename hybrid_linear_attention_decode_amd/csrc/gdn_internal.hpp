@@ -45,9 +45,10 @@ struct SlotArgs {
   const float* spec_ssm;     // commit only
   const void* spec_conv;
   int32_t t_max;
+  void* buf;                 // pack / unpack: n items of (ssm slot || conv slot)
 };
 
-enum SlotMode { kSlotCopy = 0, kSlotZero = 1, kSlotCommit = 2 };
+enum SlotMode { kSlotCopy = 0, kSlotZero = 1, kSlotCommit = 2, kSlotPack = 3, kSlotUnpack = 4 };
 
 // Commit by index (snapshots in pool slots).
 struct CommitIndexArgs {

@@ -4,6 +4,8 @@
 // streaming copies; one workgroup moves a contiguous 16 KiB piece of one
 // item's ssm slot followed by its conv slot.  When the snapshots themselves
 // live in pool slots, the commit is an index update (commit_index_kernel).
+// Pack / unpack move slots to and from a contiguous buffer of (ssm || conv)
+// items, bitwise -- the local half of moving state between engines.
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
@@ -42,16 +44,34 @@ __global__ void __launch_bounds__(kThreads) slot_kernel(const SlotArgs a) {
   } else if (MODE == kSlotZero) {
     if (ia < 0 || ia >= a.num_slots) return;
     dst = ia;
-  } else {  // commit: item = request, a = slots, b = accepted lengths
+  } else if (MODE == kSlotCommit) {  // item = request, a = slots, b = accepted lengths
     const int32_t L = a.b[item];
     if (ia < 0 || ia >= a.num_slots || L < 1 || L > a.t_max) return;
     dst = ia;
     const int64_t row = static_cast<int64_t>(item) * a.t_max + (L - 1);
     src_ssm = reinterpret_cast<const char*>(a.spec_ssm) + row * ssm_bytes;
     src_conv = static_cast<const char*>(a.spec_conv) + row * conv_bytes;
+  } else {  // pack / unpack: item i of the buffer <-> slot a[i]
+    if (ia < 0 || ia >= a.num_slots) return;
+    char* packed = static_cast<char*>(a.buf) + item * (ssm_bytes + conv_bytes);
+    if (MODE == kSlotPack) {
+      src_ssm = reinterpret_cast<const char*>(a.ssm) + ia * ssm_bytes;
+      src_conv = static_cast<const char*>(a.conv) + ia * conv_bytes;
+    } else {
+      src_ssm = packed;
+      src_conv = packed + ssm_bytes;
+      dst = ia;
+    }
   }
-  char* dst_ssm = reinterpret_cast<char*>(a.ssm) + dst * ssm_bytes;
-  char* dst_conv = static_cast<char*>(a.conv) + dst * conv_bytes;
+  char* dst_ssm;
+  char* dst_conv;
+  if (MODE == kSlotPack) {
+    dst_ssm = static_cast<char*>(a.buf) + item * (ssm_bytes + conv_bytes);
+    dst_conv = dst_ssm + ssm_bytes;
+  } else {
+    dst_ssm = reinterpret_cast<char*>(a.ssm) + dst * ssm_bytes;
+    dst_conv = static_cast<char*>(a.conv) + dst * conv_bytes;
+  }
 
   const int64_t v0 = static_cast<int64_t>(blockIdx.x) * kVecPerBlock;
   const int64_t total = a.ssm_vec + a.conv_vec;
@@ -114,6 +134,12 @@ hipError_t launch_slots(const SlotArgs& a, SlotMode mode, hipStream_t s) {
       break;
     case kSlotCommit:
       hipLaunchKernelGGL(slot_kernel<kSlotCommit>, grid, dim3(kThreads), 0, s, a);
+      break;
+    case kSlotPack:
+      hipLaunchKernelGGL(slot_kernel<kSlotPack>, grid, dim3(kThreads), 0, s, a);
+      break;
+    case kSlotUnpack:
+      hipLaunchKernelGGL(slot_kernel<kSlotUnpack>, grid, dim3(kThreads), 0, s, a);
       break;
   }
   return hipGetLastError();

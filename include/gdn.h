@@ -235,6 +235,24 @@ gdn_status gdn_slot_copy(const gdn_layer* layer, const gdn_pool* pool, const int
 gdn_status gdn_slot_zero(const gdn_layer* layer, const gdn_pool* pool, const int32_t* idx,
                          int32_t n, void* stream);
 
+/*
+ * Slot pack / unpack: the local half of moving working state between engines
+ * (mechatronicstore.cl note, section on prefill / decode disaggregation: slot
+ * indices become byte offsets become contiguous blocks).  A packed item is
+ * one slot's ssm bytes followed by its conv bytes, bitwise, gdn_slot_bytes()
+ * long; item i of the buffer is slot idx[i].
+ *   pack: buffer[i] <- slot idx[i];  unpack: slot idx[i] <- buffer[i].
+ *   idx [n] int32 (device); an index outside the pool skips its item (the
+ *   buffer item, or the slot, is left as it was).  buffer (device, 16-byte
+ *   aligned) holds at least n * gdn_slot_bytes() bytes, else
+ *   GDN_ERR_BAD_SHAPE.  Unpack targets must be distinct.
+ */
+size_t gdn_slot_bytes(const gdn_layer* layer);
+gdn_status gdn_slot_pack(const gdn_layer* layer, const gdn_pool* pool, const int32_t* idx,
+                         int32_t n, void* buffer, size_t buffer_bytes, void* stream);
+gdn_status gdn_slot_unpack(const gdn_layer* layer, const gdn_pool* pool, const void* buffer,
+                           size_t buffer_bytes, const int32_t* idx, int32_t n, void* stream);
+
 /* Static string for a status code (never NULL). */
 const char* gdn_status_string(gdn_status status);
 

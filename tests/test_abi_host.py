@@ -116,6 +116,29 @@ def test_bad_commit_index_arguments():
                                       4, None) == gdn.GDN_ERR_BAD_SHAPE
 
 
+def test_slot_pack_arguments():
+    """Packed slot size and the refusals of pack / unpack (nothing enqueued)."""
+    lib = gdn.lib()
+    L = qwen_layer()
+    item = 32 * 128 * 128 * 4 + 3 * 8192 * 2          # ssm slot + bf16 conv window
+    assert lib.gdn_slot_bytes(ct.byref(L)) == item
+    K = qwen_layer(gate="channel", n_k_heads=32, n_v_heads=32, act_dtype="f32")
+    assert lib.gdn_slot_bytes(ct.byref(K)) == 32 * 128 * 128 * 4 + 3 * 12288 * 4
+    bad = qwen_layer(d_k=96)
+    assert lib.gdn_slot_bytes(ct.byref(bad)) == 0
+    pool = GdnPool(FAKE, FAKE, 8)
+    for fn, args in ((lib.gdn_slot_pack, lambda n, buf, nb, idx: (idx, n, buf, nb)),
+                     (lib.gdn_slot_unpack, lambda n, buf, nb, idx: (buf, nb, idx, n))):
+        call = lambda n, buf=FAKE, nb=4 * item, idx=FAKE: fn(ct.byref(L), ct.byref(pool),
+                                                            *args(n, buf, nb, idx), None)
+        assert call(4, nb=4 * item - 1) == gdn.GDN_ERR_BAD_SHAPE     # buffer too small
+        assert call(4, buf=ct.c_void_p(0x10008)) == gdn.GDN_ERR_BAD_SHAPE
+        assert call(4, buf=None) == gdn.GDN_ERR_NULL_ARG
+        assert call(4, idx=None) == gdn.GDN_ERR_NULL_ARG
+        assert call(-1) == gdn.GDN_ERR_BAD_SHAPE
+        assert call(0, buf=None, idx=None) == gdn.GDN_OK
+
+
 def test_bad_slot_and_commit_arguments():
     L = qwen_layer()
     pool = GdnPool(FAKE, FAKE, 8)

@@ -1,6 +1,6 @@
 """GPU checks of the slot preparation fused into the decode step (zero start,
-copy-on-write source) and of speculative snapshots kept in pool slots with the
-commit by index.  Each is compared bit for bit with the separate-kernel path it
+copy-on-write source), of speculative snapshots kept in pool slots with the
+commit by index, and of slot pack / unpack.  Each is compared bit for bit with the separate-kernel path it
 replaces (slot zero / copy, then decode; spec-cache draft, then copy commit),
 which the other GPU tests hold against the oracle; outputs are also checked
 against the oracle directly."""
@@ -121,7 +121,7 @@ def test_pool_snapshots_and_commit_by_index(shape, B):
     equals the copy commit's working slot; L = 0 and a dropped snapshot (its
     slot outside the pool) leave the index alone."""
     torch = _torch()
-    T, slots = 7, (1024 if shape is synth.QWEN35 else 1024)
+    T, slots = 7, 1024
     case = synth.decode_case(shape, B=B, T=T, num_slots=slots, n_calls=1, seed=33)
     acc = synth.accepted_lengths(B, T, seed=33)
     g, o = layers(shape)
@@ -177,3 +177,45 @@ def test_pool_snapshots_and_commit_by_index(shape, B):
                         spec_ssm=np.zeros((B, T) + s64.shape[1:]),
                         spec_conv=np.zeros((B, T) + c64.shape[1:]))
     assert rel_err(host(ob), ref) <= OUT_TOL
+
+
+@pytest.mark.parametrize("shape", [synth.QWEN35, synth.Shape(2, 2, 32, 32, 4, "channel", "f32")])
+def test_slot_pack_unpack_bitwise(shape):
+    """Packed items are the slots' own bytes (ssm then conv); unpacking them
+    into other slots reproduces the slots bit for bit; an index outside the
+    pool leaves its buffer item (pack) or nothing (unpack) untouched."""
+    torch = _torch()
+    slots, n = 48, 6
+    case = synth.decode_case(shape, B=n, T=1, num_slots=slots, n_calls=1, seed=34, all_live=True,
+                             rotate=False)
+    g, _ = layers(shape)
+    ssm, conv = _pools(case)
+    src = np.array([3, 17, 40, 0, 47, 22], np.int32)
+    src_bad = src.copy()
+    src_bad[2] = slots + 3
+    item = gdn.gdn_slot_bytes(g)
+    assert item == ssm[0].numel() * 4 + conv[0].numel() * conv.element_size()
+    buf = torch.full((n * item,), 0xA5, dtype=torch.uint8, device="cuda")
+    gdn.gdn_slot_pack(g, ssm, conv, dev(src_bad), buffer=buf)
+    torch.cuda.synchronize()
+    b = host(buf).reshape(n, item)
+    s_bytes = host(ssm).view(np.uint8).reshape(slots, -1)
+    c_bytes = host(conv).view(np.uint8).reshape(slots, -1)
+    for i in range(n):
+        if i == 2:
+            assert (b[i] == 0xA5).all()
+        else:
+            np.testing.assert_array_equal(b[i], np.concatenate([s_bytes[src[i]], c_bytes[src[i]]]))
+    # full pack, then unpack into fresh slots (one target outside the pool)
+    buf = gdn.gdn_slot_pack(g, ssm, conv, dev(src))
+    before = bits(ssm), bits(conv)
+    dst = np.array([5, 6, 7, 8, 9, slots + 1], np.int32)
+    gdn.gdn_slot_unpack(g, ssm, conv, buf, dev(dst))
+    torch.cuda.synchronize()
+    after = bits(ssm), bits(conv)
+    for i in range(5):
+        np.testing.assert_array_equal(after[0][dst[i]], before[0][src[i]])
+        np.testing.assert_array_equal(after[1][dst[i]], before[1][src[i]])
+    others = np.setdiff1d(np.arange(slots), dst[:5])
+    np.testing.assert_array_equal(after[0][others], before[0][others])
+    np.testing.assert_array_equal(after[1][others], before[1][others])
