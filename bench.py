@@ -480,6 +480,60 @@ def bench_prefill(torch, gdn, synth, K=10, W=2, seqlens=(8192,) * 4, shape=None)
     return rec
 
 
+def bench_prefill_ckpt(torch, gdn, synth, K=10, W=2):
+    """The agentic path on the Qwen3.5 layer: a 4 x 8192 prefill that also
+    emits a checkpoint (state + conv window) every 128 tokens into 256 pool
+    slots, and a short append of 4 x 512 tokens that starts from checkpoint
+    slots (copy-on-write into fresh working slots)."""
+    shape = synth.QWEN35
+    seqlens, every = [8192] * 4, 128
+    case = synth.prefill_case(shape, seqlens, 272, seed=18)
+    dev = _dev(torch)
+    g = gdn.Layer(shape.n_k_heads, shape.n_v_heads, shape.d_k, shape.d_v, shape.conv_width,
+                  shape.gate, shape.dtype)
+    ssm, conv = dev(case.pool.ssm), dev(case.pool.conv)
+    used = set(case.dst.tolist()) | set(case.init_slot[case.init_slot >= 0].tolist())
+    spare = np.array([s for s in range(272) if s not in used], np.int32)
+    tab = dev(spare[:4 * 64].reshape(4, 64))
+    x, al, be, w = dev(case.x), dev(case.alpha), dev(case.beta), dev(case.conv_w)
+    dst, init, cu = dev(case.dst), dev(case.init_slot), dev(case.cu_seqlens)
+    total = int(case.cu_seqlens[-1])
+    out = torch.empty((total, shape.n_v_heads, shape.d_v), dtype=torch.float32, device="cuda")
+
+    def full(_c):
+        gdn.gdn_prefill_chunked(g, ssm, conv, dst, init, cu, 8192, x, al, be, w, out=out,
+                                ckpt_slots=tab, ckpt_every=every)
+    for c in range(W):
+        full(c)
+    ms = time_calls(torch, full, W, K) / K
+    nbytes, flops, _ = prefill_counts(shape, seqlens)
+    slot_bytes = shape.n_v_heads * shape.d_v * shape.d_k * 4 + \
+        (shape.conv_width - 1) * shape.channels * 2
+    ck_bytes = 4 * 64 * slot_bytes
+    rec = path_record(ms, nbytes + ck_bytes, total, "chunked prefill, Qwen3.5 shape, 4 x 8192 "
+                                                    "tokens, a checkpoint every 128 tokens "
+                                                    "(256 slots)")
+    rec["checkpoint_bytes"] = int(ck_bytes)
+    # append: 4 x 512 tokens from checkpoints 16, 32, 48, 63 of the sequences
+    alens = [512] * 4
+    acu = dev(np.arange(0, 5 * 512, 512, dtype=np.int32))
+    starts = dev(np.array([spare[16], spare[64 + 32], spare[128 + 48], spare[192 + 63]],
+                          np.int32))
+    adst = dev(spare[4 * 64:4 * 64 + 4].copy())
+    ax, aal, abe = x[:2048].contiguous(), al[:2048].contiguous(), be[:2048].contiguous()
+    aout = torch.empty((2048, shape.n_v_heads, shape.d_v), dtype=torch.float32, device="cuda")
+
+    def append(_c):
+        gdn.gdn_prefill_chunked(g, ssm, conv, adst, starts, acu, 512, ax, aal, abe, w, out=aout)
+    for c in range(W):
+        append(c)
+    ms_a = time_calls(torch, append, W, 5 * K) / (5 * K)
+    abytes, _, _ = prefill_counts(shape, alens)
+    arec = path_record(ms_a, abytes, 2048, "short append, Qwen3.5 shape, 4 x 512 tokens, each "
+                                           "starting from a checkpoint slot")
+    return rec, arec
+
+
 def copy_calibration(torch, mib: int = 256, reps: int = 5):
     """A plain device copy of known size, for scaling the PMC byte counters."""
     n = mib * (1 << 20) // 4
@@ -528,7 +582,7 @@ def main():
         for r in (bench_decode_b16(torch, gdn, synth), *bench_spec(torch, gdn, synth),
                   *bench_spec_pool(torch, gdn, synth), *bench_kda_stack(torch, gdn, synth),
                   *bench_slot_pack(torch, gdn, synth),
-                  bench_prefill(torch, gdn, synth),
+                  bench_prefill(torch, gdn, synth), *bench_prefill_ckpt(torch, gdn, synth),
                   bench_prefill(torch, gdn, synth, shape=synth.KDA)):
             print(json.dumps(r), flush=True)
         return
@@ -566,13 +620,15 @@ def main():
     if args.only == "all":
         log("bench: other paths (B=16 decode, speculative draft + commit with snapshots in "
             "spec buffers and in pool slots, KDA 48-layer stack with separate and fused slot "
-            "preparation, chunked prefill of both layers)")
+            "preparation, slot pack / unpack, chunked prefill of both layers, with checkpoints and "
+            "the append from them)")
         d16 = bench_decode_b16(torch, gdn, synth)
         draft, commit = bench_spec(torch, gdn, synth)
         pdraft, pcommit = bench_spec_pool(torch, gdn, synth)
         kda, kda_fused = bench_kda_stack(torch, gdn, synth)
         pack, unpack = bench_slot_pack(torch, gdn, synth)
         pf = bench_prefill(torch, gdn, synth)
+        pfc, app = bench_prefill_ckpt(torch, gdn, synth)
         pfk = bench_prefill(torch, gdn, synth, shape=synth.KDA)
         paths = {"decode_qwen35_b16": d16, "spec_draft_qwen35_b64_t7": draft,
                  "spec_commit_qwen35_b64": commit,
@@ -580,7 +636,8 @@ def main():
                  "spec_commit_index_b64": pcommit,
                  "kda_stack_b64_48layers": kda, "kda_stack_b64_48layers_fused_prep": kda_fused,
                  "slot_pack_qwen35_64": pack, "slot_unpack_qwen35_64": unpack,
-                 "prefill_qwen35_4x8192": pf, "prefill_kda_4x8192": pfk}
+                 "prefill_qwen35_4x8192": pf, "prefill_qwen35_4x8192_ckpt128": pfc,
+                 "append_qwen35_4x512_from_ckpt": app, "prefill_kda_4x8192": pfk}
 
     cpu = None
     if not args.no_cpu_baseline and args.only == "all":

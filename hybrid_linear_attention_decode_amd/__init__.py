@@ -59,6 +59,10 @@ class GdnSpecCache(ct.Structure):
                 ("slots", ct.c_void_p)]
 
 
+class GdnPrefillCkpt(ct.Structure):
+    _fields_ = [("slots", ct.c_void_p), ("every", ct.c_int32), ("per_seq", ct.c_int32)]
+
+
 class GdnInputs(ct.Structure):
     _fields_ = [("x", ct.c_void_p), ("alpha", ct.c_void_p), ("beta", ct.c_void_p),
                 ("conv_w", ct.c_void_p), ("conv_b", ct.c_void_p)]
@@ -83,8 +87,8 @@ def lib() -> ct.CDLL:
         L.gdn_decode_step.argtypes = [lp, pp, P, P, i32, i32, ip, P, sp, P]
         L.gdn_spec_decode_commit.argtypes = [lp, pp, P, sp, P, i32, P]
         L.gdn_spec_commit_index.argtypes = [pp, sp, P, P, P, i32, P]
-        L.gdn_prefill_chunked.argtypes = [lp, pp, P, P, i32, P, i32, i32, i32, ip, P, P,
-                                          ct.c_size_t, P]
+        L.gdn_prefill_chunked.argtypes = [lp, pp, P, P, i32, P, i32, i32, i32, ip, P,
+                                          ct.POINTER(GdnPrefillCkpt), P, ct.c_size_t, P]
         L.gdn_prefill_workspace_size.argtypes = [lp, i32, i32, i32, i32]
         L.gdn_prefill_workspace_size.restype = ct.c_size_t
         L.gdn_slot_copy.argtypes = [lp, pp, P, P, i32, P]
@@ -292,11 +296,19 @@ def gdn_prefill_workspace_size(layer: Layer, N: int, max_seqlen: int, total_toke
 
 def gdn_prefill_chunked(layer: Layer, ssm, conv, dst_slots, init_slot, cu_seqlens, max_seqlen,
                         x, alpha, beta, conv_w, conv_b=None, out=None, workspace=None,
-                        chunk: int = 64, stream=None):
-    """x [total, C]; cu_seqlens [N+1] int32 (device); returns out [total, H_v, d_v] fp32."""
+                        chunk: int = 64, ckpt_slots=None, ckpt_every: int = 128, stream=None):
+    """x [total, C]; cu_seqlens [N+1] int32 (device); returns out [total, H_v, d_v] fp32.
+    ckpt_slots [N, per_seq] int32: checkpoint k of sequence s (the state after
+    (k+1)*ckpt_every tokens) goes to pool slot ckpt_slots[s, k]."""
     import torch
     _dev(ssm, conv, dst_slots, init_slot, cu_seqlens, x, alpha, beta, conv_w, conv_b, out,
-         workspace)
+         workspace, ckpt_slots)
+    ck = None
+    if ckpt_slots is not None:
+        if ckpt_slots.dtype != torch.int32 or ckpt_slots.dim() != 2 or \
+                ckpt_slots.shape[0] != dst_slots.numel():
+            raise ValueError("ckpt_slots must be int32 [N, per_seq]")
+        ck = ct.byref(GdnPrefillCkpt(_ptr(ckpt_slots), int(ckpt_every), ckpt_slots.shape[1]))
     N = dst_slots.numel()
     total = x.shape[0]
     if out is None:
@@ -310,7 +322,7 @@ def gdn_prefill_chunked(layer: Layer, ssm, conv, dst_slots, init_slot, cu_seqlen
     inp = GdnInputs(_ptr(x), _ptr(alpha), _ptr(beta), _ptr(conv_w), _ptr(conv_b))
     st = lib().gdn_prefill_chunked(ct.byref(L), ct.byref(P), _ptr(dst_slots), _ptr(init_slot),
                                    N, _ptr(cu_seqlens), int(max_seqlen), int(total), int(chunk),
-                                   ct.byref(inp), _ptr(out), _ptr(workspace),
+                                   ct.byref(inp), _ptr(out), ck, _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "gdn_prefill_chunked")
     return out

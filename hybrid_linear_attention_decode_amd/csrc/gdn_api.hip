@@ -249,8 +249,8 @@ size_t gdn_prefill_workspace_size(const gdn_layer* L, int32_t N, int32_t max_seq
 gdn_status gdn_prefill_chunked(const gdn_layer* L, const gdn_pool* P, const int32_t* dst,
                                const int32_t* init_slot, int32_t N, const int32_t* cu_seqlens,
                                int32_t max_seqlen, int32_t total_tokens, int32_t chunk,
-                               const gdn_inputs* in, float* out, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+                               const gdn_inputs* in, float* out, const gdn_prefill_ckpt* ckpt,
+                               void* workspace, size_t workspace_bytes, void* stream) {
   gdn_status st = check_layer(L);
   if (st != GDN_OK) return st;
   if ((st = check_pool(L, P)) != GDN_OK) return st;
@@ -259,6 +259,11 @@ gdn_status gdn_prefill_chunked(const gdn_layer* L, const gdn_pool* P, const int3
   if (!gdn::prefill_supported(L->d_k, L->gate == GDN_GATE_CHANNEL)) return GDN_ERR_UNSUPPORTED;
   const int32_t nblk = (L->d_v + 63) / 64;
   if (static_cast<int64_t>(N) * L->n_v_heads * nblk > INT32_MAX) return GDN_ERR_BAD_SHAPE;
+  if (ckpt) {
+    if (ckpt->per_seq < 0 || ckpt->per_seq > 65534) return GDN_ERR_BAD_SHAPE;
+    if (ckpt->every < 64 || ckpt->every % 64) return GDN_ERR_BAD_SHAPE;
+    if (ckpt->per_seq > 0 && !ckpt->slots) return GDN_ERR_NULL_ARG;
+  }
   if (N == 0) return GDN_OK;
   if (!dst || !cu_seqlens || !in) return GDN_ERR_NULL_ARG;
   if (total_tokens > 0 && (!in->x || !in->alpha || !in->beta || !in->conv_w || !out))
@@ -300,6 +305,11 @@ gdn_status gdn_prefill_chunked(const gdn_layer* L, const gdn_pool* P, const int3
   a.bias = in->conv_b;
   a.out = out;
   a.ws = workspace;
+  if (ckpt && ckpt->per_seq > 0) {
+    a.ckpt = ckpt->slots;
+    a.ckpt_every = ckpt->every;
+    a.ckpt_per_seq = ckpt->per_seq;
+  }
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   if (kda)
     return from_hip(gdn::launch_prefill_kda(a, L->d_k, L->act_dtype == GDN_BF16, max_seqlen, hs));

@@ -81,6 +81,9 @@ struct PrefillArgs {
   const void* bias;          // [C] or nullptr
   float* out;                // [total][Hv][dv]
   void* ws;                  // per-channel decay: diagonal-block records (workspace)
+  const int32_t* ckpt;       // [N][ckpt_per_seq] checkpoint slots, or nullptr
+  int32_t ckpt_every;        // tokens between checkpoints (a multiple of the chunk)
+  int32_t ckpt_per_seq;
 };
 
 // Launchers: return hipSuccess or the launch error.  The caller has validated

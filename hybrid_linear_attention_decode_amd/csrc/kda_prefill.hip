@@ -938,7 +938,15 @@ __global__ void __launch_bounds__(kThreads, 1) kda_chunk_kernel(PrefillArgs a) {
     }
     for (int c = 0; c < nch; ++c) {
       const bool next = c + 1 < nch;
-      if (cols) k.columns(c * kC, S, cv, next);
+      if (cols) {
+        k.columns(c * kC, S, cv, next);
+        const int32_t cs = ckpt_slot(a, s, (c + 1) * kC, k.T);
+        if (cs >= 0) {        // the state after (c + 1) * 64 tokens, to a checkpoint slot
+          float* o = a.ssm + cs * slot_elems + head + static_cast<int64_t>(k.e0 + k.lr) * DK;
+#pragma unroll
+          for (int d = 0; d < K::kDt; ++d) *reinterpret_cast<f4*>(o + 16 * d + 4 * k.lg) = S[d];
+        }
+      }
       lds_barrier();          // chunk c consumed
       if (next) {
         lds_barrier();        // producers stored chunk c + 1
@@ -970,7 +978,7 @@ hipError_t launch_kda(const PrefillArgs& a, int max_seqlen, hipStream_t st) {
                      bytes, st, a);
   e = hipGetLastError();
   if (e != hipSuccess || a.W < 2) return e;
-  hipLaunchKernelGGL((prefill_conv_tail<Act>), dim3((a.C + 255) / 256, a.N), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((prefill_conv_tail<Act>), conv_tail_grid(a), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

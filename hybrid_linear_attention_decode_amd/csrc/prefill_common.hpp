@@ -248,10 +248,23 @@ struct PrefillCore {
   using Core::win_rows; using Core::x_off; using Core::win_off; using Core::tap;          \
   using Core::act
 
-// The destination conv window: the last W-1 inputs of the sequence (taken
-// from the initial window when the sequence is shorter).  Runs after the
-// main kernel, so an in-place sequence (init == dst) has read its window.
-// Each thread reads its channel's rows before writing any.
+// Pool slot of checkpoint k = tok / every - 1 of sequence s, taken after its
+// first tok tokens, or -1 when there is none (no checkpoint table, tok past
+// the sequence or not a multiple of the interval, k past the table's
+// columns, an entry outside the pool).
+__device__ __forceinline__ int32_t ckpt_slot(const PrefillArgs& a, int s, int tok, int T) {
+  if (!a.ckpt || tok > T || tok % a.ckpt_every) return -1;
+  const int k = tok / a.ckpt_every - 1;
+  if (k < 0 || k >= a.ckpt_per_seq) return -1;
+  const int32_t sl = a.ckpt[static_cast<int64_t>(s) * a.ckpt_per_seq + k];
+  return (sl < 0 || sl >= a.num_slots) ? -1 : sl;
+}
+
+// Conv windows written after the main kernel.  z = 0: the destination's,
+// the last W-1 inputs of the sequence (taken from the initial window when
+// the sequence is shorter; the main kernel has read an in-place sequence's
+// old window by now, and each thread reads its channel's rows before writing
+// any).  z = k + 1: checkpoint k's, the W-1 inputs before its token.
 template <typename Act>
 __global__ void __launch_bounds__(256) prefill_conv_tail(PrefillArgs a) {
   const int s = blockIdx.y;
@@ -263,6 +276,13 @@ __global__ void __launch_bounds__(256) prefill_conv_tail(PrefillArgs a) {
   if (t0 < 0 || t1 < t0 || t1 > a.total || dst < 0 || dst >= a.num_slots || init >= a.num_slots)
     return;
   const int T = t1 - t0, W1 = a.W - 1;
+  int end = T;              // the window ends before row `end`
+  int32_t to = dst;
+  if (blockIdx.z > 0) {
+    end = static_cast<int>(blockIdx.z) * a.ckpt_every;
+    to = ckpt_slot(a, s, end, T);
+    if (to < 0) return;
+  }
   const Act* x = static_cast<const Act*>(a.x);
   Act* conv = static_cast<Act*>(a.conv);
   Act v[3];
@@ -270,7 +290,7 @@ __global__ void __launch_bounds__(256) prefill_conv_tail(PrefillArgs a) {
   for (int jj = 0; jj < 3; ++jj) {
     v[jj] = from_exact<Act>(0.f);
     if (jj < W1) {
-      const int rho = T - W1 + jj;
+      const int rho = end - W1 + jj;
       if (rho >= 0)
         v[jj] = x[(static_cast<int64_t>(t0) + rho) * a.C + c];
       else if (init >= 0)
@@ -279,7 +299,12 @@ __global__ void __launch_bounds__(256) prefill_conv_tail(PrefillArgs a) {
   }
 #pragma unroll
   for (int jj = 0; jj < 3; ++jj)
-    if (jj < W1) conv[(static_cast<int64_t>(dst) * W1 + jj) * a.C + c] = v[jj];
+    if (jj < W1) conv[(static_cast<int64_t>(to) * W1 + jj) * a.C + c] = v[jj];
+}
+
+// Grid of prefill_conv_tail: channel blocks x sequences x (1 + checkpoints).
+inline dim3 conv_tail_grid(const PrefillArgs& a) {
+  return dim3((a.C + 255) / 256, a.N, 1 + (a.ckpt ? a.ckpt_per_seq : 0));
 }
 
 }  // namespace

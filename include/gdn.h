@@ -168,6 +168,20 @@ gdn_status gdn_spec_decode_commit(const gdn_layer* layer, const gdn_pool* pool,
                                   const gdn_spec_cache* spec, const int32_t* accepted_len,
                                   int32_t B, void* stream);
 
+/* (host) checkpoints a prefill emits on the way (mechatronicstore.cl note,
+ * section on slot lifecycles: checkpoint slots at block-aligned positions for
+ * prefix reuse): slots [N][per_seq] int32 (device); checkpoint k of sequence
+ * s is the state (ssm and conv window) after its first (k+1)*every tokens,
+ * written to pool slot slots[s][k] when (k+1)*every <= the sequence's
+ * length; entries outside the pool are skipped.  every is a multiple of the
+ * chunk (64).  Checkpoint slots must be distinct and must not be any
+ * sequence's destination or initial slot. */
+typedef struct {
+  const int32_t* slots;
+  int32_t every;
+  int32_t per_seq;
+} gdn_prefill_ckpt;
+
 /*
  * Chunked prefill of N variable-length sequences ("Scheduler dual": prefill
  * populates the initial state; "Riesgo de correctitud": a fresh working slot
@@ -186,6 +200,9 @@ gdn_status gdn_spec_decode_commit(const gdn_layer* layer, const gdn_pool* pool,
  *   in->alpha: [total][H_v] (scalar decay) or [total][H_v][d_k] (per-channel
  *     decay, 16-byte aligned).
  *   out [total][H_v][d_v] fp32.
+ *   ckpt: NULL, or the checkpoints to emit (gdn_prefill_ckpt).  A later
+ *     prefill that starts from a checkpoint (init_slot = its slot) continues
+ *     the sequence bit for bit.
  *   workspace: device scratch of at least gdn_prefill_workspace_size() bytes,
  *     256-byte aligned, owned by the caller and free again when the call's
  *     stream work has finished (the scalar decay needs none; the per-channel
@@ -196,8 +213,8 @@ gdn_status gdn_prefill_chunked(const gdn_layer* layer, const gdn_pool* pool,
                                const int32_t* dst_slots, const int32_t* init_slot, int32_t N,
                                const int32_t* cu_seqlens, int32_t max_seqlen,
                                int32_t total_tokens, int32_t chunk, const gdn_inputs* in,
-                               float* out, void* workspace, size_t workspace_bytes,
-                               void* stream);
+                               float* out, const gdn_prefill_ckpt* ckpt, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace gdn_prefill_chunked needs for these sizes: 0 for the
  * scalar decay; for the per-channel decay 2048 * H_v * (floor(total/16) +

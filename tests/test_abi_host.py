@@ -164,11 +164,12 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 
 
 def prefill(L, N=2, dst=FAKE, init=None, cu=FAKE, max_len=64, total=128, chunk=64, inp=None,
-            out=FAKE, ws=None, ws_bytes=0):
+            out=FAKE, ws=None, ws_bytes=0, ckpt=None):
     pool = GdnPool(FAKE, FAKE, 8)
     inp = inp or GdnInputs(FAKE, FAKE, FAKE, FAKE, None)
     return gdn.lib().gdn_prefill_chunked(ct.byref(L), ct.byref(pool), dst, init, N, cu,
-                                         max_len, total, chunk, ct.byref(inp), out, ws,
+                                         max_len, total, chunk, ct.byref(inp), out,
+                                         None if ckpt is None else ct.byref(ckpt), ws,
                                          ws_bytes, None)
 
 
@@ -186,6 +187,13 @@ def test_bad_prefill_arguments():
     misaligned = GdnInputs(ct.c_void_p(0x10002), FAKE, FAKE, FAKE, None)
     assert prefill(L, inp=misaligned) == gdn.GDN_ERR_BAD_SHAPE
     assert prefill(L, N=0) == gdn.GDN_OK                  # nothing to do, nothing enqueued
+    # checkpoints: a chunk-multiple interval, a slot table when any are asked for
+    Ck = gdn.GdnPrefillCkpt
+    assert prefill(L, N=0, ckpt=Ck(FAKE, 96, 4)) == gdn.GDN_ERR_BAD_SHAPE
+    assert prefill(L, N=0, ckpt=Ck(FAKE, 0, 4)) == gdn.GDN_ERR_BAD_SHAPE
+    assert prefill(L, N=0, ckpt=Ck(FAKE, 128, -1)) == gdn.GDN_ERR_BAD_SHAPE
+    assert prefill(L, N=0, ckpt=Ck(None, 128, 4)) == gdn.GDN_ERR_NULL_ARG
+    assert prefill(L, N=0, ckpt=Ck(None, 128, 0)) == gdn.GDN_OK
     # the scalar-decay kernel keeps every intermediate on chip
     assert gdn.lib().gdn_prefill_workspace_size(ct.byref(L), 4, 8192, 32768, 64) == 0
 
