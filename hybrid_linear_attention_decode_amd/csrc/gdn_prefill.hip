@@ -690,14 +690,13 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
     }
     for (int c = 0; c < nch; ++c) {
       const bool next = c + 1 < nch;
-      if (cols) {
-        k.columns(c * kC, S);
-        const int32_t cs = ckpt_slot(a, s, (c + 1) * kC, k.T);
-        if (cs >= 0) {        // the state after (c + 1) * 64 tokens, to a checkpoint slot
-          float* o = a.ssm + cs * slot_elems + head + static_cast<int64_t>(k.e0 + k.lr) * DK;
+      if (cols) k.columns(c * kC, S);
+      const int32_t cs = __builtin_amdgcn_readfirstlane(ckpt_slot(a, s, (c + 1) * kC, k.T));
+      if (cols && cs >= 0) {  // the state after (c + 1) * 64 tokens, to a checkpoint slot
+        const int l = k.lane_now();
+        float* o = a.ssm + cs * slot_elems + head + static_cast<int64_t>(k.e0 + (l & 15)) * DK;
 #pragma unroll
-          for (int d = 0; d < K::kDt; ++d) *reinterpret_cast<f4*>(o + 16 * d + 4 * k.lg) = S[d];
-        }
+        for (int d = 0; d < K::kDt; ++d) *reinterpret_cast<f4*>(o + 16 * d + 4 * (l >> 4)) = S[d];
       }
       lds_barrier();          // chunk c consumed
       if (next) {

@@ -51,12 +51,15 @@ __device__ __forceinline__ int64_t ws_block(int s, int t0, int jb) {
 }
 
 // =====================================================================
-// Kernel 1: the diagonal 16 x 16 blocks, one wave per (sequence, value
-// head, token block).  Workspace record (2 KiB): lane l = 4 r + q holds
-// columns 4q..4q+3 of row r as X hi, X lo, P hi, P lo (4 bf16 each), where
-// X = (I + N)^{-1}, N_ri = b_r sum_c k_rc k_ic prod_{i < s <= r} a_sc
-// (i < r), and P_ri = sum_c q_rc k_ic prod_{i < s <= r} a_sc (i <= r).
+// Kernel 1: the diagonal 16 x 16 blocks, one workgroup of four waves per
+// (sequence, value head, token block).  Workspace record (2 KiB): lane
+// l = 4 r + q holds columns 4q..4q+3 of row r as X hi, X lo, P hi, P lo (4
+// bf16 each), where X = (I + N)^{-1}, N_ri = b_r sum_c k_rc k_ic
+// prod_{i < s <= r} a_sc (i < r), and P_ri = sum_c q_rc k_ic
+// prod_{i < s <= r} a_sc (i <= r).
 // =====================================================================
+constexpr int kDiagThreads = 256;
+
 template <int DK>
 struct DiagPlan {
   static constexpr int kRow = DK + 4;            // fp32 per row of q, k, a (padded)
@@ -65,26 +68,32 @@ struct DiagPlan {
   static constexpr int oA = oK + kBlk * kRow * 4;
   static constexpr int oN = oA + kBlk * kRow * 4;  // fp32 [16][16]
   static constexpr int oP = oN + kBlk * kBlk * 4;
-  static constexpr int oBeta = oP + kBlk * kBlk * 4;
-  static constexpr int kBytes = oBeta + kBlk * 4;
+  static constexpr int oRed = oP + kBlk * kBlk * 4;  // fp32 [4 waves][2][17][8] partial sums
+  static constexpr int oBeta = oRed + 4 * 2 * 17 * 8 * 4;
+  // conv taps (f4) and bias of the head's q and k channels, [m][octet]
+  static constexpr int oW = oBeta + kBlk * 4;
+  static constexpr int oB = oW + 2 * DK * 16;
+  static constexpr int kBytes = oB + 2 * DK * 4;
 };
 
 template <int DK, typename Act>
-__global__ void __launch_bounds__(64) kda_diag_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(kDiagThreads, 4) kda_diag_kernel(PrefillArgs a) {
   using DP = DiagPlan<DK>;
-  constexpr int kGrp = DK / 8;       // channel octets per head
-  constexpr int kTpl = kGrp / 2;     // tokens per lane in the conv stage
-  constexpr int kCw = DK / 8;        // channels per lane in the pair stage
-  constexpr int kAo = DK / 32;       // decay octets per lane
+  constexpr int kGrp = DK / 8;        // channel octets per head
+  constexpr int kItems = 2 * kGrp * kBlk;   // (q|k octet, token) conv items
+  constexpr int kNg = DK / 4;         // groups of 4 channels in the pair stage
+  constexpr int kWaves = (kNg + 7) / 8;     // waves taking part in the pair stage
   __shared__ __align__(16) unsigned char lds[DP::kBytes];
   float* yq = reinterpret_cast<float*>(lds + DP::oQ);
   float* yk = reinterpret_cast<float*>(lds + DP::oK);
   float* al = reinterpret_cast<float*>(lds + DP::oA);
   float* nm = reinterpret_cast<float*>(lds + DP::oN);
   float* pm = reinterpret_cast<float*>(lds + DP::oP);
+  float* red = reinterpret_cast<float*>(lds + DP::oRed);
   float* bt = reinterpret_cast<float*>(lds + DP::oBeta);
 
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int s = blockIdx.x / a.Hv, h = blockIdx.x % a.Hv;
   const int t0 = a.cu[s], t1 = a.cu[s + 1];
   const int32_t dst = a.dst[s];
@@ -102,144 +111,154 @@ __global__ void __launch_bounds__(64) kda_diag_kernel(PrefillArgs a) {
   core.h = h;
   core.hk = h / a.G;
 
-  // conv stage: lane = (channel octet co of q | k, token group tg)
-  const int co = lane % (2 * kGrp), tg = lane / (2 * kGrp);
+  // conv stage: item = co + 2 kGrp * token (co: channel octet of q | k), so
+  // the kGrp octets of one head and token are consecutive lanes
+  const int co = tid % (2 * kGrp);
   const bool isk = co >= kGrp;
   const int oc = isk ? co - kGrp : co;
   const int ch = (isk ? a.Hk * DK : 0) + core.hk * DK + 8 * oc;
-  f4 wt[8];
-  float bias[8];
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    wt[m] = f4{core.tap(ch + m, 0), core.tap(ch + m, 1), core.tap(ch + m, 2), core.tap(ch + m, 3)};
-    bias[m] = a.bias ? to_f32(static_cast<const Act*>(a.bias)[ch + m]) : 0.f;
+  // decay stage: item = (token r, channel octet)
+  // pair stage: lane = (column pair cp, channel group cg of 4 channels);
+  // columns cp and 15 - cp take 17 (row, column) steps in all
+  const int cp = (tid >> 3) & 7, cg = (tid & 7) + 8 * wave;
+  for (int i = tid; i < 2 * kBlk * kBlk; i += kDiagThreads) nm[i] = 0.f;  // upper parts stay 0
+  float* wl = reinterpret_cast<float*>(lds + DP::oW);
+  float* bl = reinterpret_cast<float*>(lds + DP::oB);
+  for (int i = tid; i < 2 * DK; i += kDiagThreads) {
+    const int c = i < DK ? core.hk * DK + i : a.Hk * DK + core.hk * DK + (i - DK);
+    const int at = (i & 7) * (2 * kGrp) + (i >> 3);
+    *reinterpret_cast<f4*>(wl + 4 * at) = f4{core.tap(c, 0), core.tap(c, 1), core.tap(c, 2), core.tap(c, 3)};
+    bl[at] = a.bias ? to_f32(static_cast<const Act*>(a.bias)[c]) : 0.f;
   }
-  // decay stage: lane = (token r, channel quarter q4)
-  const int ar = lane >> 2, aq = lane & 3;
-  // pair stage: lane = (channel group cg, column pair cp): columns cp and
-  // 15 - cp, 17 (row, column) steps in all, channels cg * kCw ..
-  const int cg = lane & 7, cp = lane >> 3;
-  for (int i = lane; i < 2 * kBlk * kBlk; i += 64) nm[i] = 0.f;  // N and P: upper parts stay 0
 
+  lds_barrier();                // taps and bias in LDS
   for (int jb = blockIdx.y; jb < nb; jb += gridDim.y) {
     const int tb = jb * kBlk;   // first token of the block
     const int n = T - tb < kBlk ? (T > tb ? T - tb : 0) : kBlk;
-    // ---- loads: raw q / k rows (and the initial window), decays, b ----
-    Row8<Act> raw[kTpl + 3];
-    Row8<Act> dv[kAo];
-    float bv = 0.f;
+    // ---- conv1d + SiLU + L2 norm of q and k, one token per item ----
     {
       const rsrc_t rx = core.x_rows(tb);
+      const rsrc_t rw = core.win_rows();
 #pragma unroll
-      for (int r = 0; r < kTpl + 3; ++r)
-        raw[r].load(rx, core.x_off(tb, tb + kTpl * tg - 3 + r, ch));
-      if (tb == 0) {
-        const rsrc_t rw = core.win_rows();
+      for (int it = 0; it < (kItems + kDiagThreads - 1) / kDiagThreads; ++it) {
+        const int item = tid + it * kDiagThreads;
+        if (item < kItems) {    // whole waves: kItems is a multiple of 64 or all of one wave
+          const int tok = item / (2 * kGrp);
+          Row8<Act> raw[4];
 #pragma unroll
-        for (int r = 0; r < 3; ++r) {
-          Row8<Act> wr;
-          wr.load(rw, core.win_off(kTpl * tg - 3 + r, ch));
-          raw[r].merge(wr);
+          for (int r = 0; r < 4; ++r) {
+            raw[r].load(rx, core.x_off(tb, tb + tok - 3 + r, ch));
+            if (tb == 0) {
+              Row8<Act> wr;
+              wr.load(rw, core.win_off(tok - 3 + r, ch));
+              raw[r].merge(wr);
+            }
+          }
+          float y[8], ss = 0.f;
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const f4 wt = *reinterpret_cast<const f4*>(wl + 4 * (m * 2 * kGrp + co));
+            float v = bl[m * 2 * kGrp + co];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) v = fmaf(wt[jj], raw[jj].get(m), v);
+            v = core.act(v);
+            y[m] = v;
+            ss = fmaf(v, v, ss);
+          }
+          const float sum = group_sum<kGrp>(ss);
+          float sc = a.l2norm ? rsqrtf(sum + a.eps) : 1.0f;
+          if (!isk) sc *= a.q_scale;
+          if (tb + tok >= T) sc = 0.f;
+          float* row = (isk ? yk : yq) + tok * DP::kRow + 8 * oc;
+          *reinterpret_cast<f4*>(row) = f4{y[0], y[1], y[2], y[3]} * sc;
+          *reinterpret_cast<f4*>(row + 4) = f4{y[4], y[5], y[6], y[7]} * sc;
         }
       }
+    }
+    // ---- decays (1 past the sequence) and b ----
+    {
       const int64_t rowe = static_cast<int64_t>(a.Hv) * DK;
       const rsrc_t ra = make_rsrc(static_cast<const Act*>(a.alpha) + (t0 + static_cast<int64_t>(tb)) * rowe,
                                   static_cast<uint32_t>(n * rowe * sizeof(Act)));
+      if (tid < kBlk * (DK / 8)) {
+        const int r = tid / (DK / 8), c = 8 * (tid % (DK / 8));
+        Row8<Act> v;
+        v.load(ra, static_cast<int>(((r * a.Hv + h) * DK + c) * sizeof(Act)));
+        f4 lo4, hi4;
 #pragma unroll
-      for (int o = 0; o < kAo; ++o)
-        dv[o].load(ra, static_cast<int>(((ar * a.Hv + h) * DK + 8 * (4 * o + aq)) * sizeof(Act)));
-      if (lane < n)
-        bv = to_f32(static_cast<const Act*>(a.beta)[(t0 + static_cast<int64_t>(tb) + lane) * a.Hv + h]);
-    }
-    // ---- conv1d + SiLU + L2 norm of q and k ----
-#pragma unroll
-    for (int tt = 0; tt < kTpl; ++tt) {
-      float y[8], ss = 0.f;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        float v = bias[m];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) v = fmaf(wt[m][jj], raw[tt + jj].get(m), v);
-        v = core.act(v);
-        y[m] = v;
-        ss = fmaf(v, v, ss);
-      }
-      const float sum = group_sum<kGrp>(ss);
-      float sc = a.l2norm ? rsqrtf(sum + a.eps) : 1.0f;
-      if (!isk) sc *= a.q_scale;
-      const int tok = kTpl * tg + tt;
-      if (tb + tok >= T) sc = 0.f;
-      float* row = (isk ? yk : yq) + tok * DP::kRow + 8 * oc;
-      *reinterpret_cast<f4*>(row) = f4{y[0], y[1], y[2], y[3]} * sc;
-      *reinterpret_cast<f4*>(row + 4) = f4{y[4], y[5], y[6], y[7]} * sc;
-    }
-    // decays (1 past the sequence) and b
-#pragma unroll
-    for (int o = 0; o < kAo; ++o) {
-      float* dstp = al + ar * DP::kRow + 8 * (4 * o + aq);
-      f4 lo4, hi4;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        lo4[m] = ar < n ? dv[o].get(m) : 1.f;
-        hi4[m] = ar < n ? dv[o].get(m + 4) : 1.f;
-      }
-      *reinterpret_cast<f4*>(dstp) = lo4;
-      *reinterpret_cast<f4*>(dstp + 4) = hi4;
-    }
-    if (lane < kBlk) bt[lane] = bv;
-    lds_barrier();
-    // ---- N and P by products of the decays, 4 channels at a time ----
-    {
-      float accn[17], accp[17];
-#pragma unroll
-      for (int st = 0; st < 17; ++st) accn[st] = accp[st] = 0.f;
-      for (int c4 = 0; c4 < kCw; c4 += 4) {
-        f4 w = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < 17; ++st) {
-          const bool first = st < 16 - cp;
-          const int i = first ? cp : 15 - cp;
-          const int r = first ? cp + st : st - 1;
-          const int off = r * DP::kRow + cg * kCw + c4;
-          const f4 kv = *reinterpret_cast<const f4*>(yk + off);
-          const f4 qv = *reinterpret_cast<const f4*>(yq + off);
-          const f4 av = *reinterpret_cast<const f4*>(al + off);
-          const bool start = r == i;
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            w[m] = start ? kv[m] : w[m] * av[m];
-            accn[st] = fmaf(kv[m], w[m], accn[st]);
-            accp[st] = fmaf(qv[m], w[m], accp[st]);
-          }
+        for (int m = 0; m < 4; ++m) {
+          lo4[m] = r < n ? v.get(m) : 1.f;
+          hi4[m] = r < n ? v.get(m + 4) : 1.f;
         }
+        float* dstp = al + r * DP::kRow + c;
+        *reinterpret_cast<f4*>(dstp) = lo4;
+        *reinterpret_cast<f4*>(dstp + 4) = hi4;
       }
+      if (tid < kBlk)
+        bt[tid] = tid < n ? to_f32(static_cast<const Act*>(a.beta)[(t0 + static_cast<int64_t>(tb) + tid) * a.Hv + h])
+                          : 0.f;
+    }
+    lds_barrier();
+    // ---- N and P by products of the decays; partial sums per wave ----
+    if (wave < kWaves) {
+      float accn[17], accp[17];
+      const bool on = cg < kNg;
+      f4 w = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < 17; ++st) {
-        accn[st] = group_sum<8>(accn[st]);
-        accp[st] = group_sum<8>(accp[st]);
+        const bool first = st < 16 - cp;
+        const int i = first ? cp : 15 - cp;
+        const int r = first ? cp + st : st - 1;
+        const int off = r * DP::kRow + 4 * (on ? cg : 0);
+        const f4 kv = *reinterpret_cast<const f4*>(yk + off);
+        const f4 qv = *reinterpret_cast<const f4*>(yq + off);
+        const f4 av = *reinterpret_cast<const f4*>(al + off);
+        const bool start = r == i;
+        float sn = 0.f, sp = 0.f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          w[m] = start ? kv[m] : w[m] * av[m];
+          sn = fmaf(kv[m], w[m], sn);
+          sp = fmaf(qv[m], w[m], sp);
+        }
+        accn[st] = group_sum<8>(on ? sn : 0.f);
+        accp[st] = group_sum<8>(on ? sp : 0.f);
       }
-      if (cg == 0) {
+      if ((tid & 7) == 0) {
 #pragma unroll
         for (int st = 0; st < 17; ++st) {
-          const bool first = st < 16 - cp;
-          const int i = first ? cp : 15 - cp;
-          const int r = first ? cp + st : st - 1;
-          if (r > i) nm[r * kBlk + i] = bt[r] * accn[st];
-          pm[r * kBlk + i] = accp[st];
+          red[((wave * 2 + 0) * 17 + st) * 8 + cp] = accn[st];
+          red[((wave * 2 + 1) * 17 + st) * 8 + cp] = accp[st];
         }
       }
     }
     lds_barrier();
-    // ---- X = (I + N)^{-1} on MFMA, and the record ----
-    {
+    // ---- totals over the waves -> N (times b_r) and P ----
+    for (int e = tid; e < 2 * 17 * 8; e += kDiagThreads) {
+      const int which = e / (17 * 8), st = (e / 8) % 17, cpe = e % 8;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) v += red[((w * 2 + which) * 17 + st) * 8 + cpe];
+      const bool first = st < 16 - cpe;
+      const int i = first ? cpe : 15 - cpe;
+      const int r = first ? cpe + st : st - 1;
+      if (which == 0) {
+        if (r > i) nm[r * kBlk + i] = bt[r] * v;
+      } else {
+        pm[r * kBlk + i] = v;
+      }
+    }
+    lds_barrier();
+    // ---- X = (I + N)^{-1} on MFMA, and the record (wave 0) ----
+    if (wave == 0) {
       const int lr = lane & 15, lg = lane >> 4;
-      f4 na, nb;
+      f4 na, nbv;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         na[v] = nm[lr * kBlk + 4 * lg + v];
-        nb[v] = nm[(4 * lg + v) * kBlk + lr];
+        nbv[v] = nm[(4 * lg + v) * kBlk + lr];
       }
-      const f4 xv = unit_lower_inverse(na, nb, lr, lg);      // X[lr][4 lg + v]
+      const f4 xv = unit_lower_inverse(na, nbv, lr, lg);      // X[lr][4 lg + v]
       const f4 pv = *reinterpret_cast<const f4*>(pm + lr * kBlk + 4 * lg);
       s4 xh, xl, ph, pl;
       split4(xv, xh, xl);
@@ -938,14 +957,13 @@ __global__ void __launch_bounds__(kThreads, 1) kda_chunk_kernel(PrefillArgs a) {
     }
     for (int c = 0; c < nch; ++c) {
       const bool next = c + 1 < nch;
-      if (cols) {
-        k.columns(c * kC, S, cv, next);
-        const int32_t cs = ckpt_slot(a, s, (c + 1) * kC, k.T);
-        if (cs >= 0) {        // the state after (c + 1) * 64 tokens, to a checkpoint slot
-          float* o = a.ssm + cs * slot_elems + head + static_cast<int64_t>(k.e0 + k.lr) * DK;
+      if (cols) k.columns(c * kC, S, cv, next);
+      const int32_t cs = __builtin_amdgcn_readfirstlane(ckpt_slot(a, s, (c + 1) * kC, k.T));
+      if (cols && cs >= 0) {  // the state after (c + 1) * 64 tokens, to a checkpoint slot
+        const int l = k.lane_now();
+        float* o = a.ssm + cs * slot_elems + head + static_cast<int64_t>(k.e0 + (l & 15)) * DK;
 #pragma unroll
-          for (int d = 0; d < K::kDt; ++d) *reinterpret_cast<f4*>(o + 16 * d + 4 * k.lg) = S[d];
-        }
+        for (int d = 0; d < K::kDt; ++d) *reinterpret_cast<f4*>(o + 16 * d + 4 * (l >> 4)) = S[d];
       }
       lds_barrier();          // chunk c consumed
       if (next) {
@@ -967,7 +985,8 @@ hipError_t launch_kda(const PrefillArgs& a, int max_seqlen, hipStream_t st) {
   // diagonal blocks: grid x strides over the token blocks of a sequence
   const int64_t want = 4 * ((static_cast<int64_t>(max_seqlen) + kC - 1) / kC);
   const int gy = static_cast<int>(want < 1 ? 1 : (want > 65535 ? 65535 : want));
-  hipLaunchKernelGGL((kda_diag_kernel<DK, Act>), dim3(a.N * a.Hv, gy), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((kda_diag_kernel<DK, Act>), dim3(a.N * a.Hv, gy), dim3(kDiagThreads), 0,
+                     st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int bytes = KdaPlan<DK>::kBytes;
