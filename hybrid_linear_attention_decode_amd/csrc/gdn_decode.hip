@@ -272,7 +272,7 @@ struct DecodeCta {
   // unit's copied first-token inputs; act is the unit's activation buffer.
   __device__ __forceinline__ void run(int b, int32_t slot, f4 (&s)[NR][CPL],
                                       const float (&wt)[kMaxW1 + 1], float bias,
-                                      const uint32_t* raw, float* act) const {
+                                      const uint32_t* raw, float* act, bool wait_next) const {
     const int64_t tok0 = static_cast<int64_t>(b) * T;
     const Act* const x_req = static_cast<const Act*>(a.x) + tok0 * C;
     Act* const conv_slot = static_cast<Act*>(a.conv) + static_cast<int64_t>(slot) * W1 * C;
@@ -429,6 +429,11 @@ struct DecodeCta {
     }
 
     if (!spec) {
+      // The next unit's copies are waited for here, before this unit's state
+      // stores are issued: the wait then covers the copies and the few output
+      // and window stores, and the state stores drain while the next unit is
+      // computed.
+      if (wait_next) vm_wait<0>();
       float* dst = state(a.ssm, slot) + lane_off;
 #pragma unroll
       for (int p = 0; p < NR; ++p)
@@ -487,6 +492,7 @@ __global__ void __launch_bounds__(512, RPW <= 16 ? 4 : 2) decode_kernel(const De
   int32_t sl = uniform(slot_tab[0]), sr = uniform(slot_tab[1]);
   if (sl >= 0) cta.copy_unit(cta.b0, sr, stage, raw0);
   f4 s[Cta::NR][Cta::CPL];
+  bool waited = false;  // this unit's copies were waited for inside the previous run
   for (int k = 0; k < mine; ++k) {
     const int b = cta.b0 + k * cta.m;
     uint32_t* const raw = raw0 + (k & 1) * P.raw_len;
@@ -494,7 +500,7 @@ __global__ void __launch_bounds__(512, RPW <= 16 ? 4 : 2) decode_kernel(const De
     // the previous unit's activations before this unit writes them
     float* const act = act0;
     // drain: this unit's copies (and the previous unit's stores) are done
-    vm_wait<0>();
+    if (!waited) vm_wait<0>();
     if (sl >= 0) {
       if (sr >= 0) {
         cta.stage_read(stage, s);
@@ -513,7 +519,9 @@ __global__ void __launch_bounds__(512, RPW <= 16 ? 4 : 2) decode_kernel(const De
       srn = uniform(slot_tab[2 * (k + 1) + 1]);
     }
     if (sn >= 0) cta.copy_unit(b + cta.m, srn, stage, raw0 + ((k + 1) & 1) * P.raw_len);
-    if (sl >= 0) cta.run(b, sl, s, wt, bias, raw, act);
+    const bool early = sl >= 0 && sn >= 0 && !cta.spec;
+    if (sl >= 0) cta.run(b, sl, s, wt, bias, raw, act, early);
+    waited = early;
     sl = sn;
     sr = srn;
   }
