@@ -60,9 +60,20 @@ __device__ __forceinline__ int64_t ws_block(int s, int t0, int jb) {
 // =====================================================================
 constexpr int kDiagThreads = 256;
 
+// Rows of q, k and the decays in LDS: DK floats, the 16-byte chunk index of
+// odd rows XOR 8 (d_k >= 64), so two consecutive rows read at the same
+// chunk fall in opposite halves of the banks.
+template <int DK>
+__device__ __forceinline__ int diag_at(int r, int c) {
+  if constexpr (DK >= 64)
+    return r * DK + (((c >> 2) ^ ((r & 1) << 3)) << 2) + (c & 3);
+  else
+    return r * DK + c;
+}
+
 template <int DK>
 struct DiagPlan {
-  static constexpr int kRow = DK + 4;            // fp32 per row of q, k, a (padded)
+  static constexpr int kRow = DK;                // fp32 per row of q, k, a
   static constexpr int oQ = 0;
   static constexpr int oK = oQ + kBlk * kRow * 4;
   static constexpr int oA = oK + kBlk * kRow * 4;
@@ -169,9 +180,9 @@ __global__ void __launch_bounds__(kDiagThreads, 4) kda_diag_kernel(PrefillArgs a
           float sc = a.l2norm ? rsqrtf(sum + a.eps) : 1.0f;
           if (!isk) sc *= a.q_scale;
           if (tb + tok >= T) sc = 0.f;
-          float* row = (isk ? yk : yq) + tok * DP::kRow + 8 * oc;
-          *reinterpret_cast<f4*>(row) = f4{y[0], y[1], y[2], y[3]} * sc;
-          *reinterpret_cast<f4*>(row + 4) = f4{y[4], y[5], y[6], y[7]} * sc;
+          float* yb = isk ? yk : yq;
+          *reinterpret_cast<f4*>(yb + diag_at<DK>(tok, 8 * oc)) = f4{y[0], y[1], y[2], y[3]} * sc;
+          *reinterpret_cast<f4*>(yb + diag_at<DK>(tok, 8 * oc + 4)) = f4{y[4], y[5], y[6], y[7]} * sc;
         }
       }
     }
@@ -190,26 +201,25 @@ __global__ void __launch_bounds__(kDiagThreads, 4) kda_diag_kernel(PrefillArgs a
           lo4[m] = r < n ? v.get(m) : 1.f;
           hi4[m] = r < n ? v.get(m + 4) : 1.f;
         }
-        float* dstp = al + r * DP::kRow + c;
-        *reinterpret_cast<f4*>(dstp) = lo4;
-        *reinterpret_cast<f4*>(dstp + 4) = hi4;
+        *reinterpret_cast<f4*>(al + diag_at<DK>(r, c)) = lo4;
+        *reinterpret_cast<f4*>(al + diag_at<DK>(r, c + 4)) = hi4;
       }
       if (tid < kBlk)
         bt[tid] = tid < n ? to_f32(static_cast<const Act*>(a.beta)[(t0 + static_cast<int64_t>(tb) + tid) * a.Hv + h])
                           : 0.f;
     }
     lds_barrier();
-    // ---- N and P by products of the decays; partial sums per wave ----
+    // ---- N and P by products of the decays; partial sums per wave, per
+    // step straight to LDS (no accumulator arrays held across the steps) ----
     if (wave < kWaves) {
-      float accn[17], accp[17];
       const bool on = cg < kNg;
       f4 w = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
+#pragma unroll 4
       for (int st = 0; st < 17; ++st) {
         const bool first = st < 16 - cp;
         const int i = first ? cp : 15 - cp;
         const int r = first ? cp + st : st - 1;
-        const int off = r * DP::kRow + 4 * (on ? cg : 0);
+        const int off = diag_at<DK>(r, 4 * (on ? cg : 0));
         const f4 kv = *reinterpret_cast<const f4*>(yk + off);
         const f4 qv = *reinterpret_cast<const f4*>(yq + off);
         const f4 av = *reinterpret_cast<const f4*>(al + off);
@@ -221,14 +231,11 @@ __global__ void __launch_bounds__(kDiagThreads, 4) kda_diag_kernel(PrefillArgs a
           sn = fmaf(kv[m], w[m], sn);
           sp = fmaf(qv[m], w[m], sp);
         }
-        accn[st] = group_sum<8>(on ? sn : 0.f);
-        accp[st] = group_sum<8>(on ? sp : 0.f);
-      }
-      if ((tid & 7) == 0) {
-#pragma unroll
-        for (int st = 0; st < 17; ++st) {
-          red[((wave * 2 + 0) * 17 + st) * 8 + cp] = accn[st];
-          red[((wave * 2 + 1) * 17 + st) * 8 + cp] = accp[st];
+        sn = group_sum<8>(on ? sn : 0.f);
+        sp = group_sum<8>(on ? sp : 0.f);
+        if ((tid & 7) == 0) {
+          red[((wave * 2 + 0) * 17 + st) * 8 + cp] = sn;
+          red[((wave * 2 + 1) * 17 + st) * 8 + cp] = sp;
         }
       }
     }
