@@ -33,6 +33,16 @@ __device__ __forceinline__ bf16 from_exact<bf16>(float v) {
   return bf16{static_cast<uint16_t>(__float_as_uint(v) >> 16)};
 }
 
+// Raw buffer accesses (gfx9 descriptor, no stride): an access whose 32-bit
+// byte offset lies at or past num_records reads zero or is dropped, which
+// masks rows or lanes without branches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+// A byte offset past every descriptor here: its loads read zero.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
 // Streaming (non-temporal) 16-byte accesses for data touched once per call.
 __device__ __forceinline__ f4 ld_stream(const float* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));

@@ -76,14 +76,6 @@ __device__ __forceinline__ s4 ld_tr(const short* p) {
       (__attribute__((address_space(3))) s4*)(const_cast<short*>(p)));
 }
 
-// Raw buffer accesses (gfx9 descriptor, no stride): an access whose 32-bit
-// byte offset lies at or past num_records reads zero or is dropped, which
-// masks rows outside a sequence without branches.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-
 // SiLU with the hardware exp2 / reciprocal.
 __device__ __forceinline__ float silu(float y) {
   return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y));
