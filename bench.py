@@ -534,6 +534,20 @@ def bench_prefill_ckpt(torch, gdn, synth, K=10, W=2):
     return rec, arec
 
 
+def copy_rate(torch, nbytes: int, reps: int = 200) -> float:
+    """GB/s of a plain device copy (torch copy_, read nbytes/2 + write
+    nbytes/2) moving the same byte volume as one decode call: the practical
+    streaming ceiling the decode kernel is set against."""
+    n = nbytes // 2 // 4
+    a = torch.ones(n, device="cuda")
+    b = torch.empty(n, device="cuda")
+    for _ in range(20):
+        b.copy_(a)
+    ms = time_calls(torch, lambda c: b.copy_(a), 0, reps) / reps
+    del a, b
+    return 2 * n * 4 / (ms * 1e-3) / 1e9
+
+
 def copy_calibration(torch, mib: int = 256, reps: int = 5):
     """A plain device copy of known size, for scaling the PMC byte counters."""
     n = mib * (1 << 20) // 4
@@ -608,13 +622,16 @@ def main():
     achieved = nbytes / (ms_step * 1e-3) / 1e9
     tok_s = B / (ms_step * 1e-3)
     log(f"bench: {ms_step * 1e3:.2f} us/call, {tok_s:.0f} tok/s, {achieved:.0f} GB/s")
+    copy_gbs = copy_rate(torch, nbytes)
+    log(f"bench: device copy of the same byte volume: {copy_gbs:.0f} GB/s")
 
     kernel_src = os.path.join(ROOT, "hybrid_linear_attention_decode_amd", "csrc",
                               "gdn_decode.hip")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profile(kernel_src), "kernel": DECODE_KERNEL,
-                "algorithmic_bytes_per_launch": nbytes}
+                "algorithmic_bytes_per_launch": nbytes,
+                "copy_gbps": round(copy_gbs, 1), "frac_of_copy": round(achieved / copy_gbs, 4)}
 
     paths = None
     if args.only == "all":

@@ -352,6 +352,15 @@ struct DecodeCta {
           qq[n] = *reinterpret_cast<const f4*>(ab + col) * qs;
         }
         const float be = bl[hl];
+        // where the rows go after this token: the snapshot of token t (spec),
+        // the slot after the last token (in place), or nowhere yet; each row
+        // is stored as soon as it is updated
+        float* rows_dst = nullptr;
+        if (spec)
+          rows_dst = snap_ssm(t);
+        else if (t == T - 1)
+          rows_dst = state(a.ssm, slot);
+        if (rows_dst) rows_dst += lane_off;
         f4 ga[CPL];
         if constexpr (KDA) {
 #pragma unroll
@@ -391,27 +400,13 @@ struct DecodeCta {
             s[p][n].w = fmaf(u, kk[n].w, s[p][n].w);
           }
           if (lc == 0) out_req[static_cast<uint32_t>(t) * Hv * dv + hl * dv + i] = o;
-        }
-        if (spec) {
-          float* dst = snap_ssm(t);
-          if (dst) {
-            dst += lane_off;
+          if (rows_dst) {
 #pragma unroll
-            for (int p = 0; p < NR; ++p)
-#pragma unroll
-              for (int n = 0; n < CPL; ++n) st_stream(dst + p * DK + 4 * n * LPR, s[p][n]);
+            for (int n = 0; n < CPL; ++n) st_stream(rows_dst + p * DK + 4 * n * LPR, s[p][n]);
           }
         }
       }
       if (t0 + TC < T) lds_barrier();  // the next chunk rewrites this buffer
-    }
-
-    if (!spec) {
-      float* dst = state(a.ssm, slot) + lane_off;
-#pragma unroll
-      for (int p = 0; p < NR; ++p)
-#pragma unroll
-        for (int n = 0; n < CPL; ++n) st_stream(dst + p * DK + 4 * n * LPR, s[p][n]);
     }
   }
 };
