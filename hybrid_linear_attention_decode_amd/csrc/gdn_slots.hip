@@ -16,16 +16,15 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kVecPerThread = 4;
 constexpr int64_t kVecPerBlock = kThreads * kVecPerThread;
+constexpr uint32_t kPieceBytes = kVecPerBlock * 16;
 
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ u4 ld_u4(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u4*>(p));
-}
-__device__ __forceinline__ void st_u4(void* p, u4 v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<u4*>(p));
-}
-
+// Workgroup (x, item): piece x of the item's ssm slot for x < the ssm
+// pieces, else a piece of its conv slot.  Every access is a buffer access
+// over the piece's segment, so the tail of a segment reads zero and drops its
+// stores with no per-vector branch, and all loads of a thread are in flight
+// together.
 template <int MODE>
 __global__ void __launch_bounds__(kThreads) slot_kernel(const SlotArgs a) {
   const int item = blockIdx.y;
@@ -73,26 +72,30 @@ __global__ void __launch_bounds__(kThreads) slot_kernel(const SlotArgs a) {
     dst_conv = static_cast<char*>(a.conv) + dst * conv_bytes;
   }
 
-  const int64_t v0 = static_cast<int64_t>(blockIdx.x) * kVecPerBlock;
-  const int64_t total = a.ssm_vec + a.conv_vec;
+  // this workgroup's piece: segment, byte offset in it, bytes left in it
+  const int64_t ssm_pieces = (ssm_bytes + kPieceBytes - 1) / kPieceBytes;
+  const int64_t x = blockIdx.x;
+  const bool in_ssm = x < ssm_pieces;
+  const int64_t off = (in_ssm ? x : x - ssm_pieces) * kPieceBytes;
+  const int64_t seg = in_ssm ? ssm_bytes : conv_bytes;
+  if (off >= seg) return;
+  const uint32_t n = static_cast<uint32_t>(seg - off < kPieceBytes ? seg - off : kPieceBytes);
+  const rsrc_t d = make_rsrc((in_ssm ? dst_ssm : dst_conv) + off, n);
   u4 buf[kVecPerThread];
+  if (MODE == kSlotZero) {
 #pragma unroll
-  for (int k = 0; k < kVecPerThread; ++k) {
-    const int64_t v = v0 + k * kThreads + threadIdx.x;
-    buf[k] = u4{0u, 0u, 0u, 0u};
-    if (MODE != kSlotZero && v < total)
-      buf[k] = v < a.ssm_vec ? ld_u4(src_ssm + v * 16) : ld_u4(src_conv + (v - a.ssm_vec) * 16);
+    for (int k = 0; k < kVecPerThread; ++k) buf[k] = u4{0u, 0u, 0u, 0u};
+  } else {
+    const rsrc_t s = make_rsrc((in_ssm ? src_ssm : src_conv) + off, n);
+#pragma unroll
+    for (int k = 0; k < kVecPerThread; ++k)
+      buf[k] = __builtin_amdgcn_raw_buffer_load_b128(s, (k * kThreads + threadIdx.x) * 16u, 0,
+                                                     2 /* non-temporal */);
   }
 #pragma unroll
-  for (int k = 0; k < kVecPerThread; ++k) {
-    const int64_t v = v0 + k * kThreads + threadIdx.x;
-    if (v < total) {
-      if (v < a.ssm_vec)
-        st_u4(dst_ssm + v * 16, buf[k]);
-      else
-        st_u4(dst_conv + (v - a.ssm_vec) * 16, buf[k]);
-    }
-  }
+  for (int k = 0; k < kVecPerThread; ++k)
+    __builtin_amdgcn_raw_buffer_store_b128(buf[k], d, (k * kThreads + threadIdx.x) * 16u, 0,
+                                           2 /* non-temporal */);
 }
 
 // Commit by index: request b's working slot becomes the pool slot holding
@@ -123,8 +126,9 @@ hipError_t launch_commit_index(const CommitIndexArgs& a, hipStream_t s) {
 
 hipError_t launch_slots(const SlotArgs& a, SlotMode mode, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
-  const int64_t total = a.ssm_vec + a.conv_vec;
-  const dim3 grid(static_cast<unsigned>((total + kVecPerBlock - 1) / kVecPerBlock), a.n);
+  const int64_t pieces = (a.ssm_vec + kVecPerBlock - 1) / kVecPerBlock +
+                         (a.conv_vec + kVecPerBlock - 1) / kVecPerBlock;
+  const dim3 grid(static_cast<unsigned>(pieces), a.n);
   switch (mode) {
     case kSlotCopy:
       hipLaunchKernelGGL(slot_kernel<kSlotCopy>, grid, dim3(kThreads), 0, s, a);
