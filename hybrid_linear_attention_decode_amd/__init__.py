@@ -26,6 +26,7 @@ GDN_ERR_BAD_DTYPE = 3
 GDN_ERR_UNSUPPORTED = 4
 GDN_ERR_WORKSPACE = 5
 GDN_ERR_LAUNCH = 6
+GDN_ERR_PRECONDITION = 7
 
 GDN_F32, GDN_BF16 = 0, 1
 GDN_GATE_SCALAR, GDN_GATE_CHANNEL = 0, 1

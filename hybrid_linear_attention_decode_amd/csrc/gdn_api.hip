@@ -5,6 +5,10 @@
 #include "gdn_internal.hpp"
 
 #include <stdint.h>
+#include <stdlib.h>
+
+#include <algorithm>
+#include <vector>
 
 namespace {
 
@@ -55,6 +59,70 @@ gdn_status check_spec(const gdn_layer* L, const gdn_spec_cache* S) {
 
 gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH; }
 
+// ---- Device-side preconditions, checked only when GDN_DEBUG is set (and not
+// "0") in the environment at the time of the call: the index arrays are
+// copied to the host on the call's stream (which waits for it) and checked
+// before anything is enqueued.
+
+bool debug_checks() {
+  const char* e = getenv("GDN_DEBUG");
+  return e && e[0] && !(e[0] == '0' && e[1] == 0);
+}
+
+// n int32 values of a device array (an empty vector for n <= 0 or no array);
+// false when the copy fails.
+bool fetch(const int32_t* d, int64_t n, hipStream_t s, std::vector<int32_t>& h) {
+  h.clear();
+  if (!d || n <= 0) return true;
+  h.resize(static_cast<size_t>(n));
+  if (hipMemcpyAsync(h.data(), d, static_cast<size_t>(n) * sizeof(int32_t),
+                     hipMemcpyDeviceToHost, s) != hipSuccess)
+    return false;
+  return hipStreamSynchronize(s) == hipSuccess;
+}
+
+bool in_pool(int32_t v, int64_t num_slots) { return v >= 0 && v < num_slots; }
+
+// The in-pool entries of a, sorted; false if two are equal.
+bool distinct(const std::vector<int32_t>& a, int64_t num_slots, std::vector<int32_t>& sorted) {
+  sorted.clear();
+  for (int32_t v : a)
+    if (in_pool(v, num_slots)) sorted.push_back(v);
+  std::sort(sorted.begin(), sorted.end());
+  return std::adjacent_find(sorted.begin(), sorted.end()) == sorted.end();
+}
+bool contains(const std::vector<int32_t>& sorted, int32_t v) {
+  return std::binary_search(sorted.begin(), sorted.end(), v);
+}
+
+// Rows i of a batch write slot dst[i] (skipped when out of the pool) and read
+// slot src[i] (the same when src is empty).  Writes must not collide, and no
+// row may read a slot that another row writes.
+gdn_status check_rows(const std::vector<int32_t>& dst, const std::vector<int32_t>& src,
+                      int64_t num_slots, std::vector<int32_t>& written) {
+  if (!distinct(dst, num_slots, written)) return GDN_ERR_PRECONDITION;
+  for (size_t i = 0; i < src.size(); ++i) {
+    if (!in_pool(dst[i], num_slots) || !in_pool(src[i], num_slots) || src[i] == dst[i]) continue;
+    if (contains(written, src[i])) return GDN_ERR_PRECONDITION;
+  }
+  return GDN_OK;
+}
+
+// Extra targets (snapshot or checkpoint slots, -1 = none): distinct, and none
+// of them a slot that the rows read or write.
+gdn_status check_targets(const std::vector<int32_t>& t, const std::vector<int32_t>& dst,
+                         const std::vector<int32_t>& src, int64_t num_slots) {
+  std::vector<int32_t> ts;
+  if (!distinct(t, num_slots, ts)) return GDN_ERR_PRECONDITION;
+  for (size_t i = 0; i < dst.size(); ++i) {
+    if (!in_pool(dst[i], num_slots)) continue;
+    if (contains(ts, dst[i])) return GDN_ERR_PRECONDITION;
+    if (!src.empty() && in_pool(src[i], num_slots) && contains(ts, src[i]))
+      return GDN_ERR_PRECONDITION;
+  }
+  return GDN_OK;
+}
+
 SlotArgs slot_args(const gdn_layer* L, const gdn_pool* P, int32_t n) {
   SlotArgs a{};
   a.n = n;
@@ -83,6 +151,11 @@ gdn_status pack_common(const gdn_layer* L, const gdn_pool* P, const int32_t* idx
   if (!idx || !buffer) return GDN_ERR_NULL_ARG;
   if (!aligned16(buffer)) return GDN_ERR_BAD_SHAPE;
   if (buffer_bytes / static_cast<size_t>(n) < slot_bytes(L)) return GDN_ERR_BAD_SHAPE;
+  if (mode == gdn::kSlotUnpack && debug_checks()) {
+    std::vector<int32_t> d, written;
+    if (!fetch(idx, n, static_cast<hipStream_t>(stream), d)) return GDN_ERR_LAUNCH;
+    if (!distinct(d, P->num_slots, written)) return GDN_ERR_PRECONDITION;
+  }
   SlotArgs a = slot_args(L, P, n);
   a.a = idx;
   a.buf = const_cast<void*>(buffer);
@@ -102,6 +175,8 @@ const char* gdn_status_string(gdn_status s) {
     case GDN_ERR_UNSUPPORTED: return "shape not supported by the built kernels";
     case GDN_ERR_WORKSPACE: return "prefill workspace missing or too small";
     case GDN_ERR_LAUNCH: return "HIP kernel launch failed";
+    case GDN_ERR_PRECONDITION:
+      return "device-side precondition failed (colliding slots or bad cu_seqlens; GDN_DEBUG)";
   }
   return "unknown status";
 }
@@ -125,6 +200,20 @@ gdn_status gdn_decode_step(const gdn_layer* L, const gdn_pool* P, const int32_t*
     return GDN_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(B) * L->n_k_heads > INT32_MAX) return GDN_ERR_BAD_SHAPE;
   if (B == 0) return GDN_OK;
+  if (debug_checks()) {
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    std::vector<int32_t> d, src, tab, written;
+    if (!fetch(idx, B, hs, d) || !fetch(init_slot, B, hs, src)) return GDN_ERR_LAUNCH;
+    if ((st = check_rows(d, src, P->num_slots, written)) != GDN_OK) return st;
+    if (spec && spec->slots) {
+      if (!fetch(spec->slots, static_cast<int64_t>(B) * spec->t_max, hs, tab)) return GDN_ERR_LAUNCH;
+      std::vector<int32_t> used;  // the snapshot slots of tokens 0..T-1
+      for (int32_t b = 0; b < B; ++b)
+        if (in_pool(d[b], P->num_slots))
+          for (int32_t t = 0; t < T; ++t) used.push_back(tab[static_cast<size_t>(b) * spec->t_max + t]);
+      if ((st = check_targets(used, d, src, P->num_slots)) != GDN_OK) return st;
+    }
+  }
 
   DecodeArgs a{};
   a.Hk = L->n_k_heads;
@@ -169,6 +258,11 @@ gdn_status gdn_spec_decode_commit(const gdn_layer* L, const gdn_pool* P, const i
   if ((st = check_spec(L, spec)) != GDN_OK) return st;
   if (spec->slots) return GDN_ERR_BAD_SHAPE;  // pool-slot snapshots commit by index
   if (B < 0 || B > 65535) return GDN_ERR_BAD_SHAPE;
+  if (debug_checks() && B > 0) {
+    std::vector<int32_t> d, written;
+    if (!fetch(idx, B, static_cast<hipStream_t>(stream), d)) return GDN_ERR_LAUNCH;
+    if (!distinct(d, P->num_slots, written)) return GDN_ERR_PRECONDITION;
+  }
   SlotArgs a = slot_args(L, P, B);
   a.a = idx;
   a.b = accepted_len;
@@ -202,6 +296,14 @@ gdn_status gdn_slot_copy(const gdn_layer* L, const gdn_pool* P, const int32_t* s
   if ((st = check_pool(L, P)) != GDN_OK) return st;
   if (n < 0 || n > 65535) return GDN_ERR_BAD_SHAPE;
   if (n > 0 && (!src || !dst)) return GDN_ERR_NULL_ARG;
+  if (debug_checks() && n > 0) {
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    std::vector<int32_t> d, sv, written;
+    if (!fetch(dst, n, hs, d) || !fetch(src, n, hs, sv)) return GDN_ERR_LAUNCH;
+    for (int32_t i = 0; i < n; ++i)  // a row with a source outside the pool is skipped
+      if (!in_pool(sv[i], P->num_slots)) d[i] = -1;
+    if ((st = check_rows(d, sv, P->num_slots, written)) != GDN_OK) return st;
+  }
   SlotArgs a = slot_args(L, P, n);
   a.a = src;
   a.b = dst;
@@ -270,6 +372,33 @@ gdn_status gdn_prefill_chunked(const gdn_layer* L, const gdn_pool* P, const int3
     return GDN_ERR_NULL_ARG;
   if (in->x && !aligned16(in->x)) return GDN_ERR_BAD_SHAPE;
   if (out && !aligned16(out)) return GDN_ERR_BAD_SHAPE;
+  if (debug_checks()) {
+    // cu_seqlens: 0, non-decreasing, ending at total_tokens, no sequence
+    // longer than max_seqlen; destination writes distinct; no sequence reading
+    // a slot another one writes; used checkpoint slots distinct and apart
+    // from every destination and source
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    std::vector<int32_t> cu, d, src, tab, written;
+    if (!fetch(cu_seqlens, static_cast<int64_t>(N) + 1, hs, cu) || !fetch(dst, N, hs, d) ||
+        !fetch(init_slot, N, hs, src))
+      return GDN_ERR_LAUNCH;
+    if (cu[0] != 0 || cu[N] != total_tokens) return GDN_ERR_PRECONDITION;
+    for (int32_t i = 0; i < N; ++i)
+      if (cu[i + 1] < cu[i] || cu[i + 1] - cu[i] > max_seqlen) return GDN_ERR_PRECONDITION;
+    if ((st = check_rows(d, src, P->num_slots, written)) != GDN_OK) return st;
+    if (ckpt && ckpt->per_seq > 0) {
+      if (!fetch(ckpt->slots, static_cast<int64_t>(N) * ckpt->per_seq, hs, tab))
+        return GDN_ERR_LAUNCH;
+      std::vector<int32_t> used;  // checkpoints that fall inside their sequence
+      for (int32_t i = 0; i < N; ++i) {
+        if (!in_pool(d[i], P->num_slots)) continue;
+        const int32_t n_ck = std::min((cu[i + 1] - cu[i]) / ckpt->every, ckpt->per_seq);
+        for (int32_t k = 0; k < n_ck; ++k)
+          used.push_back(tab[static_cast<size_t>(i) * ckpt->per_seq + k]);
+      }
+      if ((st = check_targets(used, d, src, P->num_slots)) != GDN_OK) return st;
+    }
+  }
   const bool kda = L->gate == GDN_GATE_CHANNEL;
   if (kda && total_tokens > 0) {
     if (in->alpha && !aligned16(in->alpha)) return GDN_ERR_BAD_SHAPE;

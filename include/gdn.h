@@ -44,7 +44,14 @@
  *   - Device-resident indices are not range-checked on the host.  A slot index
  *     < 0 or >= num_slots skips that row (no read, no write, output untouched);
  *     an accepted length outside [0, t_max] is treated as 0.  Destination slots
- *     of one call must be distinct (two rows updating one slot race).
+ *     of one call must be distinct (two rows updating one slot race), no row
+ *     may read a slot that another row of the call writes, and snapshot /
+ *     checkpoint slots must be distinct and apart from both.
+ *   - With the environment variable GDN_DEBUG set (and not "0") at the time of
+ *     a call, the call first copies its device index arrays (and cu_seqlens)
+ *     to the host on `stream`, waiting for the stream, and returns
+ *     GDN_ERR_PRECONDITION with nothing enqueued if any of the rules above or
+ *     the cu_seqlens contract is broken.  For debugging only: it synchronises.
  *   - `out` must not alias any input or either pool.
  *
  * Layouts (row-major; act = gdn_layer.act_dtype, C = 2 H_k d_k + H_v d_v):
@@ -76,7 +83,8 @@ typedef enum {
   GDN_ERR_BAD_DTYPE = 3,   /* unknown dtype / gate enum */
   GDN_ERR_UNSUPPORTED = 4, /* valid but not built (e.g. d_k not in {16,32,64,128}) */
   GDN_ERR_WORKSPACE = 5,   /* prefill workspace missing or too small */
-  GDN_ERR_LAUNCH = 6       /* the HIP launch failed */
+  GDN_ERR_LAUNCH = 6,      /* the HIP launch failed */
+  GDN_ERR_PRECONDITION = 7 /* a device-side precondition failed (only with GDN_DEBUG set) */
 } gdn_status;
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;

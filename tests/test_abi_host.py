@@ -28,8 +28,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in range(7):
+    for st in range(8):
         assert gdn.gdn_status_string(st)
+    assert "precondition" in gdn.gdn_status_string(gdn.GDN_ERR_PRECONDITION)
     assert gdn.gdn_status_string(99) == "unknown status"
 
 

@@ -283,6 +283,31 @@ def test_other_shapes_against_oracle(kw):
     assert rel_err(host(d.ssm)[live], s64[live]) <= STATE_TOL_16
 
 
+@pytest.mark.parametrize("shape,B", [(synth.TINY, 9), (synth.Shape(4, 8, 32, 32, 4, "scalar", "bf16"), 5)])
+def test_unit_counts_not_a_multiple_of_eight(shape, B):
+    """B * H_k = 18 and 20 units: the workgroup -> unit order deals blocks of
+    units to the XCDs and leaves the remainder in place; every unit is run
+    exactly once (outputs and states against the oracle, every slot outside
+    the batch bit-identical)."""
+    torch = _torch()
+    slots = 2 * B + 3
+    case = synth.decode_case(shape, B=B, T=1, num_slots=slots, n_calls=3, seed=12)
+    g, o = layers(shape)
+    d = DevCase(case)
+    before = bits(d.ssm), bits(d.conv)
+    outs = [d.call(g, c) for c in range(3)]
+    torch.cuda.synchronize()
+    s64, c64 = shadow(case.pool)
+    refs = run_oracle(o, case, s64, c64, range(3))
+    for c in range(3):
+        assert rel_err(host(outs[c]), refs[c]) <= OUT_TOL
+    used = np.unique(case.indices[:3])
+    assert rel_err(host(d.ssm)[used], s64[used]) <= STATE_TOL_16
+    others = np.setdiff1d(np.arange(slots), used)
+    np.testing.assert_array_equal(bits(d.ssm)[others], before[0][others])
+    np.testing.assert_array_equal(bits(d.conv)[others], before[1][others])
+
+
 def test_kda_decode_with_slot_prep():
     """KDA-style decode (per-channel gate), 32/32 heads, d=128: a quarter of the
     requests on zeroed fresh slots, a quarter CoW from checkpoints, then decode;
