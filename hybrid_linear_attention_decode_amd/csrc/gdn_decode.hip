@@ -7,10 +7,11 @@
 // ordering exists.
 //
 // Schedule.  The grid is B * H_k workgroups, one per unit, each small in LDS
-// (the activations of a few tokens) and in registers, so several are
-// resident on a CU at once and the dispatcher hands the next unit to
-// whichever CU frees a slot first: one workgroup's state stores drain while
-// another's loads stream in, and CUs on faster memory paths take more units.
+// (the activations of a few tokens) and in registers, and the dispatcher
+// hands the next unit to whichever CU frees a slot first.  Units of up to
+// 64 KiB of state run two per CU (one's stores drain while the other's loads
+// stream in); larger ones one per CU, which keeps fewer requests queued at
+// HBM and measures faster.
 // Within a unit the first-token inputs (x, conv window, taps, gates, betas)
 // are loaded first and the state rows, straight into registers, once they
 // are in: the conv and the norms run while the state streams in.
@@ -45,6 +46,7 @@ namespace {
 constexpr int kMaxW1 = 3;     // conv_width <= 4
 constexpr int kBatch = 2;     // later tokens whose x are loaded together
 constexpr int kMaxChunk = 8;  // tokens whose activations sit in LDS at once
+constexpr size_t kHalfLds = 80 * 1024;  // half the LDS of a gfx950 CU
 
 // Lane layout of a state row of d_k fp32: LPR lanes, each holding CPL 16-byte
 // chunks (chunk n*LPR + lc in lane lc); one instruction of a wave covers
@@ -411,8 +413,8 @@ struct DecodeCta {
   }
 };
 
-// At most 128 registers per lane: four waves per SIMD, two 8-wave units per
-// CU.
+// At most 128 registers per lane: room for two 8-wave workgroups per CU
+// (units of 128 KiB of state run one per CU, see launch_decode).
 template <int DK, int RPW, typename Act, bool KDA>
 __global__ void __launch_bounds__(512, 4) decode_kernel(const DecodeArgs a) {
   using Cta = DecodeCta<DK, RPW, Act, KDA>;
@@ -526,7 +528,13 @@ hipError_t launch_decode(const DecodeArgs& args, int dk, int act_bf16, int kda, 
   if (units < 1 || units > INT32_MAX) return hipErrorInvalidValue;
   DecodeArgs a = args;
   a.tchunk = args.T < kMaxChunk ? args.T : kMaxChunk;
-  const size_t lds = decode_lds_bytes(dk, args.G, args.dv, kda, a.tchunk);
+  // Units of 128 KiB of state or more run one workgroup per CU, reserved
+  // through LDS: two such units per CU queue more requests than HBM serves
+  // well (Qwen3.5 shape, B=64: 50.5 us against 51.9 us with two); 64 KiB
+  // units are fastest two per CU (51.9 us against 54.9 us with one).
+  const int64_t unit_bytes = static_cast<int64_t>(args.G) * args.dv * dk * 4;
+  size_t lds = decode_lds_bytes(dk, args.G, args.dv, kda, a.tchunk);
+  if (unit_bytes >= 128 * 1024 && lds < kHalfLds + 16) lds = kHalfLds + 16;
   const dim3 grid(static_cast<unsigned>(units));
   if (act_bf16)
     return kda ? launch_dk<bf16, true>(a, dk, rpw, grid, lds, s)
