@@ -360,3 +360,27 @@ def test_64bit_offsets_top_slots():
     assert rel_err(host(out), ref) <= OUT_TOL
     assert rel_err(host(ssm[dev(top).long()]), s64) <= OUT_TOL
     assert float(ssm[:1024].abs().sum()) == 0.0 and float(ssm[1025:1099].abs().sum()) == 0.0
+
+
+def test_max_batch_tiny():
+    """B = 65535 (the largest the ABI takes) on the tiny shape, one token,
+    every request on its own slot of a 65536-slot pool; all outputs and
+    states against the oracle, the one unused slot untouched."""
+    torch = _torch()
+    B, slots = 65535, 65536
+    case = synth.decode_case(synth.TINY, B=B, T=1, num_slots=slots, n_calls=1, seed=13)
+    g, o = layers(synth.TINY)
+    d = DevCase(case)
+    before = bits(d.ssm), bits(d.conv)
+    out = d.call(g, 0)
+    torch.cuda.synchronize()
+    s64, c64 = shadow(case.pool)
+    ref = run_oracle(o, case, s64, c64, range(1))[0]
+    assert rel_err(host(out), ref) <= OUT_TOL
+    used = case.indices[0]
+    assert rel_err(host(d.ssm)[used], s64[used]) <= STATE_TOL_16
+    np.testing.assert_array_equal(host(d.conv)[used], c64[used].astype(np.float32))
+    spare = np.setdiff1d(np.arange(slots), used)
+    assert spare.size == 1
+    np.testing.assert_array_equal(bits(d.ssm)[spare], before[0][spare])
+

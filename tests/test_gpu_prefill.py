@@ -201,3 +201,14 @@ def test_unsupported_shapes_raise():
                                 dev(case.init_slot), dev(case.cu_seqlens), 64, dev(case.x),
                                 dev(case.alpha), dev(case.beta), dev(case.conv_w), chunk=32)
     torch.cuda.synchronize()
+
+
+def test_max_sequences_short():
+    """N = 65535 sequences (the largest the ABI takes) of 1-3 tokens each,
+    half from zero and half copy-on-write; every output, final state and
+    window against the oracle, every other slot untouched."""
+    shape = synth.Shape(1, 1, 32, 32, 4, "scalar", "bf16")
+    lens = (np.arange(65535) % 3 + 1).tolist()
+    r = run_case(shape, lens, num_slots=2 * 65535, seed=14)
+    print("65535 sequences: out %.2e state %.2e" % check(r))
+
