@@ -34,8 +34,12 @@
  *
  * Conventions for every entry point.
  *   - Pointers are DEVICE pointers unless marked (host).  The caller owns and
- *     allocates every buffer; the library allocates nothing, keeps no global
- *     state and is safe to call from several host threads.
+ *     allocates every buffer; the library allocates nothing and is safe to
+ *     call from several host threads.  Its only state between calls is one
+ *     4-byte work counter per (device, stream) that has run gdn_decode_step
+ *     (at most 64 per device, in the library's own device memory): calls on
+ *     one stream use it in stream order and leave it at zero.  A call on a
+ *     stream under graph capture, or on a 65th stream, uses none.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *     default stream).  Returning GDN_OK means "validated and enqueued".
  *   - Host-checkable errors (NULL pointers, shapes, dtypes, unsupported sizes,

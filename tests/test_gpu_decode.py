@@ -384,3 +384,65 @@ def test_max_batch_tiny():
     assert spare.size == 1
     np.testing.assert_array_equal(bits(d.ssm)[spare], before[0][spare])
 
+
+def test_graph_capture_and_two_streams():
+    """A decode call captured into a graph (its units then all fixed, no
+    ticket) replays bit-identical to eager calls, three replays with eager
+    work between them; and two streams decoding disjoint slots at once (each
+    with its own ticket counter) give what one stream gives one call after
+    the other."""
+    torch = _torch()
+    shape = synth.QWEN35
+    B = 64
+    case = synth.decode_case(shape, B=2 * B, T=1, num_slots=256, n_calls=3, seed=15,
+                             rotate=False)
+    g, _ = layers(shape)
+    idx = dev(case.indices[0])
+    ins = [(dev(case.x[c]), dev(case.alpha[c]), dev(case.beta[c])) for c in range(3)]
+    w = dev(case.conv_w)
+
+    # eager reference: one stream, calls in order
+    ref_ssm, ref_conv = dev(case.pool.ssm), dev(case.pool.conv)
+    ref_out = [gdn.gdn_decode_step(g, ref_ssm, ref_conv, idx, *ins[c], w) for c in range(3)]
+    torch.cuda.synchronize()
+    ref_bits = bits(ref_ssm), bits(ref_conv)
+
+    # graph: static input buffers refilled before every replay
+    ssm, conv = dev(case.pool.ssm), dev(case.pool.conv)
+    xs, als, bes = (t.clone() for t in ins[0])
+    out = torch.empty_like(ref_out[0])
+    gdn.gdn_decode_step(g, ssm, conv, idx, xs, als, bes, w, out=out)   # warm-up call ...
+    torch.cuda.synchronize()
+    ssm.copy_(dev(case.pool.ssm)); conv.copy_(dev(case.pool.conv))    # ... undone
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gdn.gdn_decode_step(g, ssm, conv, idx, xs, als, bes, w, out=out)
+    torch.cuda.synchronize()
+    for c in range(3):
+        xs.copy_(ins[c][0]); als.copy_(ins[c][1]); bes.copy_(ins[c][2])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(out), bits(ref_out[c]))
+    np.testing.assert_array_equal(bits(ssm), ref_bits[0])
+    np.testing.assert_array_equal(bits(conv), ref_bits[1])
+
+    # two streams, disjoint halves of the batch, launched back to back
+    ssm2, conv2 = dev(case.pool.ssm), dev(case.pool.conv)
+    halves = [(slice(0, B), torch.cuda.Stream()), (slice(B, 2 * B), torch.cuda.Stream())]
+    parts = [[(idx[h].contiguous(), *(t[h].contiguous() for t in ins[c])) for c in range(3)]
+             for h, _ in halves]
+    outs = [[None] * 3 for _ in halves]
+    torch.cuda.synchronize()
+    for c in range(3):
+        for k, (h, st) in enumerate(halves):
+            with torch.cuda.stream(st):
+                outs[k][c] = gdn.gdn_decode_step(g, ssm2, conv2, *parts[k][c], w)
+    torch.cuda.synchronize()
+    for c in range(3):
+        got = torch.cat([outs[0][c], outs[1][c]])
+        np.testing.assert_array_equal(bits(got), bits(ref_out[c]))
+    np.testing.assert_array_equal(bits(ssm2), ref_bits[0])
+    np.testing.assert_array_equal(bits(conv2), ref_bits[1])
+
