@@ -184,17 +184,19 @@ def cpu_baseline(synth, shape, bench: DecodeBench, budget_s: float):
     x, al, be = bench.inputs_host
     t0 = time.perf_counter()
     n = 0
+    calls = bench.idx_host.shape[0]
     while True:
         i = n % bench.n_inputs
-        oracle.decode(o, s64, c64, bench.idx_host[n], x[i], al[i], be[i], bench.w_host,
+        oracle.decode(o, s64, c64, bench.idx_host[n % calls], x[i], al[i], be[i], bench.w_host,
                       nthreads=nthreads)
         n += 1
         dt = time.perf_counter() - t0
-        if dt >= budget_s or n >= bench.idx_host.shape[0]:
+        if dt >= budget_s:
             break
     return {"value": round(bench.B * n / dt, 2), "unit": "tokens/s", "cores": nthreads,
             "kind": "oracle",
-            "sample": f"{n} consecutive B={bench.B} decode calls of the headline workload "
+            "sample": f"{n} consecutive B={bench.B} decode calls of the headline workload, "
+                      f"its index stream repeated past {calls} calls "
                       f"(fp64 oracle, {nthreads} threads, {dt:.1f} s)"}
 
 
