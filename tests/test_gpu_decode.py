@@ -82,16 +82,19 @@ def test_tiny_multi_token_call_equals_single_steps_bitwise():
     np.testing.assert_array_equal(bits(a.conv), bits(b.conv))
 
 
-@pytest.mark.parametrize("n_calls", [1000])
-def test_qwen35_b16_full_run(n_calls):
-    """Qwen3.5-shaped layer: B=16, 16/32 heads, d=128, 8192 channels, bf16
-    inputs, fp32 state, pool 256 with rotating distinct indices, T=1, every
-    output of every call against the oracle, then the final pool."""
+@pytest.mark.parametrize("B,slots,n_calls,seed", [(16, 256, 1000, 1), (64, 1024, 40, 5)],
+                         ids=["b16_1000_calls", "b64_headline"])
+def test_qwen35_full_run(B, slots, n_calls, seed):
+    """Qwen3.5-shaped layer, 16/32 heads, d=128, 8192 channels, bf16 inputs,
+    fp32 state, rotating distinct indices, T=1, in the launch configuration
+    the bench times: B=16 over a 256-slot pool for 1000 calls, and the
+    headline B=64 over a 1024-slot pool (seed of the bench) for 40 calls.
+    Every output of every call against the oracle, then the final pool."""
     torch = _torch()
-    case = synth.decode_case(synth.QWEN35, B=16, T=1, num_slots=256, n_calls=n_calls, seed=1)
+    case = synth.decode_case(synth.QWEN35, B=B, T=1, num_slots=slots, n_calls=n_calls, seed=seed)
     g, o = layers(synth.QWEN35)
     d = DevCase(case)
-    out = torch.empty((n_calls, 16, 1, 32, 128), dtype=torch.float32, device="cuda")
+    out = torch.empty((n_calls, B, 1, 32, 128), dtype=torch.float32, device="cuda")
     x, al, be, ix = dev(case.x), dev(case.alpha), dev(case.beta), dev(case.indices)
     for c in range(n_calls):
         gdn.gdn_decode_step(g, d.ssm, d.conv, ix[c], x[c], al[c], be[c], d.w, out=out[c])
@@ -103,7 +106,7 @@ def test_qwen35_b16_full_run(n_calls):
         ref = oracle.decode(o, s64, c64, case.indices[c], case.x[c], case.alpha[c],
                             case.beta[c], case.conv_w)
         worst = max(worst, rel_err(got[c], ref))
-    print(f"qwen35 B=16 x {n_calls} calls: worst max|do|/max|o| = {worst:.3e}")
+    print(f"qwen35 B={B} x {n_calls} calls: worst max|do|/max|o| = {worst:.3e}")
     assert worst <= OUT_TOL
     live = np.unique(case.indices)
     assert rel_err(host(d.ssm)[live], s64[live]) <= OUT_TOL
