@@ -87,44 +87,9 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
-// Copies global -> LDS without registers (gfx950 global_load_lds).  The LDS
-// address is wave-uniform; each active lane writes at lds + 4*lane (SIZE 2
-// or 4: one zero-extended dword per lane) or lds + 16*lane (SIZE 16).
-// Counted by the vector-memory counter like a load; the compiler does not
-// order later LDS reads after it -- see vm_wait.
-#define GDN_LDS_DMA(SRC, LDS, SIZE, AUX)                                                 \
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(SRC), \
-                                   (__attribute__((address_space(3))) void*)(LDS), SIZE, 0, AUX)
-template <int SIZE>
-__device__ __forceinline__ void lds_dma(const void* src, void* lds);
-template <>
-__device__ __forceinline__ void lds_dma<2>(const void* src, void* lds) {
-  GDN_LDS_DMA(src, lds, 2, 0);
-}
-template <>
-__device__ __forceinline__ void lds_dma<4>(const void* src, void* lds) {
-  GDN_LDS_DMA(src, lds, 4, 0);
-}
-template <>
-__device__ __forceinline__ void lds_dma<16>(const void* src, void* lds) {
-  GDN_LDS_DMA(src, lds, 16, 2 /* non-temporal */);
-}
-#undef GDN_LDS_DMA
-__device__ __forceinline__ void lds_dma16(const float* src, float* lds) { lds_dma<16>(src, lds); }
-
-// Wait until at most N vector-memory operations of this wave are in flight.
-// It also keeps the compiler from moving memory accesses across it.
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-// Wait for this wave's LDS operations.
-__device__ __forceinline__ void lgkm_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
 // Workgroup barrier for LDS traffic only: this wave's LDS accesses complete,
 // then all waves meet.  Unlike __syncthreads() it does not wait for global
-// memory (or the LDS copies in flight), which keep streaming across it.
+// memory, which keeps streaming across it.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
