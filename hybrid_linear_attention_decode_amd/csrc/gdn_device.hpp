@@ -62,6 +62,12 @@ constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within 8 lanes
 
 constexpr int kDppRowMirror = 0x140;  // lane i <- lane 15-i within 16 lanes
 
+// Lane i <- lane i - N of its row of 16 lanes; lanes without one read zero.
+template <int N>
+__device__ __forceinline__ float row_shr(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + N, 0xF, 0xF, true));
+}
+
 // Sum over aligned groups of N lanes (N = 4, 8 or 16); every lane of the group
 // ends with the same bits (each step adds a commuted pair).
 template <int N>

@@ -1,7 +1,7 @@
 // gdn_prefill.hip -- chunked prefill of the gated delta rule on gfx950.
 //
 // The recurrence S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,
-// o_t = S_t q_t is evaluated 64 tokens at a time in its WY / UT-transform
+// o_t = S_t q_t is evaluated 32 tokens at a time in its WY / UT-transform
 // form (Yang et al., "Parallelizing Linear Transformers with the Delta Rule
 // over Sequence Length", 2024, sec. 3; with the scalar decay of "Gated Delta
 // Networks", 2025, sec. 3).  For a chunk with rows K, Q (normalised keys and
@@ -10,28 +10,29 @@
 //   (I + A) U = diag(b) (V - diag(e^g) K S0^T)    (U: the chunk's updates)
 //   O = diag(e^g) Q S0^T + P U,  P_ri = e^{g_r - g_i} q_r . k_i   (i <= r)
 //   S = e^{g_c} S0 + U^T diag(e^{g_c - g}) K       (g_c: the chunk's last g)
-// The triangular system is solved blockwise: the four 16x16 diagonal blocks
-// of (I + A) are inverted by forward substitution in fp32, and U is formed
-// block row by block row, U_b = X_bb (b_b R_b - sum_{j<b} A_bj U_j).
+// The triangular system is solved blockwise: the two 16x16 diagonal blocks
+// of (I + A) are inverted in fp32, and U is formed block row by block row,
+// U_b = X_bb (b_b R_b - sum_{j<b} A_bj U_j).
 //
 // Work split.  Rows of S are independent through the whole recurrence (row
 // i of S, U and O depend only on row i of S0), so a workgroup owns one
 // (sequence, value head, 64 value columns) and walks that sequence's chunks
 // in order, its 64 x d_k slice of S^T held in MFMA accumulators across
-// chunks.  Its 8 waves form a two-stage pipeline:
-//   producers (waves 0-3), one chunk ahead: raw q / k inputs prefetched a
-//     further chunk ahead, conv1d + SiLU + L2 norm (8 channels x 8 tokens
-//     per thread) into registers as bf16 (hi, lo) pairs, gates and log-decay
-//     prefix sums;
-//   consumers (waves 4-7), 16 value columns each: the value conv, K S0^T,
-//     Q S0^T, U, O and the state update of the current chunk.
-// Between chunks all 8 waves meet: producers store the next chunk's K, Q
-// and gates, then every wave takes some of the 20 lower 16x16 tiles of
-// K K^T and Q K^T (-> A and P); the four waves holding a diagonal tile of
-// K K^T also invert that block of (I + A) from the tile's registers:
-// with N strictly lower triangular, (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)
-// (I + N^8), and K K^T is symmetric, so both operand layouts of N come from
-// the one accumulator tile.
+// chunks.  Its 8 waves form a two-stage pipeline over double-buffered LDS
+// (every per-chunk plane has two copies, chunks alternate between them):
+//   producers (waves 0-3) build chunk c + 1 while chunk c is consumed:
+//     raw inputs prefetched a further chunk ahead; conv1d + SiLU + L2 norm
+//     (8 channels x 4 tokens per thread) into bf16 (hi, lo) pairs; the value
+//     conv; gates and log-decay prefix sums; then, after the mid-chunk
+//     barrier, the lower 16x16 tiles of K K^T and Q K^T (-> A and P) and the
+//     inverses of the diagonal blocks of (I + A) -- with N strictly lower
+//     triangular, (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8), and
+//     K K^T is symmetric, so both operand layouts of N come from the one
+//     accumulator tile;
+//   consumers (waves 4-7), 16 value columns each: K S0^T, Q S0^T and U
+//     before the mid-chunk barrier, O and the state update after it.
+// Two barriers per chunk: the producers' stores of chunk c + 1 sit before
+// the first, the A / P tiles they form from them before the second.
 // Every product runs on v_mfma_f32_16x16x{32,16}_bf16 with each fp32
 // operand split as x ~= hi + lo (two bf16), and a*b ~= ah*bh + ah*bl + al*bh
 // accumulated in fp32: about 16 significant bits per operand, which keeps
@@ -49,27 +50,35 @@
 namespace gdn {
 namespace {
 
-// LDS plan (bytes).  P, A and V^T rows are padded by 16 bytes so that 16
-// lanes reading 16 consecutive rows hit distinct banks; K and Q rows follow
-// QkRow.  The planes are staggered by 64 bytes so that stores of K and Q
-// rows for the same token fall in different banks.
+constexpr int kT = 32;         // chunk length (tokens)
+constexpr int kNb = kT / 16;   // 16-token blocks per chunk
+constexpr int kTpt = kT / 8;   // tokens per producer thread
+
+// LDS plan (bytes): two buffers of per-chunk planes, then the conv taps.
+// P, A and V^T rows are padded by 16 bytes so that 16 lanes reading 16
+// consecutive rows hit distinct banks; K and Q rows follow QkRow.  The K and
+// Q planes are staggered by 64 bytes.
 template <int DK>
 struct Plan {
   static constexpr int kRowQK = QkRow<DK>::kElems;  // bf16 per row of K, Q   [token][dk]
-  static constexpr int kRowT = kC + 8;   // bf16 per row of P, A   [token][token]
-  static constexpr int kQK = 2 * kC * kRowQK + 64;
-  static constexpr int kSq = 2 * kC * kRowT;
-  static constexpr int oKh = 0, oKl = oKh + kQK, oQh = oKl + kQK, oQl = oQh + kQK;
-  static constexpr int oPh = oQl + kQK, oPl = oPh + kSq, oAh = oPl + kSq, oAl = oAh + kSq;
-  static constexpr int oGate = oAl + kSq;  // fp32 [4][64]: g, b, e^g, e^{g_c - g}
-  static constexpr int kRowV = kC + 4;     // fp32 per row of V^T [value column][token]
-  static constexpr int oV = oGate + 4 * kC * 4;
+  static constexpr int kRowT = kT + 8;   // bf16 per row of P, A   [token][token]
+  static constexpr int kRowV = kT + 4;   // fp32 per row of V^T    [value column][token]
+  static constexpr int kQK = 2 * kT * kRowQK + 64;
+  static constexpr int kSq = 2 * kT * kRowT;
+  // offsets inside one buffer
+  static constexpr int bKh = 0, bKl = bKh + kQK, bQh = bKl + kQK, bQl = bQh + kQK;
+  static constexpr int bPh = bQl + kQK, bPl = bPh + kSq, bAh = bPl + kSq, bAl = bAh + kSq;
+  static constexpr int bGate = bAl + kSq;  // fp32 [4][kT]: g, b, e^g, e^{g_c - g}
+  static constexpr int bV = bGate + 4 * kT * 4;
+  static constexpr int kBuf = bV + kCols * kRowV * 4;
   // conv taps (4, left-padded) and bias of the workgroup's channels: q, k of
   // the key head, then the 64 value columns
   static constexpr int kWch = 2 * DK + kCols;
-  static constexpr int oW = oV + kCols * kRowV * 4;
+  static constexpr int oW = 2 * kBuf;
   static constexpr int oB = oW + kWch * 16;
   static constexpr int kBytes = oB + kWch * 4;
+  // Plane at in-buffer offset `o` of buffer `buf` (0 or 1).
+  __device__ static int at(int buf, int o) { return buf * kBuf + o; }
 };
 
 template <int DK, typename Act>
@@ -80,21 +89,21 @@ struct Prefill : PrefillCore<DK, Act> {
   static constexpr int kDt = DK / 16;   // 16-row tiles of d_k
   static constexpr int kNco = DK / 4;   // channel octets of q and k
   static constexpr int kGrp = DK / 8;   // octets per head (lanes of one norm)
+  static constexpr int kRaw = kTpt + 3; // raw rows per producer thread
 
   // Element offset of storage slot sl of row r in a K or Q plane.
   __device__ __forceinline__ static int qk(int r, int sl) { return QkRow<DK>::at(r, sl); }
 
   // ================= producers =================
-  // Thread (co, tau): channel octet co of q|k (q first), tokens 8 tau..+7.
+  // Thread (co, tau): channel octet co of q|k (q first), tokens 4 tau..+3.
   struct Prod {
-    Row8<Act> raw[11];          // rows 8 tau - 3 .. 8 tau + 7 of a chunk
-    s4 hi[8][2], lo[8][2];      // the chunk's normalised rows, not yet stored
-    float gate[4];              // wave 3: g, b, e^g, e^{g_c - g} of token = lane
+    Row8<Act> raw[kRaw];        // rows 4 tau - 3 .. 4 tau + 3 of a chunk
+    s4 hi[kTpt][2], lo[kTpt][2];  // the chunk's normalised rows, not yet stored
     int co, tau, ch, oc;
     bool isk, on;
-    // value conv: channels 2 vp, 2 vp + 1 of the column block, tokens 8 vt..+7
-    uint32_t vraw[11][sizeof(Act) == 2 ? 1 : 2];
-    f4 vo[2][2];                // [channel][token half], not yet stored
+    // value conv: channels 2 vp, 2 vp + 1 of the column block, tokens 4 vt..+3
+    uint32_t vraw[kRaw][sizeof(Act) == 2 ? 1 : 2];
+    f4 vo[2];                   // [channel], not yet stored
     int vp, vt, vch;
     bool von;
   };
@@ -139,12 +148,12 @@ struct Prefill : PrefillCore<DK, Act> {
     const int tau = opaque(p.tau), ch = opaque(p.ch), vt = opaque(p.vt), vch = opaque(p.vch);
     if (p.on) {
 #pragma unroll
-      for (int r = 0; r < 11; ++r) p.raw[r].load(rx, x_off(c0, c0 + 8 * tau - 3 + r, ch));
+      for (int r = 0; r < kRaw; ++r) p.raw[r].load(rx, x_off(c0, c0 + kTpt * tau - 3 + r, ch));
     }
     if (p.von) {
 #pragma unroll
-      for (int r = 0; r < 11; ++r) {
-        const int off = x_off(c0, c0 + 8 * vt - 3 + r, vch);
+      for (int r = 0; r < kRaw; ++r) {
+        const int off = x_off(c0, c0 + kTpt * vt - 3 + r, vch);
         if constexpr (sizeof(Act) == 2) {
           p.vraw[r][0] = __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0);
         } else {
@@ -156,21 +165,21 @@ struct Prefill : PrefillCore<DK, Act> {
       }
     }
     if (c0 == 0) {
-      // rows -3..-1 (thread tokens 0..2 of token octet 0) from the window;
+      // rows -3..-1 (thread tokens 0..2 of token group 0) from the window;
       // every other offset lies past the window and reads zero
       const rsrc_t rw = win_rows();
       if (p.on) {
 #pragma unroll
         for (int r = 0; r < 3; ++r) {
           Row8<Act> wr;
-          wr.load(rw, win_off(8 * tau - 3 + r, ch));
+          wr.load(rw, win_off(kTpt * tau - 3 + r, ch));
           p.raw[r].merge(wr);
         }
       }
       if (p.von) {
 #pragma unroll
         for (int r = 0; r < 3; ++r) {
-          const int off = win_off(8 * vt - 3 + r, vch);
+          const int off = win_off(kTpt * vt - 3 + r, vch);
           if constexpr (sizeof(Act) == 2) {
             p.vraw[r][0] |= __builtin_amdgcn_raw_buffer_load_b32(rw, off, 0, 0);
           } else {
@@ -197,7 +206,7 @@ struct Prefill : PrefillCore<DK, Act> {
         bias[m] = bl[8 * p.co + m];
       }
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
+      for (int tt = 0; tt < kTpt; ++tt) {
         float y[8], ss = 0.f;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
@@ -212,15 +221,15 @@ struct Prefill : PrefillCore<DK, Act> {
         const float sum = group_sum<kGrp>(ss);
         float sc = a.l2norm ? rsqrtf(sum + a.eps) : 1.0f;
         if (!p.isk) sc *= a.q_scale;
-        if (c0 + 8 * p.tau + tt >= T) sc = 0.f;
+        if (c0 + kTpt * p.tau + tt >= T) sc = 0.f;
         split4(f4{y[0], y[1], y[2], y[3]} * sc, p.hi[tt][0], p.lo[tt][0]);
         split4(f4{y[4], y[5], y[6], y[7]} * sc, p.hi[tt][1], p.lo[tt][1]);
       }
     }
     if (p.von) {
-      float xr[11][2];
+      float xr[kRaw][2];
 #pragma unroll
-      for (int r = 0; r < 11; ++r) {
+      for (int r = 0; r < kRaw; ++r) {
         if constexpr (sizeof(Act) == 2) {
           xr[r][0] = __uint_as_float(p.vraw[r][0] << 16);
           xr[r][1] = __uint_as_float(p.vraw[r][0] & 0xffff0000u);
@@ -234,46 +243,81 @@ struct Prefill : PrefillCore<DK, Act> {
         const f4 vw = *reinterpret_cast<const f4*>(wl + 4 * (2 * DK + 2 * p.vp + m));
         const float vb = bl[2 * DK + 2 * p.vp + m];
 #pragma unroll
-        for (int tt = 0; tt < 8; ++tt) {
+        for (int tt = 0; tt < kTpt; ++tt) {
           float y = vb;
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) y = fmaf(vw[jj], xr[tt + jj][m], y);
-          p.vo[m][tt >> 2][tt & 3] = c0 + 8 * p.vt + tt < T ? act(y) : 0.f;
+          p.vo[m][tt] = c0 + kTpt * p.vt + tt < T ? act(y) : 0.f;
         }
       }
     }
-    if (wave == 3) {
-      float la = 0.f, bt = 0.f;
-      if (c0 + lane < T) {
-        const int64_t row = (static_cast<int64_t>(t0) + c0 + lane) * a.Hv + h;
-        la = fmaxf(logf(to_f32(static_cast<const Act*>(a.alpha)[row])), -80.0f);
-        bt = to_f32(static_cast<const Act*>(a.beta)[row]);
-      }
-      float g = la;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(g, off);
-        if (lane >= off) g += o;
-      }
-      const float gc = __shfl(g, 63);
-      p.gate[0] = g;
-      p.gate[1] = bt;
-      p.gate[2] = expf(g);
-      p.gate[3] = expf(gc - g);
+  }
+
+  // Raw bits of the gate inputs a, b of chunk c0 (token = lane < kT),
+  // loaded a chunk ahead of their use through descriptors over the
+  // sequence's rows (rows past it read zero); converted only where used, so
+  // the loads are not waited for here.
+  struct GateIn {
+    uint32_t al, bt;
+    int c0;
+  };
+  __device__ __forceinline__ GateIn gate_load(int c0) const {
+    constexpr int kE = static_cast<int>(sizeof(Act));
+    const uint32_t bytes = static_cast<uint32_t>(T) * static_cast<uint32_t>(a.Hv) * kE;
+    const int64_t base = static_cast<int64_t>(t0) * a.Hv;
+    const rsrc_t ra = make_rsrc(static_cast<const Act*>(a.alpha) + base, bytes);
+    const rsrc_t rb = make_rsrc(static_cast<const Act*>(a.beta) + base, bytes);
+    const uint32_t off =
+        lane < kT ? static_cast<uint32_t>(((c0 + lane) * a.Hv + h) * kE) : kOutOfRange;
+    GateIn r;
+    r.c0 = c0;
+    if constexpr (kE == 2) {
+      r.al = __builtin_amdgcn_raw_buffer_load_b16(ra, off, 0, 0);
+      r.bt = __builtin_amdgcn_raw_buffer_load_b16(rb, off, 0, 0);
+    } else {
+      r.al = __builtin_amdgcn_raw_buffer_load_b32(ra, off, 0, 0);
+      r.bt = __builtin_amdgcn_raw_buffer_load_b32(rb, off, 0, 0);
+    }
+    return r;
+  }
+
+  // The gates of a chunk into buffer buf (one wave, token = lane < kT):
+  // g = prefix sums of log a over the chunk, b, e^g and e^{g_c - g}; tokens
+  // past the sequence take a = 1, b = 0 and add nothing.  The scan runs
+  // inside each row of 16 lanes (DPP shifts, zero filled), then row 1 adds
+  // row 0's total.
+  __device__ void gates(const GateIn& in, int buf) const {
+    const bool valid = lane < kT && in.c0 + lane < T;
+    const float al = valid ? __uint_as_float(sizeof(Act) == 2 ? in.al << 16 : in.al) : 1.f;
+    const float bt = valid ? __uint_as_float(sizeof(Act) == 2 ? in.bt << 16 : in.bt) : 0.f;
+    float g = fmaxf(logf(al), -80.0f);
+    g += row_shr<1>(g);
+    g += row_shr<2>(g);
+    g += row_shr<4>(g);
+    g += row_shr<8>(g);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), 15));
+    if (lane >= 16) g += r0;
+    const float gc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), kT - 1));
+    if (lane < kT) {
+      float* gt = fp(P::at(buf, P::bGate));
+      gt[lane] = g;
+      gt[kT + lane] = bt;
+      gt[2 * kT + lane] = expf(g);
+      gt[3 * kT + lane] = expf(gc - g);
     }
   }
 
-  // Store the prepared chunk: rows of K or Q (two groups of 4 channels at
-  // slot(8 oc) and +8), and the gates.
-  __device__ void prod_store(const Prod& p) const {
+  // Store the prepared chunk into buffer buf: rows of K or Q (two groups of
+  // 4 channels at slot(8 oc) and +8) and the value columns.
+  __device__ void prod_store(const Prod& p, int buf) const {
     if (p.on) {
-      short* hi = sp(p.isk ? P::oKh : P::oQh);
-      short* lo = sp(p.isk ? P::oKl : P::oQl);
+      short* hi = sp(P::at(buf, p.isk ? P::bKh : P::bQh));
+      short* lo = sp(P::at(buf, p.isk ? P::bKl : P::bQl));
       const int tau = opaque(p.tau);
       const int sb = slot(8 * opaque(p.oc));
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        const int o0 = qk(8 * tau + tt, sb), o1 = qk(8 * tau + tt, sb + 8);
+      for (int tt = 0; tt < kTpt; ++tt) {
+        const int o0 = qk(kTpt * tau + tt, sb), o1 = qk(kTpt * tau + tt, sb + 8);
         *reinterpret_cast<s4*>(hi + o0) = p.hi[tt][0];
         *reinterpret_cast<s4*>(hi + o1) = p.hi[tt][1];
         *reinterpret_cast<s4*>(lo + o0) = p.lo[tt][0];
@@ -281,23 +325,15 @@ struct Prefill : PrefillCore<DK, Act> {
       }
     }
     if (p.von) {
-      float* vt = fp(P::oV);
+      float* vt = fp(P::at(buf, P::bV));
       const int vp = opaque(p.vp), vtk = opaque(p.vt);
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        float* row = vt + (2 * vp + m) * P::kRowV + 8 * vtk;
-        *reinterpret_cast<f4*>(row) = p.vo[m][0];
-        *reinterpret_cast<f4*>(row + 4) = p.vo[m][1];
-      }
-    }
-    if (wave == 3) {
-      float* gt = fp(P::oGate);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) gt[i * kC + lane] = p.gate[i];
+      for (int m = 0; m < 2; ++m)
+        *reinterpret_cast<f4*>(vt + (2 * vp + m) * P::kRowV + kTpt * vtk) = p.vo[m];
     }
   }
 
-  // ================= all waves: A, P and the diagonal inverses =========
+  // ================= producers, second half: A, P and the inverses ======
   // Element offsets, for rows 16 blk + lr, of the 16x16x32 operand slots
   // 32 sl + 8 lg: a per-slice base plus 16 blk rows (the swizzle depends on
   // the row only through lr).
@@ -307,50 +343,64 @@ struct Prefill : PrefillCore<DK, Act> {
     for (int sl = 0; sl < kSl; ++sl) ob[sl] = qk(r, 32 * sl + 8 * g);
   }
 
-  // Block pair (IB, JB), IB >= JB: the K K^T and Q K^T blocks, computed
-  // transposed (A operand K rows JB, B operands K and Q rows IB) so that
-  // each lane holds row r = 16 IB + lr at the four columns 16 JB + 4 lg + v:
-  // they store as one 8-byte (hi, lo) group each.
-  template <int IB, int JB>
-  __device__ __forceinline__ void pair_gram(f4& g, f4& pq, const int (&ob)[kSl]) const {
-    const short* kh = sp(P::oKh);
-    const short* kl = sp(P::oKl);
-    const short* qh = sp(P::oQh);
-    const short* ql = sp(P::oQl);
-    g = f4{0.f, 0.f, 0.f, 0.f};
-    pq = f4{0.f, 0.f, 0.f, 0.f};
+  // Tiles of token blocks (IB, JB), IB >= JB, of K K^T (G) and / or Q K^T
+  // (PQ), computed transposed (A operand K rows JB, B operands K and Q rows
+  // IB) so that each lane holds row r = 16 IB + lr at the four columns
+  // 16 JB + 4 lg + v: they store as one 8-byte (hi, lo) group each.
+  template <int IB, int JB, bool G, bool PQ>
+  __device__ __forceinline__ void tiles(f4& g, f4& pq, const int (&ob)[kSl], int buf) const {
+    const short* kh = sp(P::at(buf, P::bKh));
+    const short* kl = sp(P::at(buf, P::bKl));
+    const short* qh = sp(P::at(buf, P::bQh));
+    const short* ql = sp(P::at(buf, P::bQl));
+    // two accumulators per product (even and odd slices) halve the chain
+    // of dependent MFMAs
+    f4 gs[2], ps[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      gs[i] = f4{0.f, 0.f, 0.f, 0.f};
+      ps[i] = f4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int sl = 0; sl < kSl; ++sl) {
       const int oa = 16 * JB * P::kRowQK + ob[sl], obr = 16 * IB * P::kRowQK + ob[sl];
       const s8 ah = *reinterpret_cast<const s8*>(kh + oa);
       const s8 al = *reinterpret_cast<const s8*>(kl + oa);
-      const s8 bkh = IB == JB ? ah : *reinterpret_cast<const s8*>(kh + obr);
-      const s8 bkl = IB == JB ? al : *reinterpret_cast<const s8*>(kl + obr);
-      const s8 bqh = *reinterpret_cast<const s8*>(qh + obr);
-      const s8 bql = *reinterpret_cast<const s8*>(ql + obr);
-      g = mma32(al, bkh, g);
-      pq = mma32(al, bqh, pq);
-      g = mma32(ah, bkl, g);
-      pq = mma32(ah, bql, pq);
-      g = mma32(ah, bkh, g);
-      pq = mma32(ah, bqh, pq);
+      if constexpr (G) {
+        const s8 bkh = IB == JB ? ah : *reinterpret_cast<const s8*>(kh + obr);
+        const s8 bkl = IB == JB ? al : *reinterpret_cast<const s8*>(kl + obr);
+        gs[sl & 1] = mma32x3(ah, al, bkh, bkl, gs[sl & 1]);
+      }
+      if constexpr (PQ) {
+        const s8 bqh = *reinterpret_cast<const s8*>(qh + obr);
+        const s8 bql = *reinterpret_cast<const s8*>(ql + obr);
+        ps[sl & 1] = mma32x3(ah, al, bqh, bql, ps[sl & 1]);
+      }
     }
+    g = gs[0] + gs[1];
+    pq = ps[0] + ps[1];
   }
 
-  // Scale a transposed pair and store it: A_ri = b_r e^{g_r - g_i} k_r.k_i
-  // (IB > JB only) and P_ri = e^{g_r - g_i} q_r.k_i (i <= r).
+  // Decays e^{g_r - g_i} of a transposed tile: r = 16 IB + lr, i = 16 JB +
+  // 4 lg + v.
   template <int IB, int JB>
-  __device__ __forceinline__ void pair_store(const f4& g, const f4& pq) const {
+  __device__ __forceinline__ f4 decays(const float* gt) const {
     const int l = lane_now(), lr = l & 15, lg = l >> 4;
-    const float* gt = fp(P::oGate);
-    const int r = 16 * IB + lr;
-    const float gr = gt[r];
+    const float gr = gt[16 * IB + lr];
     const f4 gi = *reinterpret_cast<const f4*>(gt + 16 * JB + 4 * lg);
     f4 dec;
 #pragma unroll
     for (int v = 0; v < 4; ++v) dec[v] = __expf(gr - gi[v]);
-    const int o = r * P::kRowT + slot(16 * JB + 4 * lg);
-    f4 pv = dec * pq;
+    return dec;
+  }
+
+  // P_ri = e^{g_r - g_i} q_r.k_i (i <= r) from a transposed Q K^T tile.
+  template <int IB, int JB>
+  __device__ __forceinline__ void store_p(const f4& pq, int buf) const {
+    const int l = lane_now(), lr = l & 15, lg = l >> 4;
+    const float* gt = fp(P::at(buf, P::bGate));
+    const int o = (16 * IB + lr) * P::kRowT + slot(16 * JB + 4 * lg);
+    f4 pv = decays<IB, JB>(gt) * pq;
     if (IB == JB) {
 #pragma unroll
       for (int v = 0; v < 4; ++v)
@@ -358,38 +408,32 @@ struct Prefill : PrefillCore<DK, Act> {
     }
     s4 h, lo;
     split4(pv, h, lo);
-    *reinterpret_cast<s4*>(sp(P::oPh) + o) = h;
-    *reinterpret_cast<s4*>(sp(P::oPl) + o) = lo;
-    if (IB > JB) {
-      split4(gt[kC + r] * dec * g, h, lo);
-      *reinterpret_cast<s4*>(sp(P::oAh) + o) = h;
-      *reinterpret_cast<s4*>(sp(P::oAl) + o) = lo;
-    }
+    *reinterpret_cast<s4*>(sp(P::at(buf, P::bPh)) + o) = h;
+    *reinterpret_cast<s4*>(sp(P::at(buf, P::bPl)) + o) = lo;
   }
 
+  // A_ri = b_r e^{g_r - g_i} k_r.k_i (IB > JB) from a transposed K K^T tile.
   template <int IB, int JB>
-  __device__ __forceinline__ void pair(const int (&ob)[kSl]) const {
-    f4 g, pq;
-    pair_gram<IB, JB>(g, pq, ob);
-    pair_store<IB, JB>(g, pq);
-  }
-  template <int B>
-  __device__ __forceinline__ void diag_pair(const int (&ob)[kSl]) const {
-    f4 g, pq;
-    pair_gram<B, B>(g, pq, ob);
-    pair_store<B, B>(g, pq);
-    diag_inverse(B, g);
+  __device__ __forceinline__ void store_a(const f4& g, int buf) const {
+    const int l = lane_now(), lr = l & 15, lg = l >> 4;
+    const float* gt = fp(P::at(buf, P::bGate));
+    const int r = 16 * IB + lr;
+    const int o = r * P::kRowT + slot(16 * JB + 4 * lg);
+    s4 h, lo;
+    split4(gt[kT + r] * decays<IB, JB>(gt) * g, h, lo);
+    *reinterpret_cast<s4*>(sp(P::at(buf, P::bAh)) + o) = h;
+    *reinterpret_cast<s4*>(sp(P::at(buf, P::bAl)) + o) = lo;
   }
 
   // Diagonal block b from its raw K K^T tile G: N = the strictly lower block
   // of A, X = (I + N)^{-1}, stored in A layout (X[lr][4 lg + v]) in the
   // diagonal block of the A planes.
-  __device__ void diag_inverse(int b, const f4& G) const {
+  __device__ void diag_inverse(int b, const f4& G, int buf) const {
     const int l = lane_now(), lr = l & 15, lg = l >> 4;
-    const float* gt = fp(P::oGate);
-    const float gi = gt[16 * b + lr], bi = gt[kC + 16 * b + lr];
+    const float* gt = fp(P::at(buf, P::bGate));
+    const float gi = gt[16 * b + lr], bi = gt[kT + 16 * b + lr];
     const f4 gr = *reinterpret_cast<const f4*>(gt + 16 * b + 4 * lg);
-    const f4 br = *reinterpret_cast<const f4*>(gt + kC + 16 * b + 4 * lg);
+    const f4 br = *reinterpret_cast<const f4*>(gt + kT + 16 * b + 4 * lg);
     f4 nb, na;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -401,41 +445,56 @@ struct Prefill : PrefillCore<DK, Act> {
     s4 xh, xl;
     split4(xt, xh, xl);
     const int o = (16 * b + lr) * P::kRowT + slot(16 * b + 4 * lg);
-    *reinterpret_cast<s4*>(sp(P::oAh) + o) = xh;
-    *reinterpret_cast<s4*>(sp(P::oAl) + o) = xl;
+    *reinterpret_cast<s4*>(sp(P::at(buf, P::bAh)) + o) = xh;
+    *reinterpret_cast<s4*>(sp(P::at(buf, P::bAl)) + o) = xl;
   }
 
-  // The 10 block pairs over 8 waves: waves 0-3 a diagonal pair each (with
-  // the inverse of that block of I + A), waves 4-7 the 6 off-diagonal pairs.
-  __device__ void gram_phase() const {
+  // The chunk in buffer buf over the 4 producer waves: waves 0 and 1 the
+  // diagonal K K^T tiles and their inverses, wave 2 the diagonal Q K^T
+  // tiles, wave 3 the off-diagonal pair.
+  __device__ void gram_phase(int buf) const {
     int ob[kSl];
     op_bases(ob);
+    f4 g, pq;
     switch (wave) {
-      case 0: diag_pair<0>(ob); break;
-      case 1: diag_pair<1>(ob); break;
-      case 2: diag_pair<2>(ob); break;
-      case 3: diag_pair<3>(ob); break;
-      case 4: pair<1, 0>(ob); pair<2, 1>(ob); break;
-      case 5: pair<2, 0>(ob); pair<3, 2>(ob); break;
-      case 6: pair<3, 0>(ob); break;
-      default: pair<3, 1>(ob); break;
+      case 0:
+        tiles<0, 0, true, false>(g, pq, ob, buf);
+        diag_inverse(0, g, buf);
+        break;
+      case 1:
+        tiles<1, 1, true, false>(g, pq, ob, buf);
+        diag_inverse(1, g, buf);
+        break;
+      case 2:
+        tiles<0, 0, false, true>(g, pq, ob, buf);
+        store_p<0, 0>(pq, buf);
+        tiles<1, 1, false, true>(g, pq, ob, buf);
+        store_p<1, 1>(pq, buf);
+        break;
+      default:
+        tiles<1, 0, true, true>(g, pq, ob, buf);
+        store_a<1, 0>(g, buf);
+        store_p<1, 0>(pq, buf);
+        break;
     }
   }
 
   // ================= consumers =================
-  // The wave's 16 value columns for chunk c0.  S[d] holds rows
-  // 16d + 4 lg + v (key index) of S^T at column e0 + lr (value index).
-  __device__ void columns(int c0, f4 (&S)[kDt]) const {
+  // First half of chunk c0 (buffer buf) for the wave's 16 value columns:
+  // K S0^T, Q S0^T and the updates U.  S[d] holds rows 16d + 4 lg + v (key
+  // index) of S^T at column e0 + lr (value index); U[b] and qs[b] rows
+  // 16 b + 4 lg + v (token) at that column.
+  __device__ void updates(const f4 (&S)[kDt], f4 (&U)[kNb], f4 (&qs)[kNb], int buf) const {
     const int l = lane_now(), lr = l & 15, lg = l >> 4;
-    const float* gt = fp(P::oGate);
-    const short* kh = sp(P::oKh);
-    const short* kl = sp(P::oKl);
-    const short* qh = sp(P::oQh);
-    const short* ql = sp(P::oQl);
+    const float* gt = fp(P::at(buf, P::bGate));
+    const short* kh = sp(P::at(buf, P::bKh));
+    const short* kl = sp(P::at(buf, P::bKl));
+    const short* qh = sp(P::at(buf, P::bQh));
+    const short* ql = sp(P::at(buf, P::bQl));
     // K S0^T and Q S0^T, rows 16 tb + 4 lg + v
-    f4 ks[4], qs[4];
+    f4 ks[kNb];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
+    for (int tb = 0; tb < kNb; ++tb) {
       ks[tb] = f4{0.f, 0.f, 0.f, 0.f};
       qs[tb] = f4{0.f, 0.f, 0.f, 0.f};
     }
@@ -443,9 +502,9 @@ struct Prefill : PrefillCore<DK, Act> {
     op_bases(ob);
 #pragma unroll
     for (int sl = 0; sl < kSl; ++sl) {
-      s8 xh[4], xl[4], yh[4], yl[4];
+      s8 xh[kNb], xl[kNb], yh[kNb], yl[kNb];
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
+      for (int tb = 0; tb < kNb; ++tb) {
         const int ra = 16 * tb * P::kRowQK + ob[sl];
         xh[tb] = *reinterpret_cast<const s8*>(kh + ra);
         xl[tb] = *reinterpret_cast<const s8*>(kl + ra);
@@ -457,142 +516,126 @@ struct Prefill : PrefillCore<DK, Act> {
       split4(S[2 * sl + 1], h1, l1);
       const s8 sbh = cat(h0, h1), sbl = cat(l0, l1);
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
+      for (int tb = 0; tb < kNb; ++tb) {
         ks[tb] = mma32(xl[tb], sbh, ks[tb]);
         qs[tb] = mma32(yl[tb], sbh, qs[tb]);
       }
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
+      for (int tb = 0; tb < kNb; ++tb) {
         ks[tb] = mma32(xh[tb], sbl, ks[tb]);
         qs[tb] = mma32(yh[tb], sbl, qs[tb]);
       }
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
+      for (int tb = 0; tb < kNb; ++tb) {
         ks[tb] = mma32(xh[tb], sbh, ks[tb]);
         qs[tb] = mma32(yh[tb], sbh, qs[tb]);
       }
     }
     // U_b = X_bb (b_b R_b - sum_{j<b} A_bj U_j),  R = V - e^g (K S0^T)
-    const float* vt = fp(P::oV) + (e0 % kCols + lr) * P::kRowV;
-    f4 U[4];
-    s4 uh[4], ul[4];
+    const float* vt = fp(P::at(buf, P::bV)) + (e0 % kCols + lr) * P::kRowV;
+    const short* ah_ = sp(P::at(buf, P::bAh));
+    const short* al_ = sp(P::at(buf, P::bAl));
+    s4 uh[kNb], ul[kNb];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int b = 0; b < kNb; ++b) {
       const int row = (16 * b + lr) * P::kRowT;
       f4 acc = {0.f, 0.f, 0.f, 0.f};
-      if (b > 0) {
-        s4 ah[3], al[3];
 #pragma unroll
-        for (int jb = 0; jb < b; ++jb) {
-          const int o = row + slot(16 * jb + 4 * lg);
-          ah[jb] = *reinterpret_cast<const s4*>(sp(P::oAh) + o);
-          al[jb] = *reinterpret_cast<const s4*>(sp(P::oAl) + o);
-        }
-#pragma unroll
-        for (int jb = 0; jb < b; ++jb) acc = mma16(al[jb], uh[jb], acc);
-#pragma unroll
-        for (int jb = 0; jb < b; ++jb) acc = mma16(ah[jb], ul[jb], acc);
-#pragma unroll
-        for (int jb = 0; jb < b; ++jb) acc = mma16(ah[jb], uh[jb], acc);
+      for (int jb = 0; jb < b; ++jb) {
+        const int o = row + slot(16 * jb + 4 * lg);
+        acc = mma16x3(*reinterpret_cast<const s4*>(ah_ + o), *reinterpret_cast<const s4*>(al_ + o),
+                      uh[jb], ul[jb], acc);
       }
       const int o = row + slot(16 * b + 4 * lg);
-      const s4 xh = *reinterpret_cast<const s4*>(sp(P::oAh) + o);
-      const s4 xl = *reinterpret_cast<const s4*>(sp(P::oAl) + o);
+      const s4 xh = *reinterpret_cast<const s4*>(ah_ + o);
+      const s4 xl = *reinterpret_cast<const s4*>(al_ + o);
       const f4 V = *reinterpret_cast<const f4*>(vt + 16 * b + 4 * lg);
-      const f4 gam = *reinterpret_cast<const f4*>(gt + 2 * kC + 16 * b + 4 * lg);
-      const f4 bt = *reinterpret_cast<const f4*>(gt + kC + 16 * b + 4 * lg);
+      const f4 gam = *reinterpret_cast<const f4*>(gt + 2 * kT + 16 * b + 4 * lg);
+      const f4 bt = *reinterpret_cast<const f4*>(gt + kT + 16 * b + 4 * lg);
       s4 zh, zl;
       split4(bt * (V - gam * ks[b]) - acc, zh, zl);
       U[b] = mma16x3(xh, xl, zh, zl, f4{0.f, 0.f, 0.f, 0.f});
       split4(U[b], uh[b], ul[b]);
     }
-    // O = e^g (Q S0^T) + P U: the six (block row, 32-slice) products at once
+  }
+
+  // Second half: O = e^g (Q S0^T) + P U to the output rows of chunk c0
+  // (rows past the sequence lie past the descriptor and are dropped), then
+  // S^T <- e^{g_c} S^T + K^T diag(e^{g_c - g}) U.
+  __device__ void outputs_and_state(int c0, f4 (&S)[kDt], const f4 (&U)[kNb],
+                                    const f4 (&qs)[kNb], int buf) const {
+    const int l = lane_now(), lr = l & 15, lg = l >> 4;
+    const float* gt = fp(P::at(buf, P::bGate));
+    s4 uh[kNb], ul[kNb];
+#pragma unroll
+    for (int b = 0; b < kNb; ++b) split4(U[b], uh[b], ul[b]);
+    const s8 u0h = cat(uh[0], uh[1]), u0l = cat(ul[0], ul[1]);
     {
-      constexpr int kB[6] = {0, 1, 2, 2, 3, 3}, kU[6] = {0, 0, 0, 1, 0, 1};
-      s8 ph[6], pl[6];
+      const short* ph_ = sp(P::at(buf, P::bPh));
+      const short* pl_ = sp(P::at(buf, P::bPl));
+      f4 o[kNb];
 #pragma unroll
-      for (int i = 0; i < 6; ++i) {
-        const int off = (16 * kB[i] + lr) * P::kRowT + 32 * kU[i] + 8 * lg;
-        ph[i] = *reinterpret_cast<const s8*>(sp(P::oPh) + off);
-        pl[i] = *reinterpret_cast<const s8*>(sp(P::oPl) + off);
+      for (int b = 0; b < kNb; ++b) {
+        const int off = (16 * b + lr) * P::kRowT + 8 * lg;
+        const s8 ph = *reinterpret_cast<const s8*>(ph_ + off);
+        const s8 pl = *reinterpret_cast<const s8*>(pl_ + off);
+        o[b] = *reinterpret_cast<const f4*>(gt + 2 * kT + 16 * b + 4 * lg) * qs[b];
+        o[b] = mma32x3(ph, pl, u0h, u0l, o[b]);
       }
-      f4 o[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        o[b] = *reinterpret_cast<const f4*>(gt + 2 * kC + 16 * b + 4 * lg) * qs[b];
-      const s8 u0h = cat(uh[0], uh[1]), u0l = cat(ul[0], ul[1]);
-      const s8 u1h = cat(uh[2], uh[3]), u1l = cat(ul[2], ul[3]);
-#pragma unroll
-      for (int i = 0; i < 6; ++i) o[kB[i]] = mma32(pl[i], kU[i] ? u1h : u0h, o[kB[i]]);
-#pragma unroll
-      for (int i = 0; i < 6; ++i) o[kB[i]] = mma32(ph[i], kU[i] ? u1l : u0l, o[kB[i]]);
-#pragma unroll
-      for (int i = 0; i < 6; ++i) o[kB[i]] = mma32(ph[i], kU[i] ? u1h : u0h, o[kB[i]]);
-      // rows t >= T - c0 lie past the descriptor and are dropped
       const int rs = a.Hv * a.dv;
-      const int n = T - c0 < kC ? T - c0 : kC;
+      const int n = T - c0 < kT ? T - c0 : kT;
       const rsrc_t ro =
           make_rsrc(a.out + ((static_cast<int64_t>(t0) + c0) * a.Hv + h) * a.dv + e0,
                     static_cast<uint32_t>(n) * static_cast<uint32_t>(rs) * 4u);
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < kNb; ++b)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[b][v]), ro,
                                                 ((16 * b + 4 * lg + v) * rs + lr) * 4, 0, 0);
     }
-    // S^T <- e^{g_c} S^T + K^T diag(e^{g_c - g}) U; K^T tiles by transposing
-    // reads of the K rows, four key tiles at a time.
-    s8 wh[2], wl[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const f4 g0 = *reinterpret_cast<const f4*>(gt + 3 * kC + 32 * u + 4 * lg);
-      const f4 g1 = *reinterpret_cast<const f4*>(gt + 3 * kC + 32 * u + 16 + 4 * lg);
+    // The state update: K^T tiles by transposing reads of the K rows.
+    const short* kh = sp(P::at(buf, P::bKh));
+    const short* kl = sp(P::at(buf, P::bKl));
+    s8 wh, wl;
+    {
+      const f4 g0 = *reinterpret_cast<const f4*>(gt + 3 * kT + 4 * lg);
+      const f4 g1 = *reinterpret_cast<const f4*>(gt + 3 * kT + 16 + 4 * lg);
       s4 h0, l0, h1, l1;
-      split4(g0 * U[2 * u], h0, l0);
-      split4(g1 * U[2 * u + 1], h1, l1);
-      wh[u] = cat(h0, h1);
-      wl[u] = cat(l0, l1);
+      split4(g0 * U[0], h0, l0);
+      split4(g1 * U[1], h1, l1);
+      wh = cat(h0, h1);
+      wl = cat(l0, l1);
     }
-    const float ec = gt[2 * kC + kC - 1];
-    // K^T tile d, 32-token slice u, half hf: rows 32u + 16hf + 4 lg + lr/4,
-    // slots 32 (d>>1) + 4 (d&1) + 8 (lr&3); a base per pair D = d >> 1 plus
-    // (32u + 16hf) rows and 4 (d&1) slots.
+    const float ec = gt[2 * kT + kT - 1];
+    // K^T tile d, half hf: rows 16hf + 4 lg + lr/4, slots 32 (d>>1) + 4 (d&1)
+    // + 8 (lr&3); a base per pair D = d >> 1 plus 16hf rows and 4 (d&1) slots.
     int tb0[kSl];
     {
-      const int l = lane_now(), r = l & 15, g = l >> 4;
+      const int l2 = lane_now(), r = l2 & 15, g = l2 >> 4;
 #pragma unroll
       for (int D = 0; D < kSl; ++D) tb0[D] = qk(4 * g + (r >> 2), 32 * D + 8 * (r & 3));
     }
     constexpr int kG = kDt < 4 ? kDt : 4;
 #pragma unroll
     for (int d0 = 0; d0 < kDt; d0 += kG) {
-      s8 th[kG][2], tl[kG][2];
+      s8 th[kG], tl[kG];
       f4 acc[kG];
 #pragma unroll
       for (int dd = 0; dd < kG; ++dd) {
         const int d = d0 + dd;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r0 = tb0[d >> 1] + 32 * u * P::kRowQK + 4 * (d & 1);
-          const int r1 = r0 + 16 * P::kRowQK;
-          th[dd][u] = cat(ld_tr(kh + r0), ld_tr(kh + r1));
-          tl[dd][u] = cat(ld_tr(kl + r0), ld_tr(kl + r1));
-        }
+        const int r0 = tb0[d >> 1] + 4 * (d & 1);
+        const int r1 = r0 + 16 * P::kRowQK;
+        th[dd] = cat(ld_tr(kh + r0), ld_tr(kh + r1));
+        tl[dd] = cat(ld_tr(kl + r0), ld_tr(kl + r1));
         acc[dd] = ec * S[d];
       }
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int dd = 0; dd < kG; ++dd) acc[dd] = mma32(tl[dd], wh, acc[dd]);
 #pragma unroll
-        for (int dd = 0; dd < kG; ++dd) acc[dd] = mma32(tl[dd][u], wh[u], acc[dd]);
+      for (int dd = 0; dd < kG; ++dd) acc[dd] = mma32(th[dd], wl, acc[dd]);
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int dd = 0; dd < kG; ++dd) acc[dd] = mma32(th[dd][u], wl[u], acc[dd]);
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int dd = 0; dd < kG; ++dd) acc[dd] = mma32(th[dd][u], wh[u], acc[dd]);
+      for (int dd = 0; dd < kG; ++dd) acc[dd] = mma32(th[dd], wh, acc[dd]);
 #pragma unroll
       for (int dd = 0; dd < kG; ++dd) S[d0 + dd] = acc[dd];
     }
@@ -631,11 +674,12 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
     return;
   k.t0 = t0;
   k.T = t1 - t0;
-  const int nch = (k.T + kC - 1) / kC;
+  const int nch = (k.T + kT - 1) / kT;
 
-  // P and A planes: the blocks above the diagonal stay zero.
-  for (int i = k.tid; i < 4 * P::kSq / 16; i += kThreads)
-    reinterpret_cast<uint4*>(lds_raw + P::oPh)[i] = uint4{0u, 0u, 0u, 0u};
+  // P and A planes of both buffers: the tiles above the diagonal stay zero.
+  for (int bf = 0; bf < 2; ++bf)
+    for (int i = k.tid; i < 4 * P::kSq / 16; i += kThreads)
+      reinterpret_cast<uint4*>(lds_raw + P::at(bf, P::bPh))[i] = uint4{0u, 0u, 0u, 0u};
   k.e0 = j * kCols;
   k.load_taps();
 
@@ -647,25 +691,23 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
     lds_barrier();            // planes zeroed, taps loaded
     if (nch > 0) {
       k.prod_prep(p, 0);
-      if (nch > 1) k.prod_load(p, kC);
-      k.prod_store(p);
-      lds_barrier();
-      k.gram_phase();
-      lds_barrier();
+      if (nch > 1) k.prod_load(p, kT);
+      k.prod_store(p, 0);
     }
+    lds_barrier();            // chunk 0 stored
+    if (nch > 0) k.gram_phase(0);
+    lds_barrier();            // chunk 0's A, P and inverses formed
     for (int c = 0; c < nch; ++c) {
       const bool next = c + 1 < nch;
       if (next) {
-        k.prod_prep(p, (c + 1) * kC);
-        if (c + 2 < nch) k.prod_load(p, (c + 2) * kC);
+        // buffer (c + 1) & 1: its last readers (chunk c - 1) are done
+        k.prod_prep(p, (c + 1) * kT);
+        if (c + 2 < nch) k.prod_load(p, (c + 2) * kT);
+        k.prod_store(p, (c + 1) & 1);
       }
-      lds_barrier();          // consumers are done with chunk c
-      if (next) {
-        k.prod_store(p);
-        lds_barrier();
-        k.gram_phase();
-        lds_barrier();
-      }
+      lds_barrier();          // chunk c + 1 stored
+      if (next) k.gram_phase((c + 1) & 1);
+      lds_barrier();          // chunk c consumed, chunk c + 1 complete
     }
   } else {
     // ---------------- consumers ----------------
@@ -682,28 +724,34 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
                                            static_cast<int64_t>(k.e0 + k.lr) * DK + 16 * d +
                                            4 * k.lg);
     }
-    lds_barrier();            // planes zeroed, taps loaded
-    if (nch > 0) {
-      lds_barrier();          // producers stored chunk 0
-      k.gram_phase();
-      lds_barrier();
+    typename K::GateIn gin{0u, 0u, 0};
+    if (k.wave == 7 && nch > 0) {
+      k.gates(k.gate_load(0), 0);
+      if (nch > 1) gin = k.gate_load(kT);
     }
+    lds_barrier();            // planes zeroed, taps loaded; chunk 0's gates
+    lds_barrier();            // chunk 0 stored
+    lds_barrier();            // chunk 0's A, P and inverses formed
     for (int c = 0; c < nch; ++c) {
-      const bool next = c + 1 < nch;
-      if (cols) k.columns(c * kC, S);
-      const int32_t cs = __builtin_amdgcn_readfirstlane(ckpt_slot(a, s, (c + 1) * kC, k.T));
-      if (cols && cs >= 0) {  // the state after (c + 1) * 64 tokens, to a checkpoint slot
+      const int cb = c & 1;
+      f4 U[kNb], qs[kNb];
+      if (cols) k.updates(S, U, qs, cb);
+      // the next chunk's gates, into the other buffer (its last readers,
+      // chunk c - 1, are done); then the inputs of the one after
+      if (k.wave == 7 && c + 1 < nch) {
+        k.gates(gin, cb ^ 1);
+        if (c + 2 < nch) gin = k.gate_load((c + 2) * kT);
+      }
+      lds_barrier();          // (the producers' chunk c + 1 stores)
+      if (cols) k.outputs_and_state(c * kT, S, U, qs, cb);
+      const int32_t cs = __builtin_amdgcn_readfirstlane(ckpt_slot(a, s, (c + 1) * kT, k.T));
+      if (cols && cs >= 0) {  // the state after (c + 1) * kT tokens, to a checkpoint slot
         const int l = k.lane_now();
         float* o = a.ssm + cs * slot_elems + head + static_cast<int64_t>(k.e0 + (l & 15)) * DK;
 #pragma unroll
         for (int d = 0; d < K::kDt; ++d) *reinterpret_cast<f4*>(o + 16 * d + 4 * (l >> 4)) = S[d];
       }
       lds_barrier();          // chunk c consumed
-      if (next) {
-        lds_barrier();        // producers stored chunk c + 1
-        k.gram_phase();
-        lds_barrier();
-      }
     }
     if (cols) {
       float* out = a.ssm + dst * slot_elems + head + static_cast<int64_t>(k.e0 + k.lr) * DK;
@@ -729,6 +777,7 @@ hipError_t launch_one(const PrefillArgs& a, hipStream_t st) {
 }
 
 static_assert(Plan<128>::kBytes <= 160 * 1024, "LDS plan exceeds 160 KiB");
+static_assert(kT == 32, "the tile code assumes two 16-token blocks per chunk");
 
 }  // namespace
 
