@@ -407,10 +407,11 @@ def prefill_counts(shape, seqlens):
     (K K^T, Q K^T, T V, W = T diag(e^g) K: 5.24 M) and the state pass
     (W S0^T, Q S0^T, P U, U^T K: 6.29 M) -- 11.53 MFLOP at d = 128; the
     per-channel decay changes elementwise factors only.
-    issued, scalar decay: per workgroup (64 value columns) and chunk, 20 Gram
-    tiles and 4 waves of K S0^T, Q S0^T, P U and state-update tiles on
-    16x16x32 MFMAs; on 16x16x16 MFMAs the U solve (10 block products per
-    wave) and the four diagonal-block inverses (8 products each).
+    issued, scalar decay (32-token blocks): per workgroup (64 value columns)
+    and block, 6 Gram tiles and 4 waves of K S0^T, Q S0^T, P U and
+    state-update tiles on 16x16x32 MFMAs; on 16x16x16 MFMAs the U solve (3
+    block products per wave) and the two diagonal-block inverses (8 products
+    each).
     issued, per-channel decay: 12 off-diagonal Gram tiles (the diagonal
     blocks are formed without MFMA), the same K S0^T, Q S0^T and P U tiles,
     and the state update as one 16x16x16 product per 16-token block.  Every
@@ -435,10 +436,12 @@ def prefill_counts(shape, seqlens):
     if kda:
         m32 = 12 * ksl * 3 + 4 * (4 * ksl * 2 * 3 + 6 * 3)
         m16 = 4 * 10 * 3 + 4 * kdt * 4 * 3
+        steps = chunks
     else:
-        m32 = 20 * ksl * 3 + 4 * (4 * ksl * 2 * 3 + 6 * 3 + kdt * 2 * 3)
-        m16 = 4 * 10 * 3 + 4 * 8 * 3
-    issued = (m32 * 16 * 16 * 32 * 2 + m16 * 16 * 16 * 16 * 2) * chunks * Hv * nblk
+        m32 = 6 * ksl * 3 + 4 * (2 * ksl * 2 * 3 + 2 * 3 + kdt * 3)
+        m16 = 4 * 3 * 3 + 2 * 8 * 3
+        steps = sum(-(-L // 32) for L in seqlens)
+    issued = (m32 * 16 * 16 * 32 * 2 + m16 * 16 * 16 * 16 * 2) * steps * Hv * nblk
     return nbytes, flops, issued
 
 
@@ -477,8 +480,7 @@ def bench_prefill(torch, gdn, synth, K=10, W=2, seqlens=(8192,) * 4, shape=None)
     rec["mfma_issued_tflops"] = round(issued / (ms * 1e-3) / 1e12, 1)
     rec["mfma_issued_frac_of_bf16_peak"] = round(issued / (ms * 1e-3) / 1e12 /
                                                  MFMA_BF16_PEAK_TFLOPS, 4)
-    if kda:
-        rec["workspace_bytes"] = int(need)
+    rec["workspace_bytes"] = int(need)
     return rec
 
 

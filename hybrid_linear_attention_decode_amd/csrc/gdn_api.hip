@@ -342,9 +342,9 @@ size_t gdn_prefill_workspace_size(const gdn_layer* L, int32_t N, int32_t max_seq
                                   int32_t total_tokens, int32_t chunk) {
   if (check_layer(L) != GDN_OK || N < 0 || max_seqlen < 0 || total_tokens < 0 || chunk != 64)
     return 0;
-  // The scalar-decay kernel keeps every intermediate in registers and LDS;
-  // the per-channel one stores the diagonal blocks of each chunk.
-  if (L->gate != GDN_GATE_CHANNEL) return 0;
+  // The scalar-decay prefill stores the prepared q / k rows (computed once
+  // per key head); the per-channel one the diagonal blocks of each chunk.
+  if (L->gate != GDN_GATE_CHANNEL) return gdn::qk_workspace_bytes(L->n_k_heads, L->d_k, total_tokens);
   return gdn::kda_workspace_bytes(L->n_v_heads, N, total_tokens);
 }
 
@@ -400,9 +400,10 @@ gdn_status gdn_prefill_chunked(const gdn_layer* L, const gdn_pool* P, const int3
     }
   }
   const bool kda = L->gate == GDN_GATE_CHANNEL;
-  if (kda && total_tokens > 0) {
-    if (in->alpha && !aligned16(in->alpha)) return GDN_ERR_BAD_SHAPE;
-    const size_t need = gdn::kda_workspace_bytes(L->n_v_heads, N, total_tokens);
+  if (kda && total_tokens > 0 && in->alpha && !aligned16(in->alpha)) return GDN_ERR_BAD_SHAPE;
+  if (total_tokens > 0) {
+    const size_t need = kda ? gdn::kda_workspace_bytes(L->n_v_heads, N, total_tokens)
+                            : gdn::qk_workspace_bytes(L->n_k_heads, L->d_k, total_tokens);
     if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255))
       return GDN_ERR_WORKSPACE;
   }
@@ -442,7 +443,7 @@ gdn_status gdn_prefill_chunked(const gdn_layer* L, const gdn_pool* P, const int3
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   if (kda)
     return from_hip(gdn::launch_prefill_kda(a, L->d_k, L->act_dtype == GDN_BF16, max_seqlen, hs));
-  return from_hip(gdn::launch_prefill(a, L->d_k, L->act_dtype == GDN_BF16, hs));
+  return from_hip(gdn::launch_prefill(a, L->d_k, L->act_dtype == GDN_BF16, max_seqlen, hs));
 }
 
 }  // extern "C"

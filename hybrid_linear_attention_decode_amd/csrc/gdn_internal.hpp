@@ -83,7 +83,8 @@ struct PrefillArgs {
   const void* w;             // [C][W]
   const void* bias;          // [C] or nullptr
   float* out;                // [total][Hv][dv]
-  void* ws;                  // per-channel decay: diagonal-block records (workspace)
+  void* ws;                  // workspace: prepared q / k rows (scalar decay) or
+                             // diagonal-block records (per-channel decay)
   const int32_t* ckpt;       // [N][ckpt_per_seq] checkpoint slots, or nullptr
   int32_t ckpt_every;        // tokens between checkpoints (a multiple of the chunk)
   int32_t ckpt_per_seq;
@@ -94,11 +95,14 @@ struct PrefillArgs {
 hipError_t launch_decode(const DecodeArgs& a, int dk, int act_bf16, int kda, hipStream_t s);
 hipError_t launch_slots(const SlotArgs& a, SlotMode mode, hipStream_t s);
 hipError_t launch_commit_index(const CommitIndexArgs& a, hipStream_t s);
-hipError_t launch_prefill(const PrefillArgs& a, int dk, int act_bf16, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, int dk, int act_bf16, int max_seqlen,
+                          hipStream_t s);
 hipError_t launch_prefill_kda(const PrefillArgs& a, int dk, int act_bf16, int max_seqlen,
                               hipStream_t s);
 // Workspace bytes of the per-channel-decay prefill for N sequences of total tokens.
 size_t kda_workspace_bytes(int Hv, int64_t N, int64_t total);
+// Workspace bytes of the scalar-decay prefill: the prepared q / k rows.
+size_t qk_workspace_bytes(int Hk, int dk, int64_t total);
 
 // Rows of state per wave of the decode kernel for a shape; 0 when unsupported.
 int decode_rows_per_wave(int dk, int G, int dv, int W1, int kda);

@@ -14,25 +14,24 @@
 // of (I + A) are inverted in fp32, and U is formed block row by block row,
 // U_b = X_bb (b_b R_b - sum_{j<b} A_bj U_j).
 //
-// Work split.  Rows of S are independent through the whole recurrence (row
-// i of S, U and O depend only on row i of S0), so a workgroup owns one
+// Two kernels.  The first prepares q and k once per key head: conv1d +
+// SiLU + L2 norm (+ q scale), split into bf16 (hi, lo) rows in a workspace.
+// In the second, rows of S are independent through the whole recurrence
+// (row i of S, U and O depend only on row i of S0), so a workgroup owns one
 // (sequence, value head, 64 value columns) and walks that sequence's chunks
 // in order, its 64 x d_k slice of S^T held in MFMA accumulators across
-// chunks.  Its 8 waves form a two-stage pipeline over double-buffered LDS
-// (every per-chunk plane has two copies, chunks alternate between them):
-//   producers (waves 0-3) build chunk c + 1 while chunk c is consumed:
-//     raw inputs prefetched a further chunk ahead; conv1d + SiLU + L2 norm
-//     (8 channels x 4 tokens per thread) into bf16 (hi, lo) pairs; the value
-//     conv; gates and log-decay prefix sums; then, after the mid-chunk
-//     barrier, the lower 16x16 tiles of K K^T and Q K^T (-> A and P) and the
-//     inverses of the diagonal blocks of (I + A) -- with N strictly lower
-//     triangular, (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8), and
-//     K K^T is symmetric, so both operand layouts of N come from the one
-//     accumulator tile;
-//   consumers (waves 4-7), 16 value columns each: K S0^T, Q S0^T and U
-//     before the mid-chunk barrier, O and the state update after it.
-// Two barriers per chunk: the producers' stores of chunk c + 1 sit before
-// the first, the A / P tiles they form from them before the second.
+// chunks.  Its 8 waves form a pipeline over LDS buffers that rotate by chunk
+// (K, Q, V^T and gates: three; P and A: two), with one barrier per chunk.
+// Between barriers c - 1 and c:
+//   consumers (waves 4-7), 16 value columns each, run chunk c: K S0^T,
+//     Q S0^T, U, O and the state update; wave 7 also writes chunk c + 2's
+//     gates (log-decay prefix sums) from inputs loaded a chunk ahead;
+//   producers (waves 0-3) copy chunk c + 2's prepared K, Q rows into LDS with
+//     its value conv, and form chunk c + 1's A and P from the lower 16x16
+//     tiles of K K^T and Q K^T, with the inverses of the diagonal blocks of
+//     (I + A): for N strictly lower triangular, (I + N)^{-1} = (I - N)
+//     (I + N^2)(I + N^4)(I + N^8), and K K^T is symmetric, so both operand
+//     layouts of N come from the one accumulator tile.
 // Every product runs on v_mfma_f32_16x16x{32,16}_bf16 with each fp32
 // operand split as x ~= hi + lo (two bf16), and a*b ~= ah*bh + ah*bl + al*bh
 // accumulated in fp32: about 16 significant bits per operand, which keeps
@@ -54,31 +53,144 @@ constexpr int kT = 32;         // chunk length (tokens)
 constexpr int kNb = kT / 16;   // 16-token blocks per chunk
 constexpr int kTpt = kT / 8;   // tokens per producer thread
 
-// LDS plan (bytes): two buffers of per-chunk planes, then the conv taps.
-// P, A and V^T rows are padded by 16 bytes so that 16 lanes reading 16
-// consecutive rows hit distinct banks; K and Q rows follow QkRow.  The K and
-// Q planes are staggered by 64 bytes.
+// LDS plan (bytes).  Chunk c's planes sit in buffer c % 3 (K, Q, V^T and
+// gates) or c % 2 (P and A): while the consumers read chunk c, the producers
+// form chunk c + 1's P and A from its K, Q and gates (stored an iteration
+// earlier) and store chunk c + 2's K, Q and V^T.  P, A and V^T rows are
+// padded by 16 bytes so that 16 lanes reading 16 consecutive rows hit
+// distinct banks; K and Q rows follow QkRow; K and Q planes are staggered by
+// 64 bytes.
 template <int DK>
 struct Plan {
   static constexpr int kRowQK = QkRow<DK>::kElems;  // bf16 per row of K, Q   [token][dk]
   static constexpr int kRowT = kT + 8;   // bf16 per row of P, A   [token][token]
   static constexpr int kRowV = kT + 4;   // fp32 per row of V^T    [value column][token]
-  static constexpr int kQK = 2 * kT * kRowQK + 64;
-  static constexpr int kSq = 2 * kT * kRowT;
-  // offsets inside one buffer
-  static constexpr int bKh = 0, bKl = bKh + kQK, bQh = bKl + kQK, bQl = bQh + kQK;
-  static constexpr int bPh = bQl + kQK, bPl = bPh + kSq, bAh = bPl + kSq, bAl = bAh + kSq;
-  static constexpr int bGate = bAl + kSq;  // fp32 [4][kT]: g, b, e^g, e^{g_c - g}
-  static constexpr int bV = bGate + 4 * kT * 4;
-  static constexpr int kBuf = bV + kCols * kRowV * 4;
-  // conv taps (4, left-padded) and bias of the workgroup's channels: q, k of
-  // the key head, then the 64 value columns
-  static constexpr int kWch = 2 * DK + kCols;
-  static constexpr int oW = 2 * kBuf;
+  static constexpr int kQK = 2 * kT * kRowQK + 64;   // one K or Q plane
+  static constexpr int kSq = 2 * kT * kRowT;         // one P or A plane
+  static constexpr int kVt = kCols * kRowV * 4;      // V^T
+  static constexpr int kGt = 4 * kT * 4;             // fp32 [4][kT]: g, b, e^g, e^{g_c - g}
+  static constexpr int oKQ = 0;                      // [3][Kh, Kl, Qh, Ql]
+  static constexpr int oPA = oKQ + 3 * 4 * kQK;      // [2][Ph, Pl, Ah, Al]
+  static constexpr int oV = oPA + 2 * 4 * kSq;       // [3]
+  static constexpr int oG = oV + 3 * kVt;            // [3]
+  // conv taps (4, left-padded) and bias of the workgroup's 64 value columns
+  static constexpr int kWch = kCols;
+  static constexpr int oW = oG + 3 * kGt;
   static constexpr int oB = oW + kWch * 16;
   static constexpr int kBytes = oB + kWch * 4;
-  // Plane at in-buffer offset `o` of buffer `buf` (0 or 1).
-  __device__ static int at(int buf, int o) { return buf * kBuf + o; }
+  enum { Kh = 0, Kl = 1, Qh = 2, Ql = 3 };   // planes of a K / Q buffer
+  enum { Ph = 0, Pl = 1, Ah = 2, Al = 3 };   // planes of a P / A buffer
+  __device__ static int kq(int c, int plane) { return oKQ + ((c % 3) * 4 + plane) * kQK; }
+  __device__ static int pa(int c, int plane) { return oPA + ((c & 1) * 4 + plane) * kSq; }
+  __device__ static int v(int c) { return oV + (c % 3) * kVt; }
+  __device__ static int gate(int c) { return oG + (c % 3) * kGt; }
+};
+
+// Prepared q / k rows in the workspace: [token][H_k][q | k][hi | lo][DK]
+// bf16, each row in storage-slot order (the order of K and Q rows in LDS
+// before the swizzle).  A descriptor covers the rows of one chunk of a
+// sequence (rows past the sequence read zero); offsets are in bytes.
+template <int DK>
+__device__ __forceinline__ rsrc_t qk_rows(const PrefillArgs& a, int t0, int T, int c0, int n) {
+  const int64_t row = static_cast<int64_t>(a.Hk) * 4 * DK;   // bf16 per token
+  const int rows = T - c0 < n ? (T > c0 ? T - c0 : 0) : n;
+  return make_rsrc(static_cast<const short*>(a.ws) + (static_cast<int64_t>(t0) + c0) * row,
+                   static_cast<uint32_t>(rows * row * 2));
+}
+template <int DK>
+__device__ __forceinline__ int qk_off(const PrefillArgs& a, int r, int hk, bool isk, int lo, int sl) {
+  return (((r * a.Hk + hk) * 4 + (isk ? 2 : 0) + lo) * DK + sl) * 2;
+}
+
+// The q / k preparation pass (its own kernel, before the main one): one
+// workgroup per (sequence, 32-token chunk, key head), thread (co, tau):
+// channel octet co of q | k (q first), tokens 4 tau..+3 -- conv1d + SiLU +
+// L2 norm (+ q scale), split into bf16 (hi, lo).  Once per key head, where
+// the main kernel's workgroups that share the key head would each repeat it.
+template <int DK, typename Act>
+struct QkPrep : PrefillCore<DK, Act> {
+  GDN_PREFILL_CORE(DK, Act);
+  static constexpr int kNco = DK / 4;   // channel octets of q and k
+  static constexpr int kGrp = DK / 8;   // octets per head (lanes of one norm)
+  static constexpr int kRaw = kTpt + 3; // raw rows per thread
+
+  // Raw rows 4 tau - 3 .. 4 tau + 3 of chunk c0 for the thread's channels.
+  __device__ __forceinline__ void load(Row8<Act> (&raw)[kRaw], int c0, int tau, int ch) const {
+    const rsrc_t rx = x_rows(c0);
+#pragma unroll
+    for (int r = 0; r < kRaw; ++r) raw[r].load(rx, x_off(c0, c0 + kTpt * tau - 3 + r, ch));
+    if (c0 == 0) {
+      // rows -3..-1 (thread tokens 0..2 of token group 0) from the window;
+      // every other offset lies past the window and reads zero
+      const rsrc_t rw = win_rows();
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {
+        Row8<Act> wr;
+        wr.load(rw, win_off(kTpt * tau - 3 + r, ch));
+        raw[r].merge(wr);
+      }
+    }
+  }
+
+  // Chunks first, first + step, ... of the sequence, the next one's rows
+  // loaded while the current one is computed.
+  __device__ void run(int first, int step) const {
+    if (tid >= 8 * kNco) return;        // whole 16-lane groups drop out together
+    const int co = tid % kNco, tau = tid / kNco;
+    const bool isk = co >= kGrp;
+    const int oc = isk ? co - kGrp : co;
+    const int ch = (isk ? a.Hk * DK : 0) + hk * DK + 8 * oc;
+    if (first * kT >= T) return;
+    f4 wt[8];
+    float bias[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      wt[m] = f4{tap(ch + m, 0), tap(ch + m, 1), tap(ch + m, 2), tap(ch + m, 3)};
+      bias[m] = a.bias ? to_f32(static_cast<const Act*>(a.bias)[ch + m]) : 0.f;
+    }
+    short* ws = static_cast<short*>(a.ws);
+    const int sb = slot(8 * oc);
+    Row8<Act> raw[kRaw], nxt[kRaw];
+    load(raw, first * kT, tau, ch);
+    for (int c = first; c * kT < T; c += step) {
+      const int c0 = c * kT;
+      const bool more = (c + step) * kT < T;
+      if (more) load(nxt, (c + step) * kT, tau, ch);
+#pragma unroll
+      for (int tt = 0; tt < kTpt; ++tt) {
+        float y[8], ss = 0.f;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          float v = bias[m];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) v = fmaf(wt[m][jj], raw[tt + jj].get(m), v);
+          v = act(v);
+          y[m] = v;
+          ss = fmaf(v, v, ss);
+        }
+        const float sum = group_sum<kGrp>(ss);
+        float sc = a.l2norm ? rsqrtf(sum + a.eps) : 1.0f;
+        if (!isk) sc *= a.q_scale;
+        const int tok = c0 + kTpt * tau + tt;
+        if (tok < T) {
+          s4 h0, l0, h1, l1;
+          split4(f4{y[0], y[1], y[2], y[3]} * sc, h0, l0);
+          split4(f4{y[4], y[5], y[6], y[7]} * sc, h1, l1);
+          short* hi = ws + ((static_cast<int64_t>(t0) + tok) * a.Hk + hk) * 4 * DK +
+                      (isk ? 2 : 0) * DK;
+          short* lo = hi + DK;
+          *reinterpret_cast<s4*>(hi + sb) = h0;
+          *reinterpret_cast<s4*>(hi + sb + 8) = h1;
+          *reinterpret_cast<s4*>(lo + sb) = l0;
+          *reinterpret_cast<s4*>(lo + sb + 8) = l1;
+        }
+      }
+      if (more) {
+#pragma unroll
+        for (int r = 0; r < kRaw; ++r) raw[r] = nxt[r];
+      }
+    }
+  }
 };
 
 template <int DK, typename Act>
@@ -97,9 +209,8 @@ struct Prefill : PrefillCore<DK, Act> {
   // ================= producers =================
   // Thread (co, tau): channel octet co of q|k (q first), tokens 4 tau..+3.
   struct Prod {
-    Row8<Act> raw[kRaw];        // rows 4 tau - 3 .. 4 tau + 3 of a chunk
-    s4 hi[kTpt][2], lo[kTpt][2];  // the chunk's normalised rows, not yet stored
-    int co, tau, ch, oc;
+    s4 hi[kTpt][2], lo[kTpt][2];  // the next chunk's prepared rows, not yet stored
+    int co, tau, oc;
     bool isk, on;
     // value conv: channels 2 vp, 2 vp + 1 of the column block, tokens 4 vt..+3
     uint32_t vraw[kRaw][sizeof(Act) == 2 ? 1 : 2];
@@ -114,28 +225,19 @@ struct Prefill : PrefillCore<DK, Act> {
     p.tau = tid / kNco;
     p.isk = p.co >= kGrp;
     p.oc = p.isk ? p.co - kGrp : p.co;
-    p.ch = (p.isk ? a.Hk * DK : 0) + hk * DK + 8 * p.oc;
     p.vp = tid % 32;
     p.vt = tid / 32;
     p.von = e0 + 2 * p.vp < a.dv;
     p.vch = 2 * a.Hk * DK + h * a.dv + e0 + 2 * p.vp;
   }
 
-  // Taps and bias of the workgroup's channels into LDS (all threads).
+  // Taps and bias of the workgroup's value columns into LDS (all threads).
   __device__ void load_taps() const {
     float* wt = fp(P::oW);
     float* bs = fp(P::oB);
     for (int i = tid; i < P::kWch; i += kThreads) {
-      int ch;
-      bool ok = true;
-      if (i < DK)
-        ch = hk * DK + i;
-      else if (i < 2 * DK)
-        ch = a.Hk * DK + hk * DK + (i - DK);
-      else {
-        ch = 2 * a.Hk * DK + h * a.dv + e0 + (i - 2 * DK);
-        ok = e0 + (i - 2 * DK) < a.dv;
-      }
+      const int ch = 2 * a.Hk * DK + h * a.dv + e0 + i;
+      const bool ok = e0 + i < a.dv;
       f4 t = {0.f, 0.f, 0.f, 0.f};
       if (ok) t = f4{tap(ch, 0), tap(ch, 1), tap(ch, 2), tap(ch, 3)};
       *reinterpret_cast<f4*>(wt + 4 * i) = t;
@@ -143,13 +245,25 @@ struct Prefill : PrefillCore<DK, Act> {
     }
   }
 
+  // Prepared q / k rows of chunk c0 (the thread's two 4-channel groups of
+  // each of its tokens, hi and lo) and the raw value inputs.
   __device__ __forceinline__ void prod_load(Prod& p, int c0) const {
-    const rsrc_t rx = x_rows(c0);
-    const int tau = opaque(p.tau), ch = opaque(p.ch), vt = opaque(p.vt), vch = opaque(p.vch);
+    const int tau = opaque(p.tau), vt = opaque(p.vt), vch = opaque(p.vch);
     if (p.on) {
+      typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+      const rsrc_t rq = qk_rows<DK>(a, t0, T, c0, kT);
+      const int sb = slot(8 * opaque(p.oc));
 #pragma unroll
-      for (int r = 0; r < kRaw; ++r) p.raw[r].load(rx, x_off(c0, c0 + kTpt * tau - 3 + r, ch));
+      for (int tt = 0; tt < kTpt; ++tt) {
+        const int oh = qk_off<DK>(a, kTpt * tau + tt, hk, p.isk, 0, sb);
+        const int ol = qk_off<DK>(a, kTpt * tau + tt, hk, p.isk, 1, sb);
+        p.hi[tt][0] = __builtin_bit_cast(s4, __builtin_amdgcn_raw_buffer_load_b64(rq, oh, 0, 0));
+        p.hi[tt][1] = __builtin_bit_cast(s4, __builtin_amdgcn_raw_buffer_load_b64(rq, oh + 16, 0, 0));
+        p.lo[tt][0] = __builtin_bit_cast(s4, __builtin_amdgcn_raw_buffer_load_b64(rq, ol, 0, 0));
+        p.lo[tt][1] = __builtin_bit_cast(s4, __builtin_amdgcn_raw_buffer_load_b64(rq, ol + 16, 0, 0));
+      }
     }
+    const rsrc_t rx = x_rows(c0);
     if (p.von) {
 #pragma unroll
       for (int r = 0; r < kRaw; ++r) {
@@ -168,14 +282,6 @@ struct Prefill : PrefillCore<DK, Act> {
       // rows -3..-1 (thread tokens 0..2 of token group 0) from the window;
       // every other offset lies past the window and reads zero
       const rsrc_t rw = win_rows();
-      if (p.on) {
-#pragma unroll
-        for (int r = 0; r < 3; ++r) {
-          Row8<Act> wr;
-          wr.load(rw, win_off(kTpt * tau - 3 + r, ch));
-          p.raw[r].merge(wr);
-        }
-      }
       if (p.von) {
 #pragma unroll
         for (int r = 0; r < 3; ++r) {
@@ -193,39 +299,10 @@ struct Prefill : PrefillCore<DK, Act> {
     }
   }
 
-  // conv + SiLU + L2 norm (+ q scale) of the prefetched rows of chunk c0.
+  // The value conv (+ SiLU) of the prefetched inputs of chunk c0.
   __device__ void prod_prep(Prod& p, int c0) const {
     const float* wl = fp(P::oW);
     const float* bl = fp(P::oB);
-    if (p.on) {
-      f4 wt[8];
-      float bias[8];
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        wt[m] = *reinterpret_cast<const f4*>(wl + 4 * (8 * p.co + m));
-        bias[m] = bl[8 * p.co + m];
-      }
-#pragma unroll
-      for (int tt = 0; tt < kTpt; ++tt) {
-        float y[8], ss = 0.f;
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          float v = bias[m];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-            v = fmaf(wt[m][jj], p.raw[tt + jj].get(m), v);
-          v = act(v);
-          y[m] = v;
-          ss = fmaf(v, v, ss);
-        }
-        const float sum = group_sum<kGrp>(ss);
-        float sc = a.l2norm ? rsqrtf(sum + a.eps) : 1.0f;
-        if (!p.isk) sc *= a.q_scale;
-        if (c0 + kTpt * p.tau + tt >= T) sc = 0.f;
-        split4(f4{y[0], y[1], y[2], y[3]} * sc, p.hi[tt][0], p.lo[tt][0]);
-        split4(f4{y[4], y[5], y[6], y[7]} * sc, p.hi[tt][1], p.lo[tt][1]);
-      }
-    }
     if (p.von) {
       float xr[kRaw][2];
 #pragma unroll
@@ -240,8 +317,8 @@ struct Prefill : PrefillCore<DK, Act> {
       }
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        const f4 vw = *reinterpret_cast<const f4*>(wl + 4 * (2 * DK + 2 * p.vp + m));
-        const float vb = bl[2 * DK + 2 * p.vp + m];
+        const f4 vw = *reinterpret_cast<const f4*>(wl + 4 * (2 * p.vp + m));
+        const float vb = bl[2 * p.vp + m];
 #pragma unroll
         for (int tt = 0; tt < kTpt; ++tt) {
           float y = vb;
@@ -281,12 +358,12 @@ struct Prefill : PrefillCore<DK, Act> {
     return r;
   }
 
-  // The gates of a chunk into buffer buf (one wave, token = lane < kT):
+  // The gates of chunk c into its buffer (one wave, token = lane < kT):
   // g = prefix sums of log a over the chunk, b, e^g and e^{g_c - g}; tokens
   // past the sequence take a = 1, b = 0 and add nothing.  The scan runs
   // inside each row of 16 lanes (DPP shifts, zero filled), then row 1 adds
   // row 0's total.
-  __device__ void gates(const GateIn& in, int buf) const {
+  __device__ void gates(const GateIn& in, int c) const {
     const bool valid = lane < kT && in.c0 + lane < T;
     const float al = valid ? __uint_as_float(sizeof(Act) == 2 ? in.al << 16 : in.al) : 1.f;
     const float bt = valid ? __uint_as_float(sizeof(Act) == 2 ? in.bt << 16 : in.bt) : 0.f;
@@ -299,7 +376,7 @@ struct Prefill : PrefillCore<DK, Act> {
     if (lane >= 16) g += r0;
     const float gc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), kT - 1));
     if (lane < kT) {
-      float* gt = fp(P::at(buf, P::bGate));
+      float* gt = fp(P::gate(c));
       gt[lane] = g;
       gt[kT + lane] = bt;
       gt[2 * kT + lane] = expf(g);
@@ -307,12 +384,12 @@ struct Prefill : PrefillCore<DK, Act> {
     }
   }
 
-  // Store the prepared chunk into buffer buf: rows of K or Q (two groups of
-  // 4 channels at slot(8 oc) and +8) and the value columns.
-  __device__ void prod_store(const Prod& p, int buf) const {
+  // Store prepared chunk c: rows of K or Q (two groups of 4 channels at
+  // slot(8 oc) and +8) and the value columns.
+  __device__ void prod_store(const Prod& p, int c) const {
     if (p.on) {
-      short* hi = sp(P::at(buf, p.isk ? P::bKh : P::bQh));
-      short* lo = sp(P::at(buf, p.isk ? P::bKl : P::bQl));
+      short* hi = sp(P::kq(c, p.isk ? P::Kh : P::Qh));
+      short* lo = sp(P::kq(c, p.isk ? P::Kl : P::Ql));
       const int tau = opaque(p.tau);
       const int sb = slot(8 * opaque(p.oc));
 #pragma unroll
@@ -325,7 +402,7 @@ struct Prefill : PrefillCore<DK, Act> {
       }
     }
     if (p.von) {
-      float* vt = fp(P::at(buf, P::bV));
+      float* vt = fp(P::v(c));
       const int vp = opaque(p.vp), vtk = opaque(p.vt);
 #pragma unroll
       for (int m = 0; m < 2; ++m)
@@ -348,11 +425,11 @@ struct Prefill : PrefillCore<DK, Act> {
   // IB) so that each lane holds row r = 16 IB + lr at the four columns
   // 16 JB + 4 lg + v: they store as one 8-byte (hi, lo) group each.
   template <int IB, int JB, bool G, bool PQ>
-  __device__ __forceinline__ void tiles(f4& g, f4& pq, const int (&ob)[kSl], int buf) const {
-    const short* kh = sp(P::at(buf, P::bKh));
-    const short* kl = sp(P::at(buf, P::bKl));
-    const short* qh = sp(P::at(buf, P::bQh));
-    const short* ql = sp(P::at(buf, P::bQl));
+  __device__ __forceinline__ void tiles(f4& g, f4& pq, const int (&ob)[kSl], int c) const {
+    const short* kh = sp(P::kq(c, P::Kh));
+    const short* kl = sp(P::kq(c, P::Kl));
+    const short* qh = sp(P::kq(c, P::Qh));
+    const short* ql = sp(P::kq(c, P::Ql));
     // two accumulators per product (even and odd slices) halve the chain
     // of dependent MFMAs
     f4 gs[2], ps[2];
@@ -396,9 +473,9 @@ struct Prefill : PrefillCore<DK, Act> {
 
   // P_ri = e^{g_r - g_i} q_r.k_i (i <= r) from a transposed Q K^T tile.
   template <int IB, int JB>
-  __device__ __forceinline__ void store_p(const f4& pq, int buf) const {
+  __device__ __forceinline__ void store_p(const f4& pq, int c) const {
     const int l = lane_now(), lr = l & 15, lg = l >> 4;
-    const float* gt = fp(P::at(buf, P::bGate));
+    const float* gt = fp(P::gate(c));
     const int o = (16 * IB + lr) * P::kRowT + slot(16 * JB + 4 * lg);
     f4 pv = decays<IB, JB>(gt) * pq;
     if (IB == JB) {
@@ -408,29 +485,29 @@ struct Prefill : PrefillCore<DK, Act> {
     }
     s4 h, lo;
     split4(pv, h, lo);
-    *reinterpret_cast<s4*>(sp(P::at(buf, P::bPh)) + o) = h;
-    *reinterpret_cast<s4*>(sp(P::at(buf, P::bPl)) + o) = lo;
+    *reinterpret_cast<s4*>(sp(P::pa(c, P::Ph)) + o) = h;
+    *reinterpret_cast<s4*>(sp(P::pa(c, P::Pl)) + o) = lo;
   }
 
   // A_ri = b_r e^{g_r - g_i} k_r.k_i (IB > JB) from a transposed K K^T tile.
   template <int IB, int JB>
-  __device__ __forceinline__ void store_a(const f4& g, int buf) const {
+  __device__ __forceinline__ void store_a(const f4& g, int c) const {
     const int l = lane_now(), lr = l & 15, lg = l >> 4;
-    const float* gt = fp(P::at(buf, P::bGate));
+    const float* gt = fp(P::gate(c));
     const int r = 16 * IB + lr;
     const int o = r * P::kRowT + slot(16 * JB + 4 * lg);
     s4 h, lo;
     split4(gt[kT + r] * decays<IB, JB>(gt) * g, h, lo);
-    *reinterpret_cast<s4*>(sp(P::at(buf, P::bAh)) + o) = h;
-    *reinterpret_cast<s4*>(sp(P::at(buf, P::bAl)) + o) = lo;
+    *reinterpret_cast<s4*>(sp(P::pa(c, P::Ah)) + o) = h;
+    *reinterpret_cast<s4*>(sp(P::pa(c, P::Al)) + o) = lo;
   }
 
   // Diagonal block b from its raw K K^T tile G: N = the strictly lower block
   // of A, X = (I + N)^{-1}, stored in A layout (X[lr][4 lg + v]) in the
   // diagonal block of the A planes.
-  __device__ void diag_inverse(int b, const f4& G, int buf) const {
+  __device__ void diag_inverse(int b, const f4& G, int c) const {
     const int l = lane_now(), lr = l & 15, lg = l >> 4;
-    const float* gt = fp(P::at(buf, P::bGate));
+    const float* gt = fp(P::gate(c));
     const float gi = gt[16 * b + lr], bi = gt[kT + 16 * b + lr];
     const f4 gr = *reinterpret_cast<const f4*>(gt + 16 * b + 4 * lg);
     const f4 br = *reinterpret_cast<const f4*>(gt + kT + 16 * b + 4 * lg);
@@ -445,52 +522,52 @@ struct Prefill : PrefillCore<DK, Act> {
     s4 xh, xl;
     split4(xt, xh, xl);
     const int o = (16 * b + lr) * P::kRowT + slot(16 * b + 4 * lg);
-    *reinterpret_cast<s4*>(sp(P::at(buf, P::bAh)) + o) = xh;
-    *reinterpret_cast<s4*>(sp(P::at(buf, P::bAl)) + o) = xl;
+    *reinterpret_cast<s4*>(sp(P::pa(c, P::Ah)) + o) = xh;
+    *reinterpret_cast<s4*>(sp(P::pa(c, P::Al)) + o) = xl;
   }
 
-  // The chunk in buffer buf over the 4 producer waves: waves 0 and 1 the
+  // A, P and the inverses of chunk c over the 4 producer waves: waves 0 and 1 the
   // diagonal K K^T tiles and their inverses, wave 2 the diagonal Q K^T
   // tiles, wave 3 the off-diagonal pair.
-  __device__ void gram_phase(int buf) const {
+  __device__ void gram_phase(int c) const {
     int ob[kSl];
     op_bases(ob);
     f4 g, pq;
     switch (wave) {
       case 0:
-        tiles<0, 0, true, false>(g, pq, ob, buf);
-        diag_inverse(0, g, buf);
+        tiles<0, 0, true, false>(g, pq, ob, c);
+        diag_inverse(0, g, c);
         break;
       case 1:
-        tiles<1, 1, true, false>(g, pq, ob, buf);
-        diag_inverse(1, g, buf);
+        tiles<1, 1, true, false>(g, pq, ob, c);
+        diag_inverse(1, g, c);
         break;
       case 2:
-        tiles<0, 0, false, true>(g, pq, ob, buf);
-        store_p<0, 0>(pq, buf);
-        tiles<1, 1, false, true>(g, pq, ob, buf);
-        store_p<1, 1>(pq, buf);
+        tiles<0, 0, false, true>(g, pq, ob, c);
+        store_p<0, 0>(pq, c);
+        tiles<1, 1, false, true>(g, pq, ob, c);
+        store_p<1, 1>(pq, c);
         break;
       default:
-        tiles<1, 0, true, true>(g, pq, ob, buf);
-        store_a<1, 0>(g, buf);
-        store_p<1, 0>(pq, buf);
+        tiles<1, 0, true, true>(g, pq, ob, c);
+        store_a<1, 0>(g, c);
+        store_p<1, 0>(pq, c);
         break;
     }
   }
 
   // ================= consumers =================
-  // First half of chunk c0 (buffer buf) for the wave's 16 value columns:
+  // First half of chunk c for the wave's 16 value columns:
   // K S0^T, Q S0^T and the updates U.  S[d] holds rows 16d + 4 lg + v (key
   // index) of S^T at column e0 + lr (value index); U[b] and qs[b] rows
   // 16 b + 4 lg + v (token) at that column.
-  __device__ void updates(const f4 (&S)[kDt], f4 (&U)[kNb], f4 (&qs)[kNb], int buf) const {
+  __device__ void updates(const f4 (&S)[kDt], f4 (&U)[kNb], f4 (&qs)[kNb], int c) const {
     const int l = lane_now(), lr = l & 15, lg = l >> 4;
-    const float* gt = fp(P::at(buf, P::bGate));
-    const short* kh = sp(P::at(buf, P::bKh));
-    const short* kl = sp(P::at(buf, P::bKl));
-    const short* qh = sp(P::at(buf, P::bQh));
-    const short* ql = sp(P::at(buf, P::bQl));
+    const float* gt = fp(P::gate(c));
+    const short* kh = sp(P::kq(c, P::Kh));
+    const short* kl = sp(P::kq(c, P::Kl));
+    const short* qh = sp(P::kq(c, P::Qh));
+    const short* ql = sp(P::kq(c, P::Ql));
     // K S0^T and Q S0^T, rows 16 tb + 4 lg + v
     f4 ks[kNb];
 #pragma unroll
@@ -532,9 +609,9 @@ struct Prefill : PrefillCore<DK, Act> {
       }
     }
     // U_b = X_bb (b_b R_b - sum_{j<b} A_bj U_j),  R = V - e^g (K S0^T)
-    const float* vt = fp(P::at(buf, P::bV)) + (e0 % kCols + lr) * P::kRowV;
-    const short* ah_ = sp(P::at(buf, P::bAh));
-    const short* al_ = sp(P::at(buf, P::bAl));
+    const float* vt = fp(P::v(c)) + (e0 % kCols + lr) * P::kRowV;
+    const short* ah_ = sp(P::pa(c, P::Ah));
+    const short* al_ = sp(P::pa(c, P::Al));
     s4 uh[kNb], ul[kNb];
 #pragma unroll
     for (int b = 0; b < kNb; ++b) {
@@ -559,20 +636,21 @@ struct Prefill : PrefillCore<DK, Act> {
     }
   }
 
-  // Second half: O = e^g (Q S0^T) + P U to the output rows of chunk c0
+  // Second half: O = e^g (Q S0^T) + P U to the output rows of chunk c
   // (rows past the sequence lie past the descriptor and are dropped), then
   // S^T <- e^{g_c} S^T + K^T diag(e^{g_c - g}) U.
-  __device__ void outputs_and_state(int c0, f4 (&S)[kDt], const f4 (&U)[kNb],
-                                    const f4 (&qs)[kNb], int buf) const {
+  __device__ void outputs_and_state(f4 (&S)[kDt], const f4 (&U)[kNb], const f4 (&qs)[kNb],
+                                    int c) const {
+    const int c0 = c * kT;
     const int l = lane_now(), lr = l & 15, lg = l >> 4;
-    const float* gt = fp(P::at(buf, P::bGate));
+    const float* gt = fp(P::gate(c));
     s4 uh[kNb], ul[kNb];
 #pragma unroll
     for (int b = 0; b < kNb; ++b) split4(U[b], uh[b], ul[b]);
     const s8 u0h = cat(uh[0], uh[1]), u0l = cat(ul[0], ul[1]);
     {
-      const short* ph_ = sp(P::at(buf, P::bPh));
-      const short* pl_ = sp(P::at(buf, P::bPl));
+      const short* ph_ = sp(P::pa(c, P::Ph));
+      const short* pl_ = sp(P::pa(c, P::Pl));
       f4 o[kNb];
 #pragma unroll
       for (int b = 0; b < kNb; ++b) {
@@ -595,8 +673,8 @@ struct Prefill : PrefillCore<DK, Act> {
                                                 ((16 * b + 4 * lg + v) * rs + lr) * 4, 0, 0);
     }
     // The state update: K^T tiles by transposing reads of the K rows.
-    const short* kh = sp(P::at(buf, P::bKh));
-    const short* kl = sp(P::at(buf, P::bKl));
+    const short* kh = sp(P::kq(c, P::Kh));
+    const short* kl = sp(P::kq(c, P::Kl));
     s8 wh, wl;
     {
       const f4 g0 = *reinterpret_cast<const f4*>(gt + 3 * kT + 4 * lg);
@@ -677,37 +755,39 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
   const int nch = (k.T + kT - 1) / kT;
 
   // P and A planes of both buffers: the tiles above the diagonal stay zero.
-  for (int bf = 0; bf < 2; ++bf)
-    for (int i = k.tid; i < 4 * P::kSq / 16; i += kThreads)
-      reinterpret_cast<uint4*>(lds_raw + P::at(bf, P::bPh))[i] = uint4{0u, 0u, 0u, 0u};
+  for (int i = k.tid; i < 2 * 4 * P::kSq / 16; i += kThreads)
+    reinterpret_cast<uint4*>(lds_raw + P::oPA)[i] = uint4{0u, 0u, 0u, 0u};
   k.e0 = j * kCols;
   k.load_taps();
 
+  // One barrier per chunk.  Between barriers c - 1 and c the consumers run
+  // chunk c while the producers store chunk c + 2 and form chunk c + 1's A,
+  // P and inverses (its K, Q and gates were stored an iteration earlier), and
+  // one consumer wave writes chunk c + 2's gates.
   if (k.tid < kProd) {
     // ---------------- producers ----------------
     typename K::Prod p;
     k.prod_init(p);
     if (nch > 0) k.prod_load(p, 0);
     lds_barrier();            // planes zeroed, taps loaded
-    if (nch > 0) {
-      k.prod_prep(p, 0);
-      if (nch > 1) k.prod_load(p, kT);
-      k.prod_store(p, 0);
+    // (the prepared rows are loaded straight into the registers they are
+    // stored from: each chunk's store comes before the next chunk's load)
+    for (int c = 0; c < 2 && c < nch; ++c) {
+      k.prod_prep(p, c * kT);
+      k.prod_store(p, c);
+      if (c + 1 < nch) k.prod_load(p, (c + 1) * kT);
     }
-    lds_barrier();            // chunk 0 stored
+    lds_barrier();            // chunks 0 and 1 stored, their gates written
     if (nch > 0) k.gram_phase(0);
-    lds_barrier();            // chunk 0's A, P and inverses formed
+    lds_barrier();            // chunk 0 complete
     for (int c = 0; c < nch; ++c) {
-      const bool next = c + 1 < nch;
-      if (next) {
-        // buffer (c + 1) & 1: its last readers (chunk c - 1) are done
-        k.prod_prep(p, (c + 1) * kT);
-        if (c + 2 < nch) k.prod_load(p, (c + 2) * kT);
-        k.prod_store(p, (c + 1) & 1);
+      if (c + 2 < nch) {
+        k.prod_prep(p, (c + 2) * kT);
+        k.prod_store(p, c + 2);
+        if (c + 3 < nch) k.prod_load(p, (c + 3) * kT);
       }
-      lds_barrier();          // chunk c + 1 stored
-      if (next) k.gram_phase((c + 1) & 1);
-      lds_barrier();          // chunk c consumed, chunk c + 1 complete
+      if (c + 1 < nch) k.gram_phase(c + 1);
+      lds_barrier();          // chunk c consumed
     }
   } else {
     // ---------------- consumers ----------------
@@ -724,26 +804,24 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
                                            static_cast<int64_t>(k.e0 + k.lr) * DK + 16 * d +
                                            4 * k.lg);
     }
+    lds_barrier();            // planes zeroed, taps loaded
     typename K::GateIn gin{0u, 0u, 0};
-    if (k.wave == 7 && nch > 0) {
-      k.gates(k.gate_load(0), 0);
-      if (nch > 1) gin = k.gate_load(kT);
+    if (k.wave == 7) {
+      for (int c = 0; c < 2 && c < nch; ++c) k.gates(k.gate_load(c * kT), c);
+      if (nch > 2) gin = k.gate_load(2 * kT);
     }
-    lds_barrier();            // planes zeroed, taps loaded; chunk 0's gates
-    lds_barrier();            // chunk 0 stored
-    lds_barrier();            // chunk 0's A, P and inverses formed
+    lds_barrier();            // chunks 0 and 1 stored, their gates written
+    lds_barrier();            // chunk 0 complete
     for (int c = 0; c < nch; ++c) {
-      const int cb = c & 1;
       f4 U[kNb], qs[kNb];
-      if (cols) k.updates(S, U, qs, cb);
-      // the next chunk's gates, into the other buffer (its last readers,
-      // chunk c - 1, are done); then the inputs of the one after
-      if (k.wave == 7 && c + 1 < nch) {
-        k.gates(gin, cb ^ 1);
-        if (c + 2 < nch) gin = k.gate_load((c + 2) * kT);
+      if (cols) k.updates(S, U, qs, c);
+      // chunk c + 2's gates (their buffer's last readers, chunk c - 1 here
+      // and chunk c - 1's A and P, are done), then the inputs of the next
+      if (k.wave == 7 && c + 2 < nch) {
+        k.gates(gin, c + 2);
+        if (c + 3 < nch) gin = k.gate_load((c + 3) * kT);
       }
-      lds_barrier();          // (the producers' chunk c + 1 stores)
-      if (cols) k.outputs_and_state(c * kT, S, U, qs, cb);
+      if (cols) k.outputs_and_state(S, U, qs, c);
       const int32_t cs = __builtin_amdgcn_readfirstlane(ckpt_slot(a, s, (c + 1) * kT, k.T));
       if (cols && cs >= 0) {  // the state after (c + 1) * kT tokens, to a checkpoint slot
         const int l = k.lane_now();
@@ -763,10 +841,46 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
 
 
 template <int DK, typename Act>
-hipError_t launch_one(const PrefillArgs& a, hipStream_t st) {
+__global__ void __launch_bounds__(256) qk_prep_kernel(PrefillArgs a, int nchunk) {
+  const int hk = blockIdx.x % a.Hk;
+  const int first = (blockIdx.x / a.Hk) % nchunk;
+  const int s = blockIdx.x / a.Hk / nchunk;
+  const int t0 = a.cu[s], t1 = a.cu[s + 1];
+  const int32_t dst = a.dst[s];
+  const int32_t init = a.init ? a.init[s] : dst;
+  if (t0 < 0 || t1 < t0 || t1 > a.total || dst < 0 || dst >= a.num_slots || init >= a.num_slots)
+    return;
+  QkPrep<DK, Act> q{{a, nullptr}};
+  q.tid = threadIdx.x;
+  q.wave = __builtin_amdgcn_readfirstlane(q.tid >> 6);
+  q.lane = q.tid & 63;
+  q.lr = q.lane & 15;
+  q.lg = q.lane >> 4;
+  q.h = q.e0 = 0;
+  q.hk = hk;
+  q.t0 = t0;
+  q.T = t1 - t0;
+  q.init = init;
+  // chunks first, first + nchunk, ...: every chunk is covered whatever the
+  // grid assumed of the longest sequence
+  q.run(first, nchunk);
+}
+
+template <int DK, typename Act>
+hipError_t launch_one(const PrefillArgs& a, int max_seqlen, hipStream_t st) {
+  // About 8 workgroups per CU: each covers every nchunk-th chunk of its
+  // (sequence, key head), prefetching the next while computing one.
+  const int64_t per = static_cast<int64_t>(a.N) * a.Hk;
+  const int64_t want = 2048 / per > 0 ? 2048 / per : 1;
+  const int64_t most = max_seqlen > 0 ? (max_seqlen + kT - 1) / kT : 1;
+  const int64_t nchunk = want < most ? want : most;
+  hipLaunchKernelGGL((qk_prep_kernel<DK, Act>), dim3(static_cast<uint32_t>(nchunk * per)),
+                     dim3(256), 0, st, a, static_cast<int>(nchunk));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int bytes = Plan<DK>::kBytes;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<DK, Act>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<DK, Act>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
   const int grid = a.N * a.Hv * a.nblk;
   hipLaunchKernelGGL((prefill_kernel<DK, Act>), dim3(grid), dim3(kThreads), bytes, st, a);
@@ -786,12 +900,23 @@ int prefill_supported(int dk, int kda) {
   return dk == 32 || dk == 64 || dk == 128;
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, int dk, int act_bf16, hipStream_t s) {
+size_t qk_workspace_bytes(int Hk, int dk, int64_t total) {
+  return static_cast<size_t>(total) * Hk * dk * 8;
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int dk, int act_bf16, int max_seqlen,
+                          hipStream_t s) {
   if (a.N == 0) return hipSuccess;
   switch (dk) {
-    case 32: return act_bf16 ? launch_one<32, bf16>(a, s) : launch_one<32, float>(a, s);
-    case 64: return act_bf16 ? launch_one<64, bf16>(a, s) : launch_one<64, float>(a, s);
-    case 128: return act_bf16 ? launch_one<128, bf16>(a, s) : launch_one<128, float>(a, s);
+    case 32:
+      return act_bf16 ? launch_one<32, bf16>(a, max_seqlen, s)
+                      : launch_one<32, float>(a, max_seqlen, s);
+    case 64:
+      return act_bf16 ? launch_one<64, bf16>(a, max_seqlen, s)
+                      : launch_one<64, float>(a, max_seqlen, s);
+    case 128:
+      return act_bf16 ? launch_one<128, bf16>(a, max_seqlen, s)
+                      : launch_one<128, float>(a, max_seqlen, s);
   }
   return hipErrorInvalidValue;
 }

@@ -208,7 +208,9 @@ typedef struct {
  *   cu_seqlens [N+1] int32 (device), cu_seqlens[0] == 0, non-decreasing;
  *     max_seqlen (host) >= every length (it sizes a launch grid; a smaller
  *     value stays correct, only slower); total_tokens (host) == cu_seqlens[N].
- *   chunk: 64 (the only chunk length built).  d_k in {32, 64, 128}.
+ *   chunk: 64, the only value accepted: the granularity of checkpoints (the
+ *     scalar-decay kernel steps through 32-token blocks internally; results
+ *     do not depend on it beyond rounding).  d_k in {32, 64, 128}.
  *   in->alpha: [total][H_v] (scalar decay) or [total][H_v][d_k] (per-channel
  *     decay, 16-byte aligned).
  *   out [total][H_v][d_v] fp32.
@@ -217,9 +219,11 @@ typedef struct {
  *     the sequence bit for bit.
  *   workspace: device scratch of at least gdn_prefill_workspace_size() bytes,
  *     256-byte aligned, owned by the caller and free again when the call's
- *     stream work has finished (the scalar decay needs none; the per-channel
- *     decay stores its diagonal blocks there).  Missing, short or misaligned:
- *     GDN_ERR_WORKSPACE, nothing enqueued.
+ *     stream work has finished.  The scalar decay stores there the
+ *     normalised q and k rows (conv, SiLU, L2 norm; split into two bf16
+ *     halves), computed once per key head by a first kernel; the per-channel
+ *     decay its diagonal blocks.  Missing, short or misaligned (with
+ *     total_tokens > 0): GDN_ERR_WORKSPACE, nothing enqueued.
  */
 gdn_status gdn_prefill_chunked(const gdn_layer* layer, const gdn_pool* pool,
                                const int32_t* dst_slots, const int32_t* init_slot, int32_t N,
@@ -228,9 +232,9 @@ gdn_status gdn_prefill_chunked(const gdn_layer* layer, const gdn_pool* pool,
                                float* out, const gdn_prefill_ckpt* ckpt, void* workspace,
                                size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace gdn_prefill_chunked needs for these sizes: 0 for the
- * scalar decay; for the per-channel decay 2048 * H_v * (floor(total/16) +
- * 4 * min(N, total)).  0 on bad arguments. */
+/* Bytes of workspace gdn_prefill_chunked needs for these sizes: for the
+ * scalar decay 8 * total * H_k * d_k; for the per-channel decay 2048 * H_v *
+ * (floor(total/16) + 4 * min(N, total)).  0 on bad arguments. */
 size_t gdn_prefill_workspace_size(const gdn_layer* layer, int32_t N, int32_t max_seqlen,
                                   int32_t total_tokens, int32_t chunk);
 

@@ -195,8 +195,16 @@ def test_bad_prefill_arguments():
     assert prefill(L, N=0, ckpt=Ck(FAKE, 128, -1)) == gdn.GDN_ERR_BAD_SHAPE
     assert prefill(L, N=0, ckpt=Ck(None, 128, 4)) == gdn.GDN_ERR_NULL_ARG
     assert prefill(L, N=0, ckpt=Ck(None, 128, 0)) == gdn.GDN_OK
-    # the scalar-decay kernel keeps every intermediate on chip
-    assert gdn.lib().gdn_prefill_workspace_size(ct.byref(L), 4, 8192, 32768, 64) == 0
+    # the scalar-decay prefill stores the prepared q / k rows: 8 bytes per
+    # (token, key head, key channel); missing, short or misaligned is refused
+    size = gdn.lib().gdn_prefill_workspace_size
+    assert size(ct.byref(L), 4, 8192, 32768, 64) == 32768 * 16 * 128 * 8
+    assert size(ct.byref(L), 0, 0, 0, 64) == 0
+    need = size(ct.byref(L), 2, 64, 128, 64)
+    assert need == 128 * 16 * 128 * 8
+    assert prefill(L) == gdn.GDN_ERR_WORKSPACE
+    assert prefill(L, ws=FAKE, ws_bytes=need - 1) == gdn.GDN_ERR_WORKSPACE
+    assert prefill(L, ws=ct.c_void_p(0x10080), ws_bytes=need) == gdn.GDN_ERR_WORKSPACE
 
 
 def test_per_channel_prefill_workspace():
