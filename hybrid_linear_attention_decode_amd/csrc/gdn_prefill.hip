@@ -132,6 +132,47 @@ struct QkPrep : PrefillCore<DK, Act> {
     }
   }
 
+  // Taps (4, left-padded) and bias of channels ch..ch+7: for a width-4 conv
+  // with aligned arrays one 4-tap load per channel and one load for the 8
+  // biases, else element by element.
+  __device__ __forceinline__ void taps8(int ch, f4 (&wt)[8], float (&bias)[8]) const {
+    const Act* w = static_cast<const Act*>(a.w);
+    const Act* b = static_cast<const Act*>(a.bias);
+    const uintptr_t wa = reinterpret_cast<uintptr_t>(w), ba = reinterpret_cast<uintptr_t>(b);
+    if (a.W == 4 && wa % (4 * sizeof(Act)) == 0) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const Act* t = w + static_cast<int64_t>(ch + m) * 4;
+        if constexpr (sizeof(Act) == 2) {
+          const uint2 u = *reinterpret_cast<const uint2*>(t);
+          wt[m] = f4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+        } else {
+          wt[m] = *reinterpret_cast<const f4*>(t);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) wt[m] = f4{tap(ch + m, 0), tap(ch + m, 1), tap(ch + m, 2), tap(ch + m, 3)};
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) bias[m] = 0.f;
+    if (b) {
+      if (sizeof(Act) == 2 && ba % 16 == 0) {
+        const uint4 u = *reinterpret_cast<const uint4*>(b + ch);
+        const uint32_t q[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          bias[2 * m] = __uint_as_float(q[m] << 16);
+          bias[2 * m + 1] = __uint_as_float(q[m] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) bias[m] = to_f32(b[ch + m]);
+      }
+    }
+  }
+
   // Chunks first, first + step, ... of the sequence, the next one's rows
   // loaded while the current one is computed.
   __device__ void run(int first, int step) const {
@@ -143,11 +184,7 @@ struct QkPrep : PrefillCore<DK, Act> {
     if (first * kT >= T) return;
     f4 wt[8];
     float bias[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      wt[m] = f4{tap(ch + m, 0), tap(ch + m, 1), tap(ch + m, 2), tap(ch + m, 3)};
-      bias[m] = a.bias ? to_f32(static_cast<const Act*>(a.bias)[ch + m]) : 0.f;
-    }
+    taps8(ch, wt, bias);
     short* ws = static_cast<short*>(a.ws);
     const int sb = slot(8 * oc);
     Row8<Act> raw[kRaw], nxt[kRaw];

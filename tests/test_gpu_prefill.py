@@ -87,13 +87,14 @@ def test_value_widths(dv):
     print("dv=%d: out %.2e state %.2e" % ((dv,) + check(r)))
 
 
-def test_no_silu_no_norm_with_conv_bias():
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_no_silu_no_norm_with_conv_bias(dtype):
     """SiLU and L2 norm switched off, conv bias on (small inputs keep the
-    un-normalised state bounded)."""
-    shape = synth.Shape(1, 1, 32, 32, 4, "scalar", "f32")
+    un-normalised state bounded); fp32 and bf16 storage."""
+    shape = synth.Shape(1, 1, 32, 32, 4, "scalar", dtype)
     case = synth.prefill_case(shape, [96, 40], 4, seed=5)
-    case.x[:] *= 0.05
-    bias = (np.random.default_rng(5).standard_normal(shape.channels) * 0.05).astype(np.float32)
+    case.x[:] = synth.encode((oracle.as_f64(case.x) * 0.05).astype(np.float32), dtype)
+    bias = synth.encode(np.random.default_rng(5).standard_normal(shape.channels) * 0.05, dtype)
     g, o = layers(shape, conv_silu=False, l2norm=False)
     torch = _torch()
     ssm, conv = dev(case.pool.ssm), dev(case.pool.conv)
