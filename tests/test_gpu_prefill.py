@@ -213,3 +213,25 @@ def test_max_sequences_short():
     r = run_case(shape, lens, num_slots=2 * 65535, seed=14)
     print("65535 sequences: out %.2e state %.2e" % check(r))
 
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_small_max_seqlen_bitwise(gate):
+    """max_seqlen only sizes launch grids: a value below the longest sequence
+    (outside the contract, which GDN_DEBUG enforces) still gives the same bits
+    for outputs, final states and windows as the true one."""
+    torch = _torch()
+    shape = synth.Shape(2, 4, 32, 32, 4, gate, "bf16")
+    seqlens = [200, 70, 33, 129]
+    case = synth.prefill_case(shape, seqlens, 12, seed=21)
+    g, _ = layers(shape)
+    res = []
+    for mx in (max(seqlens), 40):
+        ssm, conv = dev(case.pool.ssm), dev(case.pool.conv)
+        out = gdn.gdn_prefill_chunked(g, ssm, conv, dev(case.dst), dev(case.init_slot),
+                                      dev(case.cu_seqlens), mx, dev(case.x), dev(case.alpha),
+                                      dev(case.beta), dev(case.conv_w))
+        torch.cuda.synchronize()
+        res.append((bits(out), bits(ssm), bits(conv)))
+    for a, b in zip(*res):
+        np.testing.assert_array_equal(a, b)
