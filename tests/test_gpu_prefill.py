@@ -235,3 +235,45 @@ def test_small_max_seqlen_bitwise(gate):
         res.append((bits(out), bits(ssm), bits(conv)))
     for a, b in zip(*res):
         np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_graph_capture_bitwise(gate):
+    """A prefill call -- every kernel it enqueues -- captured into a graph
+    replays bit-identical to the eager call: three replays, the pool restored
+    and the output poisoned by eager work between them (zero and
+    copy-on-write starts, so a replay reads nothing a replay wrote)."""
+    torch = _torch()
+    shape = synth.Shape(2, 4, 64, 64, 4, gate, "bf16")
+    seqlens = [150, 64, 33, 200]
+    case = synth.prefill_case(shape, seqlens, 12, seed=23)
+    g, _ = layers(shape)
+    mx, total = max(seqlens), sum(seqlens)
+    dst, init, cu = dev(case.dst), dev(case.init_slot), dev(case.cu_seqlens)
+    x, al, be, w = dev(case.x), dev(case.alpha), dev(case.beta), dev(case.conv_w)
+    need = gdn.gdn_prefill_workspace_size(g, len(seqlens), mx, total)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    rs, rc = dev(case.pool.ssm), dev(case.pool.conv)
+    rout = gdn.gdn_prefill_chunked(g, rs, rc, dst, init, cu, mx, x, al, be, w, workspace=ws)
+    torch.cuda.synchronize()
+    ref = bits(rout), bits(rs), bits(rc)
+
+    ssm, conv = dev(case.pool.ssm), dev(case.pool.conv)
+    out = torch.empty_like(rout)
+    call = lambda: gdn.gdn_prefill_chunked(g, ssm, conv, dst, init, cu, mx, x, al, be, w,
+                                           out=out, workspace=ws)
+    call()                      # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out.fill_(float("nan"))
+        ssm.copy_(dev(case.pool.ssm))
+        conv.copy_(dev(case.pool.conv))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((bits(out), bits(ssm), bits(conv)), ref):
+            np.testing.assert_array_equal(a, b)
