@@ -287,7 +287,6 @@ struct Prefill : PrefillCore<DK, Act> {
   __device__ __forceinline__ void prod_load(Prod& p, int c0) const {
     const int tau = opaque(p.tau), vt = opaque(p.vt), vch = opaque(p.vch);
     if (p.on) {
-      typedef uint32_t u2 __attribute__((ext_vector_type(2)));
       const rsrc_t rq = qk_rows<DK>(a, t0, T, c0, kT);
       const int sb = slot(8 * opaque(p.oc));
 #pragma unroll
