@@ -103,22 +103,48 @@ __device__ __forceinline__ int qk_off(const PrefillArgs& a, int r, int hk, bool 
 }
 
 // The q / k preparation pass (its own kernel, before the main one): one
-// workgroup per (sequence, 32-token chunk, key head), thread (co, tau):
-// channel octet co of q | k (q first), tokens 4 tau..+3 -- conv1d + SiLU +
-// L2 norm (+ q scale), split into bf16 (hi, lo).  Once per key head, where
-// the main kernel's workgroups that share the key head would each repeat it.
+// workgroup per (sequence, key head, every n-th 32-token chunk), thread
+// (co, tau): channel group co of q | k (q first), tokens 4 tau..+3 -- conv1d
+// + SiLU + L2 norm (+ q scale), split into bf16 (hi, lo).  Once per key
+// head, where the main kernel's workgroups that share the key head would
+// each repeat it.  Group oc of a head holds channels 4j..4j+3 and
+// 4j+16..4j+19 of 32-block b (oc = 4b + j): exactly the channels of storage
+// slots 8 oc..8 oc+7, so each row half goes out as one 16-byte store.
 template <int DK, typename Act>
 struct QkPrep : PrefillCore<DK, Act> {
   GDN_PREFILL_CORE(DK, Act);
-  static constexpr int kNco = DK / 4;   // channel octets of q and k
-  static constexpr int kGrp = DK / 8;   // octets per head (lanes of one norm)
+  static constexpr int kNco = DK / 4;   // channel groups of q and k
+  static constexpr int kGrp = DK / 8;   // groups per head (lanes of one norm)
   static constexpr int kRaw = kTpt + 3; // raw rows per thread
+  static constexpr int kE = static_cast<int>(sizeof(Act));
 
-  // Raw rows 4 tau - 3 .. 4 tau + 3 of chunk c0 for the thread's channels.
-  __device__ __forceinline__ void load(Row8<Act> (&raw)[kRaw], int c0, int tau, int ch) const {
+  // Channel m (0..7) of group oc, relative to the head.
+  __device__ __forceinline__ static int chan(int oc, int m) {
+    return 32 * (oc >> 2) + 4 * (oc & 3) + (m < 4 ? m : 12 + m);
+  }
+
+  // The group's 8 channels of one raw row: the two 4-channel halves.
+  __device__ __forceinline__ static void load_row(Row8<Act>& r, rsrc_t rs, int off) {
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    if constexpr (kE == 2) {
+      const u2 a0 = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+      const u2 a1 = __builtin_amdgcn_raw_buffer_load_b64(rs, off + 16 * kE, 0, 0);
+      r.w[0] = a0[0], r.w[1] = a0[1], r.w[2] = a1[0], r.w[3] = a1[1];
+    } else {
+      const u4 a0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+      const u4 a1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * kE, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r.w[i] = a0[i], r.w[4 + i] = a1[i];
+    }
+  }
+
+  // Raw rows 4 tau - 3 .. 4 tau + 3 of chunk c0 for the group starting at
+  // channel c (its first half; the second is 16 channels on).
+  __device__ __forceinline__ void load(Row8<Act> (&raw)[kRaw], int c0, int tau, int c) const {
     const rsrc_t rx = x_rows(c0);
 #pragma unroll
-    for (int r = 0; r < kRaw; ++r) raw[r].load(rx, x_off(c0, c0 + kTpt * tau - 3 + r, ch));
+    for (int r = 0; r < kRaw; ++r) load_row(raw[r], rx, x_off(c0, c0 + kTpt * tau - 3 + r, c));
     if (c0 == 0) {
       // rows -3..-1 (thread tokens 0..2 of token group 0) from the window;
       // every other offset lies past the window and reads zero
@@ -126,24 +152,24 @@ struct QkPrep : PrefillCore<DK, Act> {
 #pragma unroll
       for (int r = 0; r < 3; ++r) {
         Row8<Act> wr;
-        wr.load(rw, win_off(kTpt * tau - 3 + r, ch));
+        load_row(wr, rw, win_off(kTpt * tau - 3 + r, c));
         raw[r].merge(wr);
       }
     }
   }
 
-  // Taps (4, left-padded) and bias of channels ch..ch+7: for a width-4 conv
-  // with aligned arrays one 4-tap load per channel and one load for the 8
-  // biases, else element by element.
-  __device__ __forceinline__ void taps8(int ch, f4 (&wt)[8], float (&bias)[8]) const {
+  // Taps (4, left-padded) and bias of the group's channels (first at c): for
+  // a width-4 conv with aligned arrays one 4-tap load per channel and one
+  // load per 4 biases, else element by element.
+  __device__ __forceinline__ void taps8(int c, f4 (&wt)[8], float (&bias)[8]) const {
     const Act* w = static_cast<const Act*>(a.w);
     const Act* b = static_cast<const Act*>(a.bias);
     const uintptr_t wa = reinterpret_cast<uintptr_t>(w), ba = reinterpret_cast<uintptr_t>(b);
-    if (a.W == 4 && wa % (4 * sizeof(Act)) == 0) {
+    if (a.W == 4 && wa % (4 * kE) == 0) {
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        const Act* t = w + static_cast<int64_t>(ch + m) * 4;
-        if constexpr (sizeof(Act) == 2) {
+        const Act* t = w + static_cast<int64_t>(c + (m < 4 ? m : 12 + m)) * 4;
+        if constexpr (kE == 2) {
           const uint2 u = *reinterpret_cast<const uint2*>(t);
           wt[m] = f4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
                      __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
@@ -153,22 +179,26 @@ struct QkPrep : PrefillCore<DK, Act> {
       }
     } else {
 #pragma unroll
-      for (int m = 0; m < 8; ++m) wt[m] = f4{tap(ch + m, 0), tap(ch + m, 1), tap(ch + m, 2), tap(ch + m, 3)};
+      for (int m = 0; m < 8; ++m) {
+        const int cm = c + (m < 4 ? m : 12 + m);
+        wt[m] = f4{tap(cm, 0), tap(cm, 1), tap(cm, 2), tap(cm, 3)};
+      }
     }
 #pragma unroll
     for (int m = 0; m < 8; ++m) bias[m] = 0.f;
     if (b) {
-      if (sizeof(Act) == 2 && ba % 16 == 0) {
-        const uint4 u = *reinterpret_cast<const uint4*>(b + ch);
-        const uint32_t q[4] = {u.x, u.y, u.z, u.w};
+      if (kE == 2 && ba % 8 == 0) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          bias[2 * m] = __uint_as_float(q[m] << 16);
-          bias[2 * m + 1] = __uint_as_float(q[m] & 0xffff0000u);
+        for (int hf = 0; hf < 2; ++hf) {
+          const uint2 u = *reinterpret_cast<const uint2*>(b + c + 16 * hf);
+          bias[4 * hf + 0] = __uint_as_float(u.x << 16);
+          bias[4 * hf + 1] = __uint_as_float(u.x & 0xffff0000u);
+          bias[4 * hf + 2] = __uint_as_float(u.y << 16);
+          bias[4 * hf + 3] = __uint_as_float(u.y & 0xffff0000u);
         }
       } else {
 #pragma unroll
-        for (int m = 0; m < 8; ++m) bias[m] = to_f32(b[ch + m]);
+        for (int m = 0; m < 8; ++m) bias[m] = to_f32(b[c + (m < 4 ? m : 12 + m)]);
       }
     }
   }
@@ -180,19 +210,18 @@ struct QkPrep : PrefillCore<DK, Act> {
     const int co = tid % kNco, tau = tid / kNco;
     const bool isk = co >= kGrp;
     const int oc = isk ? co - kGrp : co;
-    const int ch = (isk ? a.Hk * DK : 0) + hk * DK + 8 * oc;
+    const int c = (isk ? a.Hk * DK : 0) + hk * DK + chan(oc, 0);
     if (first * kT >= T) return;
     f4 wt[8];
     float bias[8];
-    taps8(ch, wt, bias);
+    taps8(c, wt, bias);
     short* ws = static_cast<short*>(a.ws);
-    const int sb = slot(8 * oc);
     Row8<Act> raw[kRaw], nxt[kRaw];
-    load(raw, first * kT, tau, ch);
-    for (int c = first; c * kT < T; c += step) {
-      const int c0 = c * kT;
-      const bool more = (c + step) * kT < T;
-      if (more) load(nxt, (c + step) * kT, tau, ch);
+    load(raw, first * kT, tau, c);
+    for (int cc = first; cc * kT < T; cc += step) {
+      const int c0 = cc * kT;
+      const bool more = (cc + step) * kT < T;
+      if (more) load(nxt, (cc + step) * kT, tau, c);
 #pragma unroll
       for (int tt = 0; tt < kTpt; ++tt) {
         float y[8], ss = 0.f;
@@ -214,12 +243,9 @@ struct QkPrep : PrefillCore<DK, Act> {
           split4(f4{y[0], y[1], y[2], y[3]} * sc, h0, l0);
           split4(f4{y[4], y[5], y[6], y[7]} * sc, h1, l1);
           short* hi = ws + ((static_cast<int64_t>(t0) + tok) * a.Hk + hk) * 4 * DK +
-                      (isk ? 2 : 0) * DK;
-          short* lo = hi + DK;
-          *reinterpret_cast<s4*>(hi + sb) = h0;
-          *reinterpret_cast<s4*>(hi + sb + 8) = h1;
-          *reinterpret_cast<s4*>(lo + sb) = l0;
-          *reinterpret_cast<s4*>(lo + sb + 8) = l1;
+                      (isk ? 2 : 0) * DK + 8 * oc;
+          *reinterpret_cast<s8*>(hi) = cat(h0, h1);
+          *reinterpret_cast<s8*>(hi + DK) = cat(l0, l1);
         }
       }
       if (more) {
