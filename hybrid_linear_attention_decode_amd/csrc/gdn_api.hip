@@ -344,7 +344,8 @@ size_t gdn_prefill_workspace_size(const gdn_layer* L, int32_t N, int32_t max_seq
     return 0;
   // The scalar-decay prefill stores the prepared q / k rows (computed once
   // per key head); the per-channel one the diagonal blocks of each chunk.
-  if (L->gate != GDN_GATE_CHANNEL) return gdn::qk_workspace_bytes(L->n_k_heads, L->d_k, total_tokens);
+  if (L->gate != GDN_GATE_CHANNEL)
+    return gdn::qk_workspace_bytes(L->n_k_heads, L->d_k, total_tokens);
   return gdn::kda_workspace_bytes(L->n_v_heads, N, total_tokens);
 }
 

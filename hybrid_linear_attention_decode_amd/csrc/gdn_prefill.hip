@@ -98,7 +98,8 @@ __device__ __forceinline__ rsrc_t qk_rows(const PrefillArgs& a, int t0, int T, i
                    static_cast<uint32_t>(rows * row * 2));
 }
 template <int DK>
-__device__ __forceinline__ int qk_off(const PrefillArgs& a, int r, int hk, bool isk, int lo, int sl) {
+__device__ __forceinline__ int qk_off(const PrefillArgs& a, int r, int hk, bool isk, int lo,
+                                      int sl) {
   return (((r * a.Hk + hk) * 4 + (isk ? 2 : 0) + lo) * DK + sl) * 2;
 }
 
@@ -308,6 +309,10 @@ struct Prefill : PrefillCore<DK, Act> {
     }
   }
 
+  __device__ __forceinline__ static s4 ld8(rsrc_t r, int off) {
+    return __builtin_bit_cast(s4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  }
+
   // Prepared q / k rows of chunk c0 (the thread's two 4-channel groups of
   // each of its tokens, hi and lo) and the raw value inputs.
   __device__ __forceinline__ void prod_load(Prod& p, int c0) const {
@@ -319,10 +324,10 @@ struct Prefill : PrefillCore<DK, Act> {
       for (int tt = 0; tt < kTpt; ++tt) {
         const int oh = qk_off<DK>(a, kTpt * tau + tt, hk, p.isk, 0, sb);
         const int ol = qk_off<DK>(a, kTpt * tau + tt, hk, p.isk, 1, sb);
-        p.hi[tt][0] = __builtin_bit_cast(s4, __builtin_amdgcn_raw_buffer_load_b64(rq, oh, 0, 0));
-        p.hi[tt][1] = __builtin_bit_cast(s4, __builtin_amdgcn_raw_buffer_load_b64(rq, oh + 16, 0, 0));
-        p.lo[tt][0] = __builtin_bit_cast(s4, __builtin_amdgcn_raw_buffer_load_b64(rq, ol, 0, 0));
-        p.lo[tt][1] = __builtin_bit_cast(s4, __builtin_amdgcn_raw_buffer_load_b64(rq, ol + 16, 0, 0));
+        p.hi[tt][0] = ld8(rq, oh);
+        p.hi[tt][1] = ld8(rq, oh + 16);
+        p.lo[tt][0] = ld8(rq, ol);
+        p.lo[tt][1] = ld8(rq, ol + 16);
       }
     }
     const rsrc_t rx = x_rows(c0);
