@@ -277,3 +277,14 @@ def test_graph_capture_bitwise(gate):
         torch.cuda.synchronize()
         for a, b in zip((bits(out), bits(ssm), bits(conv)), ref):
             np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("width", [1, 3])
+def test_conv_widths(gate, width):
+    """Convs narrower than 4 -- width 1 keeps no conv state at all -- against
+    the oracle: taps left-padded in the kernels, windows of width - 1 rows,
+    both decay kinds."""
+    shape = synth.Shape(2, 4, 32, 32, width, gate, "bf16")
+    r = run_case(shape, [100, 37, 64], seed=24)
+    print("width %d %s: out %.2e state %.2e" % ((width, gate) + check(r)))
