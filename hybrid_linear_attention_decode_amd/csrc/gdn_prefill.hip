@@ -24,14 +24,14 @@
 // (K, Q, V^T and gates: three; P and A: two), with one barrier per chunk.
 // Between barriers c - 1 and c:
 //   consumers (waves 4-7), 16 value columns each, run chunk c: K S0^T,
-//     Q S0^T, U, O and the state update; wave 7 also writes chunk c + 2's
-//     gates (log-decay prefix sums) from inputs loaded a chunk ahead;
+//     Q S0^T, U, O and the state update;
 //   producers (waves 0-3) copy chunk c + 2's prepared K, Q rows into LDS with
-//     its value conv, and form chunk c + 1's A and P from the lower 16x16
-//     tiles of K K^T and Q K^T, with the inverses of the diagonal blocks of
-//     (I + A): for N strictly lower triangular, (I + N)^{-1} = (I - N)
-//     (I + N^2)(I + N^4)(I + N^8), and K K^T is symmetric, so both operand
-//     layouts of N come from the one accumulator tile.
+//     its value conv (wave 3 also its gates, the log-decay prefix sums, from
+//     inputs loaded a chunk ahead), and form chunk c + 1's A and P from the
+//     lower 16x16 tiles of K K^T and Q K^T, with the inverses of the diagonal
+//     blocks of (I + A): for N strictly lower triangular, (I + N)^{-1} =
+//     (I - N)(I + N^2)(I + N^4)(I + N^8), and K K^T is symmetric, so both
+//     operand layouts of N come from the one accumulator tile.
 // Every product runs on v_mfma_f32_16x16x{32,16}_bf16 with each fp32
 // operand split as x ~= hi + lo (two bf16), and a*b ~= ah*bh + ah*bl + al*bh
 // accumulated in fp32: about 16 significant bits per operand, which keeps
@@ -828,15 +828,20 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
   k.load_taps();
 
   // One barrier per chunk.  Between barriers c - 1 and c the consumers run
-  // chunk c while the producers store chunk c + 2 and form chunk c + 1's A,
-  // P and inverses (its K, Q and gates were stored an iteration earlier), and
-  // one consumer wave writes chunk c + 2's gates.
+  // chunk c while the producers store chunk c + 2 (wave 3: its gates too) and
+  // form chunk c + 1's A, P and inverses (its K, Q and gates were stored an
+  // iteration earlier).
   if (k.tid < kProd) {
     // ---------------- producers ----------------
     typename K::Prod p;
     k.prod_init(p);
     if (nch > 0) k.prod_load(p, 0);
     lds_barrier();            // planes zeroed, taps loaded
+    typename K::GateIn gin{0u, 0u, 0};
+    if (k.wave == 3) {
+      for (int c = 0; c < 2 && c < nch; ++c) k.gates(k.gate_load(c * kT), c);
+      if (nch > 2) gin = k.gate_load(2 * kT);
+    }
     // (the prepared rows are loaded straight into the registers they are
     // stored from: each chunk's store comes before the next chunk's load)
     for (int c = 0; c < 2 && c < nch; ++c) {
@@ -854,6 +859,10 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
         if (c + 3 < nch) k.prod_load(p, (c + 3) * kT);
       }
       if (c + 1 < nch) k.gram_phase(c + 1);
+      if (k.wave == 3 && c + 2 < nch) {
+        k.gates(gin, c + 2);
+        if (c + 3 < nch) gin = k.gate_load((c + 3) * kT);
+      }
       lds_barrier();          // chunk c consumed
     }
   } else {
@@ -872,11 +881,6 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
                                            4 * k.lg);
     }
     lds_barrier();            // planes zeroed, taps loaded
-    typename K::GateIn gin{0u, 0u, 0};
-    if (k.wave == 7) {
-      for (int c = 0; c < 2 && c < nch; ++c) k.gates(k.gate_load(c * kT), c);
-      if (nch > 2) gin = k.gate_load(2 * kT);
-    }
     lds_barrier();            // chunks 0 and 1 stored, their gates written
     lds_barrier();            // chunk 0 complete
     for (int c = 0; c < nch; ++c) {
@@ -884,10 +888,6 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
       if (cols) k.updates(S, U, qs, c);
       // chunk c + 2's gates (their buffer's last readers, chunk c - 1 here
       // and chunk c - 1's A and P, are done), then the inputs of the next
-      if (k.wave == 7 && c + 2 < nch) {
-        k.gates(gin, c + 2);
-        if (c + 3 < nch) gin = k.gate_load((c + 3) * kT);
-      }
       if (cols) k.outputs_and_state(S, U, qs, c);
       const int32_t cs = __builtin_amdgcn_readfirstlane(ckpt_slot(a, s, (c + 1) * kT, k.T));
       if (cols && cs >= 0) {  // the state after (c + 1) * kT tokens, to a checkpoint slot
