@@ -288,3 +288,12 @@ def test_conv_widths(gate, width):
     shape = synth.Shape(2, 4, 32, 32, width, gate, "bf16")
     r = run_case(shape, [100, 37, 64], seed=24)
     print("width %d %s: out %.2e state %.2e" % ((width, gate) + check(r)))
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_fp32_activations_dk128(gate):
+    """fp32 inputs at d_k = 128 (the preparation pass's 16-byte fp32 row and
+    tap loads), ragged lengths across block boundaries, both decay kinds."""
+    shape = synth.Shape(2, 4, 128, 64, 4, gate, "f32")
+    r = run_case(shape, [97, 32, 160, 1], seed=25)
+    print("fp32 d_k=128 %s: out %.2e state %.2e" % ((gate,) + check(r)))
