@@ -155,6 +155,15 @@ def _stream(stream):
     return ct.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Context for allocating buffers the library fills on `stream`: the
+    caching allocator then hands the block to no other stream's work while
+    the call's kernels may still use it."""
+    import contextlib
+    import torch
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def _dev(*tensors):
     for t in tensors:
         if t is not None and (not t.is_cuda or not t.is_contiguous()):
@@ -170,6 +179,36 @@ def _pool(ssm, conv) -> GdnPool:
     return GdnPool(_ptr(ssm), _ptr(conv), ssm.shape[0])
 
 
+def _check_pool(layer: "Layer", ssm, conv):
+    """ssm [slots, H_v, d_v, d_k] fp32; conv [slots, W-1, C] in the layer's
+    activation dtype (may be None when W == 1)."""
+    import torch
+    if ssm is None or ssm.dtype != torch.float32 or ssm.dim() != 4 or \
+            tuple(ssm.shape[1:]) != (layer.n_v_heads, layer.d_v, layer.d_k):
+        raise ValueError(f"ssm pool must be float32 [slots, {layer.n_v_heads}, {layer.d_v}, "
+                         f"{layer.d_k}]")
+    if conv is None:
+        if layer.conv_width > 1:
+            raise ValueError("conv pool missing")
+        return
+    if conv.dtype != layer.torch_act_dtype or conv.dim() != 3 or conv.shape[0] != ssm.shape[0] \
+            or tuple(conv.shape[1:]) != (layer.conv_width - 1, layer.channels):
+        raise ValueError(f"conv pool must be {layer.torch_act_dtype} [{ssm.shape[0]}, "
+                         f"{layer.conv_width - 1}, {layer.channels}]")
+
+
+def _check_act(layer: "Layer", what: str, t, numel: int):
+    """An activation-dtype input of numel elements (None allowed)."""
+    if t is not None and (t.dtype != layer.torch_act_dtype or t.numel() != numel):
+        raise ValueError(f"{what} must be {layer.torch_act_dtype} with {numel} elements")
+
+
+def _check_out(t, shape):
+    import torch
+    if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != tuple(shape)):
+        raise ValueError(f"out must be float32 {list(shape)}")
+
+
 def _spec(spec_ssm, spec_conv, spec_slots=None):
     if spec_slots is not None:
         return ct.byref(GdnSpecCache(None, None, spec_slots.shape[1], _ptr(spec_slots)))
@@ -178,10 +217,25 @@ def _spec(spec_ssm, spec_conv, spec_slots=None):
     return ct.byref(GdnSpecCache(_ptr(spec_ssm), _ptr(spec_conv), spec_ssm.shape[1], None))
 
 
-def _i32(t, n, what):
+def _i32(t, n, what, required=False):
+    """An int32 index array of n entries (the kernels read 32-bit words: an
+    int64 tensor would be read as pairs of halves)."""
     import torch
-    if t is not None and (t.dtype != torch.int32 or t.numel() != n):
-        raise ValueError(f"{what} must be int32 [{n}]")
+    if t is None:
+        if required:
+            raise ValueError(f"{what} is required")
+        return
+    if t.dtype != torch.int32 or (n is not None and t.numel() != n):
+        raise ValueError(f"{what} must be int32 [{n if n is not None else 'n'}]")
+
+
+def _check_inputs(layer: "Layer", rows: int, x, alpha, beta, conv_w, conv_b):
+    gates = layer.n_v_heads * (layer.d_k if layer.gate == "channel" else 1)
+    _check_act(layer, "x", x, rows * layer.channels)
+    _check_act(layer, "alpha", alpha, rows * gates)
+    _check_act(layer, "beta", beta, rows * layer.n_v_heads)
+    _check_act(layer, "conv_w", conv_w, layer.channels * layer.conv_width)
+    _check_act(layer, "conv_b", conv_b, layer.channels)
 
 
 def gdn_decode_step(layer: Layer, ssm, conv, mamba_pool_indices, x, alpha, beta, conv_w,
@@ -191,16 +245,30 @@ def gdn_decode_step(layer: Layer, ssm, conv, mamba_pool_indices, x, alpha, beta,
     fused slot preparation (-1 zero start, s copy-on-write source); spec_slots
     [B, t_max] int32: snapshots into pool slots.  See include/gdn.h."""
     import torch
-    _dev(ssm, conv, mamba_pool_indices, x, alpha, beta, conv_w, conv_b, out, spec_ssm, spec_conv,
-         init_slot, spec_slots)
+    _check_pool(layer, ssm, conv)
+    if x.dim() != 3:
+        raise ValueError("x must be [B, T, C]")
     B, T = x.shape[0], x.shape[1]
-    _i32(mamba_pool_indices, B, "mamba_pool_indices")
+    _check_inputs(layer, B * T, x, alpha, beta, conv_w, conv_b)
+    _i32(mamba_pool_indices, B, "mamba_pool_indices", required=True)
     _i32(init_slot, B, "init_slot")
     if spec_slots is not None and (spec_slots.dtype != torch.int32 or spec_slots.dim() != 2
                                    or spec_slots.shape[0] != B):
         raise ValueError("spec_slots must be int32 [B, t_max]")
+    if spec_ssm is not None:
+        _check_pool(layer, spec_ssm.flatten(0, 1) if spec_ssm.dim() == 5 else spec_ssm,
+                    None if spec_conv is None else
+                    (spec_conv.flatten(0, 1) if spec_conv.dim() == 4 else spec_conv))
+        if spec_ssm.dim() != 5 or spec_ssm.shape[0] != B or \
+                (spec_conv is not None and tuple(spec_conv.shape[:2]) != tuple(spec_ssm.shape[:2])):
+            raise ValueError("spec_ssm / spec_conv must be [B, t_max, ...]")
+    shape = (B, T, layer.n_v_heads, layer.d_v)
+    _check_out(out, shape)
     if out is None:
-        out = torch.empty((B, T, layer.n_v_heads, layer.d_v), dtype=torch.float32, device=x.device)
+        with _on(stream):
+            out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    _dev(ssm, conv, mamba_pool_indices, x, alpha, beta, conv_w, conv_b, out, spec_ssm, spec_conv,
+         init_slot, spec_slots)
     L = layer.c_struct()
     P = _pool(ssm, conv)
     inp = GdnInputs(_ptr(x), _ptr(alpha), _ptr(beta), _ptr(conv_w), _ptr(conv_b))
@@ -216,10 +284,14 @@ def gdn_spec_commit_index(ssm, conv, spec_slots, accepted_len, mamba_pool_indice
     """Commit by index: mamba_pool_indices[b] <- spec_slots[b, L-1] for L =
     accepted_len[b] >= 1; released [B] int32 gets each request's previous slot
     (-1 where unchanged).  See include/gdn.h."""
-    _dev(ssm, conv, spec_slots, accepted_len, mamba_pool_indices, released)
+    import torch
     B = mamba_pool_indices.numel()
-    _i32(accepted_len, B, "accepted_len")
+    _i32(mamba_pool_indices, B, "mamba_pool_indices", required=True)
+    _i32(accepted_len, B, "accepted_len", required=True)
     _i32(released, B, "released")
+    if spec_slots.dtype != torch.int32 or spec_slots.dim() != 2 or spec_slots.shape[0] != B:
+        raise ValueError("spec_slots must be int32 [B, t_max]")
+    _dev(ssm, conv, spec_slots, accepted_len, mamba_pool_indices, released)
     P = _pool(ssm, conv)
     st = lib().gdn_spec_commit_index(ct.byref(P), _spec(None, None, spec_slots),
                                      _ptr(accepted_len), _ptr(mamba_pool_indices),
@@ -229,19 +301,28 @@ def gdn_spec_commit_index(ssm, conv, spec_slots, accepted_len, mamba_pool_indice
 
 def gdn_spec_decode_commit(layer: Layer, ssm, conv, mamba_pool_indices, spec_ssm, spec_conv,
                            accepted_len, stream=None):
+    _check_pool(layer, ssm, conv)
+    B = mamba_pool_indices.numel()
+    _i32(mamba_pool_indices, B, "mamba_pool_indices", required=True)
+    _i32(accepted_len, B, "accepted_len", required=True)
+    if spec_ssm is None or spec_ssm.dim() != 5 or spec_ssm.shape[0] != B:
+        raise ValueError("spec_ssm must be [B, t_max, H_v, d_v, d_k]")
+    _check_pool(layer, spec_ssm.flatten(0, 1),
+                None if spec_conv is None else spec_conv.flatten(0, 1))
     _dev(ssm, conv, mamba_pool_indices, spec_ssm, spec_conv, accepted_len)
     L = layer.c_struct()
     P = _pool(ssm, conv)
     st = lib().gdn_spec_decode_commit(ct.byref(L), ct.byref(P), _ptr(mamba_pool_indices),
                                       _spec(spec_ssm, spec_conv), _ptr(accepted_len),
-                                      mamba_pool_indices.numel(), _stream(stream))
+                                      B, _stream(stream))
     _check(st, "gdn_spec_decode_commit")
 
 
 def gdn_slot_copy(layer: Layer, ssm, conv, src, dst, stream=None):
+    _check_pool(layer, ssm, conv)
+    _i32(src, None, "src", required=True)
+    _i32(dst, src.numel(), "dst", required=True)
     _dev(ssm, conv, src, dst)
-    if src.numel() != dst.numel():
-        raise ValueError("src and dst differ in length")
     L = layer.c_struct()
     P = _pool(ssm, conv)
     st = lib().gdn_slot_copy(ct.byref(L), ct.byref(P), _ptr(src), _ptr(dst), src.numel(),
@@ -250,6 +331,8 @@ def gdn_slot_copy(layer: Layer, ssm, conv, src, dst, stream=None):
 
 
 def gdn_slot_zero(layer: Layer, ssm, conv, idx, stream=None):
+    _check_pool(layer, ssm, conv)
+    _i32(idx, None, "idx", required=True)
     _dev(ssm, conv, idx)
     L = layer.c_struct()
     P = _pool(ssm, conv)
@@ -266,11 +349,14 @@ def gdn_slot_pack(layer: Layer, ssm, conv, idx, buffer=None, stream=None):
     """Slots idx [n] int32 -> a contiguous uint8 buffer of n packed items
     (allocated when not given); returns the buffer.  See include/gdn.h."""
     import torch
-    _dev(ssm, conv, idx, buffer)
+    _check_pool(layer, ssm, conv)
+    _i32(idx, None, "idx", required=True)
     n = idx.numel()
     if buffer is None:
-        buffer = torch.empty(max(n * gdn_slot_bytes(layer), 16), dtype=torch.uint8,
-                             device=ssm.device)
+        with _on(stream):
+            buffer = torch.empty(max(n * gdn_slot_bytes(layer), 16), dtype=torch.uint8,
+                                 device=ssm.device)
+    _dev(ssm, conv, idx, buffer)
     L = layer.c_struct()
     P = _pool(ssm, conv)
     st = lib().gdn_slot_pack(ct.byref(L), ct.byref(P), _ptr(idx), n, _ptr(buffer),
@@ -280,6 +366,8 @@ def gdn_slot_pack(layer: Layer, ssm, conv, idx, buffer=None, stream=None):
 
 
 def gdn_slot_unpack(layer: Layer, ssm, conv, buffer, idx, stream=None):
+    _check_pool(layer, ssm, conv)
+    _i32(idx, None, "idx", required=True)
     _dev(ssm, conv, idx, buffer)
     L = layer.c_struct()
     P = _pool(ssm, conv)
@@ -300,24 +388,34 @@ def gdn_prefill_chunked(layer: Layer, ssm, conv, dst_slots, init_slot, cu_seqlen
                         chunk: int = 64, ckpt_slots=None, ckpt_every: int = 128, stream=None):
     """x [total, C]; cu_seqlens [N+1] int32 (device); returns out [total, H_v, d_v] fp32.
     ckpt_slots [N, per_seq] int32: checkpoint k of sequence s (the state after
-    (k+1)*ckpt_every tokens) goes to pool slot ckpt_slots[s, k]."""
+    (k+1)*ckpt_every tokens) goes to pool slot ckpt_slots[s, k].  A workspace
+    allocated here is allocated on `stream` (the current stream if None)."""
     import torch
-    _dev(ssm, conv, dst_slots, init_slot, cu_seqlens, x, alpha, beta, conv_w, conv_b, out,
-         workspace, ckpt_slots)
+    _check_pool(layer, ssm, conv)
+    N = dst_slots.numel()
+    _i32(dst_slots, N, "dst_slots", required=True)
+    _i32(init_slot, N, "init_slot")
+    _i32(cu_seqlens, N + 1, "cu_seqlens", required=True)
     ck = None
     if ckpt_slots is not None:
         if ckpt_slots.dtype != torch.int32 or ckpt_slots.dim() != 2 or \
-                ckpt_slots.shape[0] != dst_slots.numel():
+                ckpt_slots.shape[0] != N:
             raise ValueError("ckpt_slots must be int32 [N, per_seq]")
         ck = ct.byref(GdnPrefillCkpt(_ptr(ckpt_slots), int(ckpt_every), ckpt_slots.shape[1]))
-    N = dst_slots.numel()
+    if x.dim() != 2:
+        raise ValueError("x must be [total, C]")
     total = x.shape[0]
-    if out is None:
-        out = torch.empty((total, layer.n_v_heads, layer.d_v), dtype=torch.float32,
-                          device=x.device)
+    _check_inputs(layer, total, x, alpha, beta, conv_w, conv_b)
+    shape = (total, layer.n_v_heads, layer.d_v)
+    _check_out(out, shape)
     need = gdn_prefill_workspace_size(layer, N, max_seqlen, total, chunk)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty(shape, dtype=torch.float32, device=x.device)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _dev(ssm, conv, dst_slots, init_slot, cu_seqlens, x, alpha, beta, conv_w, conv_b, out,
+         workspace, ckpt_slots)
     L = layer.c_struct()
     P = _pool(ssm, conv)
     inp = GdnInputs(_ptr(x), _ptr(alpha), _ptr(beta), _ptr(conv_w), _ptr(conv_b))

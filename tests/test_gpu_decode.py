@@ -449,3 +449,37 @@ def test_graph_capture_and_two_streams():
     np.testing.assert_array_equal(bits(ssm2), ref_bits[0])
     np.testing.assert_array_equal(bits(conv2), ref_bits[1])
 
+
+
+@pytest.mark.parametrize("shape", [synth.QWEN35, synth.Shape(2, 4, 64, 64, 3, "channel", "f32")],
+                         ids=["qwen35_bf16", "kda_f32"])
+def test_conv_bias(shape):
+    """Decode with a conv bias (bf16 storage on the Qwen3.5 shape, fp32 on a
+    per-channel-gate shape): 4 calls of T=2 against the oracle given the same
+    bias bits; windows bit-exact (the bias never enters the stored window)."""
+    torch = _torch()
+    case = synth.decode_case(shape, B=8, T=2, num_slots=24, n_calls=4, seed=16)
+    bias = synth.encode(np.random.default_rng(16).standard_normal(shape.channels)
+                        .astype(np.float32) * 0.5, shape.dtype)
+    g, o = layers(shape)
+    d = DevCase(case)
+    b_dev = dev(bias)
+    outs = [gdn.gdn_decode_step(g, d.ssm, d.conv, dev(case.indices[c]), dev(case.x[c]),
+                                dev(case.alpha[c]), dev(case.beta[c]), d.w, conv_b=b_dev)
+            for c in range(4)]
+    torch.cuda.synchronize()
+    s64, c64 = shadow(case.pool)
+    no_bias = oracle.decode(o, s64.copy(), c64.copy(), case.indices[0], case.x[0],
+                            case.alpha[0], case.beta[0], case.conv_w)
+    for c in range(4):
+        ref = oracle.decode(o, s64, c64, case.indices[c], case.x[c], case.alpha[c],
+                            case.beta[c], case.conv_w, conv_b=bias)
+        assert rel_err(host(outs[c]), ref) <= OUT_TOL
+        if c == 0:   # the bias changes the result (it is not silently dropped)
+            assert rel_err(host(outs[0]), no_bias) > 10 * OUT_TOL
+    live = case.pool.live
+    assert rel_err(host(d.ssm)[live], s64[live]) <= OUT_TOL
+    want = c64[live].astype(np.float32)
+    if shape.dtype == "bf16":
+        want = synth.f32_to_bf16_bits(want)
+    np.testing.assert_array_equal(host(d.conv)[live], want)

@@ -297,3 +297,59 @@ def test_fp32_activations_dk128(gate):
     shape = synth.Shape(2, 4, 128, 64, 4, gate, "f32")
     r = run_case(shape, [97, 32, 160, 1], seed=25)
     print("fp32 d_k=128 %s: out %.2e state %.2e" % ((gate,) + check(r)))
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_prefill_on_a_non_current_stream(gate):
+    """The binding allocates the workspace and the output on the call's stream:
+    a prefill launched on a side stream, followed at once (no sync) by
+    allocations and writes on the current stream, gives the bits of the same
+    prefill run alone."""
+    torch = _torch()
+    shape = synth.Shape(2, 4, 64, 64, 4, gate, "bf16")
+    case = synth.prefill_case(shape, [700, 333, 64], 8, seed=43)
+    g, _ = layers(shape)
+    args = lambda: (dev(case.dst), dev(case.init_slot), dev(case.cu_seqlens), 700, dev(case.x),
+                    dev(case.alpha), dev(case.beta), dev(case.conv_w))
+    ref_s, ref_c = dev(case.pool.ssm), dev(case.pool.conv)
+    ref = gdn.gdn_prefill_chunked(g, ref_s, ref_c, *args())
+    torch.cuda.synchronize()
+    ssm, conv = dev(case.pool.ssm), dev(case.pool.conv)
+    a = args()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ws_bytes = gdn.gdn_prefill_workspace_size(g, 3, 700, int(case.cu_seqlens[-1]))
+    out = gdn.gdn_prefill_chunked(g, ssm, conv, *a, stream=side)
+    # the current stream allocates and scribbles over fresh blocks of the
+    # same sizes while the side stream may still run
+    junk = [torch.full((ws_bytes,), 255, dtype=torch.uint8, device="cuda") for _ in range(3)]
+    junk += [torch.full(tuple(ref.shape), float("nan"), device="cuda") for _ in range(3)]
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(out), bits(ref))
+    np.testing.assert_array_equal(bits(ssm), bits(ref_s))
+    np.testing.assert_array_equal(bits(conv), bits(ref_c))
+    del junk
+
+
+def test_decode_on_a_non_current_stream():
+    """The same for the decode's output buffer."""
+    torch = _torch()
+    shape = synth.QWEN35
+    case = synth.decode_case(shape, B=16, T=2, num_slots=32, n_calls=1, seed=44)
+    g, _ = layers(shape)
+    ins = lambda: (dev(case.indices[0]), dev(case.x[0]), dev(case.alpha[0]), dev(case.beta[0]),
+                   dev(case.conv_w))
+    r_s, r_c = dev(case.pool.ssm), dev(case.pool.conv)
+    ref = gdn.gdn_decode_step(g, r_s, r_c, *ins())
+    torch.cuda.synchronize()
+    ssm, conv = dev(case.pool.ssm), dev(case.pool.conv)
+    a = ins()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    out = gdn.gdn_decode_step(g, ssm, conv, *a, stream=side)
+    junk = [torch.full(tuple(ref.shape), float("nan"), device="cuda") for _ in range(4)]
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(out), bits(ref))
+    np.testing.assert_array_equal(bits(ssm), bits(r_s))
+    del junk

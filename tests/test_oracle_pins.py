@@ -590,3 +590,37 @@ def test_oracle_rejects_bad_arguments():
     with pytest.raises(ValueError):
         oracle.spec_commit(L, s, c, [0], np.zeros((1, 2) + s.shape[1:]),
                            np.zeros((1, 2) + c.shape[1:]), [3])
+
+
+# --------------------------------------------------------------------------
+# the oracle's own bf16 decoding (every bf16 input reaches the oracle through it)
+
+def test_bf16_decoding_all_bit_patterns():
+    """oracle.bf16_bits_to_f64 over all 65 536 bf16 bit patterns against torch's
+    CPU bfloat16 type widened to float64 (an independent library routine):
+    equal values, equal signs of zero, NaN exactly where torch has NaN."""
+    import torch
+    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.bf16_bits_to_f64(pats)
+    ref = torch.from_numpy(pats.view(np.int16)).view(torch.bfloat16).double().numpy()
+    assert got.dtype == np.float64 and got.shape == ref.shape
+    nan = np.isnan(ref)
+    np.testing.assert_array_equal(np.isnan(got), nan)
+    assert nan.sum() == 2 * 127                    # exponent all ones, mantissa != 0
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+    np.testing.assert_array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    # as_f64 routes uint16 arrays through the same decoding, shape kept
+    np.testing.assert_array_equal(oracle.as_f64(pats.reshape(256, 256)), got.reshape(256, 256))
+
+
+def test_bf16_decoding_known_values():
+    """bf16 is the upper half of an IEEE binary32: a few patterns worked out
+    from the format (sign, 8 exponent bits with bias 127, 7 mantissa bits)."""
+    cases = {0x0000: 0.0, 0x3F80: 1.0, 0xBF80: -1.0, 0x4000: 2.0, 0xC040: -3.0,
+             0x3FC0: 1.5, 0x3F81: 1.0 + 2.0 ** -7, 0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127,
+             0x0080: 2.0 ** -126, 0x0001: 2.0 ** -133, 0x7F80: np.inf, 0xFF80: -np.inf,
+             0x3E00: 0.125}
+    pats = np.array(list(cases), dtype=np.uint16)
+    np.testing.assert_array_equal(oracle.bf16_bits_to_f64(pats), np.array(list(cases.values())))
+    assert np.signbit(oracle.bf16_bits_to_f64(np.array([0x8000], np.uint16))[0])
+    assert np.isnan(oracle.bf16_bits_to_f64(np.array([0x7FC0, 0xFFC1], np.uint16))).all()
