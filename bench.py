@@ -83,7 +83,7 @@ class DecodeBench:
     states replicated over all slots (values do not change the traffic)."""
 
     def __init__(self, torch, gdn, synth, shape, B, slots, n_calls, seed, n_inputs=64,
-                 n_distinct_slots=64, T=1, spec=False, spec_pool=False):
+                 n_distinct_slots=64, T=1, spec=False, spec_pool=False, with_work=True):
         self.torch = torch
         rs = synth.streams(seed)
         base = synth.make_pool(shape, n_distinct_slots, np.arange(n_distinct_slots), rs)
@@ -105,6 +105,9 @@ class DecodeBench:
                            shape.conv_width, shape.gate, shape.dtype)
         self.L = self.g.c_struct()
         self.P = gdn.GdnPool(self.ssm.data_ptr(), self.conv.data_ptr(), slots)
+        # the work counter of the ticket-balanced tail (zero; each call leaves it at zero)
+        self.work = torch.zeros(1, dtype=torch.int32, device="cuda") if with_work else None
+        self.work_ptr = ct.c_void_p(self.work.data_ptr()) if with_work else None
         self.fn = gdn.lib().gdn_decode_step
         self.stream = ct.c_void_p(torch.cuda.current_stream().cuda_stream)
         self.B, self.T = B, T
@@ -142,7 +145,7 @@ class DecodeBench:
     def call(self, c: int):
         spec = self.specs[c] if self.specs is not None else self.spec
         st = self.fn(self.Lref, self.Pref, self.idx_ptrs[c], None, self.B, self.T,
-                     self.inref[c % self.n_inputs], self.out_ptr, spec, self.stream)
+                     self.inref[c % self.n_inputs], self.out_ptr, spec, self.work_ptr, self.stream)
         if st != 0:
             raise RuntimeError(f"gdn_decode_step failed with status {st}")
 
@@ -340,6 +343,7 @@ def bench_kda_stack(torch, gdn, synth, K=20, W=3, layers=48):
     lib = gdn.lib()
     L = base.L
     P = [gdn.GdnPool(pools[l].data_ptr(), convs[l].data_ptr(), slots) for l in range(layers)]
+    work = base.work_ptr
     Pr = [ct.byref(p) for p in P]
     ptr = lambda t: ct.c_void_p(t.data_ptr())
     idx_p = [ptr(idx[c]) for c in range(W + K)]
@@ -354,7 +358,7 @@ def bench_kda_stack(torch, gdn, synth, K=20, W=3, layers=48):
             assert lib.gdn_slot_copy(Lr, Pr[l], src_p[c], dst_p[c], 16, stream) == 0
         for l in range(layers):
             assert lib.gdn_decode_step(Lr, Pr[l], idx_p[c], None, B, 1, base.inref[(c + l) % 4],
-                                       base.out_ptr, None, stream) == 0
+                                       base.out_ptr, None, work, stream) == 0
     for c in range(W):
         step(c)
     ms = time_calls(torch, step, W, K) / K
@@ -379,7 +383,8 @@ def bench_kda_stack(torch, gdn, synth, K=20, W=3, layers=48):
     def fused(c):
         for l in range(layers):
             assert lib.gdn_decode_step(Lr, Pr[l], idx_p[c], init_p[c], B, 1,
-                                       base.inref[(c + l) % 4], base.out_ptr, None, stream) == 0
+                                       base.inref[(c + l) % 4], base.out_ptr, None, work,
+                                       stream) == 0
     for c in range(W):
         fused(c)
     ms_f = time_calls(torch, fused, W, K) / K

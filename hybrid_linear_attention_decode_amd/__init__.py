@@ -7,8 +7,8 @@ status.  There is no fallback: if the library is not built, every call fails
 loudly.  Build it with ``python -m hybrid_linear_attention_decode_amd.build``.
 
 Entry points (same names as the C ABI):
-    gdn_decode_step, gdn_spec_decode_commit, gdn_spec_commit_index, gdn_prefill_chunked,
-    gdn_prefill_workspace_size, gdn_slot_copy, gdn_slot_zero, gdn_slot_bytes, gdn_slot_pack,
+    gdn_decode_step (+ decode_work, a zero work counter for it), gdn_spec_decode_commit,
+    gdn_spec_commit_index, gdn_prefill_chunked, gdn_prefill_workspace_size, gdn_slot_copy, gdn_slot_zero, gdn_slot_bytes, gdn_slot_pack,
     gdn_slot_unpack, gdn_status_string
 """
 from __future__ import annotations
@@ -85,7 +85,7 @@ def lib() -> ct.CDLL:
         pp = ct.POINTER(GdnPool)
         sp = ct.POINTER(GdnSpecCache)
         ip = ct.POINTER(GdnInputs)
-        L.gdn_decode_step.argtypes = [lp, pp, P, P, i32, i32, ip, P, sp, P]
+        L.gdn_decode_step.argtypes = [lp, pp, P, P, i32, i32, ip, P, sp, P, P]
         L.gdn_spec_decode_commit.argtypes = [lp, pp, P, sp, P, i32, P]
         L.gdn_spec_commit_index.argtypes = [pp, sp, P, P, P, i32, P]
         L.gdn_prefill_chunked.argtypes = [lp, pp, P, P, i32, P, i32, i32, i32, ip, P,
@@ -179,6 +179,20 @@ def _pool(ssm, conv) -> GdnPool:
     return GdnPool(_ptr(ssm), _ptr(conv), ssm.shape[0])
 
 
+def decode_work(device="cuda"):
+    """A decode work counter (the `work` argument of gdn_decode_step): one
+    zero int32 word.  Calls on one stream may share it; calls that may run at
+    the same time need their own.  The library leaves it at zero."""
+    import torch
+    return torch.zeros(1, dtype=torch.int32, device=device)
+
+
+def _check_work(work):
+    import torch
+    if work is not None and (work.dtype != torch.int32 or work.numel() < 1):
+        raise ValueError("work must be an int32 tensor of at least one element")
+
+
 def _check_pool(layer: "Layer", ssm, conv):
     """ssm [slots, H_v, d_v, d_k] fp32; conv [slots, W-1, C] in the layer's
     activation dtype (may be None when W == 1)."""
@@ -240,12 +254,14 @@ def _check_inputs(layer: "Layer", rows: int, x, alpha, beta, conv_w, conv_b):
 
 def gdn_decode_step(layer: Layer, ssm, conv, mamba_pool_indices, x, alpha, beta, conv_w,
                     conv_b=None, out=None, spec_ssm=None, spec_conv=None, init_slot=None,
-                    spec_slots=None, stream=None):
+                    spec_slots=None, work=None, stream=None):
     """x [B, T, C]; returns out [B, T, H_v, d_v] fp32.  init_slot [B] int32:
     fused slot preparation (-1 zero start, s copy-on-write source); spec_slots
-    [B, t_max] int32: snapshots into pool slots.  See include/gdn.h."""
+    [B, t_max] int32: snapshots into pool slots; work: a decode work counter
+    (decode_work()) for the run-time balanced tail.  See include/gdn.h."""
     import torch
     _check_pool(layer, ssm, conv)
+    _check_work(work)
     if x.dim() != 3:
         raise ValueError("x must be [B, T, C]")
     B, T = x.shape[0], x.shape[1]
@@ -268,13 +284,14 @@ def gdn_decode_step(layer: Layer, ssm, conv, mamba_pool_indices, x, alpha, beta,
         with _on(stream):
             out = torch.empty(shape, dtype=torch.float32, device=x.device)
     _dev(ssm, conv, mamba_pool_indices, x, alpha, beta, conv_w, conv_b, out, spec_ssm, spec_conv,
-         init_slot, spec_slots)
+         init_slot, spec_slots, work)
     L = layer.c_struct()
     P = _pool(ssm, conv)
     inp = GdnInputs(_ptr(x), _ptr(alpha), _ptr(beta), _ptr(conv_w), _ptr(conv_b))
     st = lib().gdn_decode_step(ct.byref(L), ct.byref(P), _ptr(mamba_pool_indices),
                                _ptr(init_slot), B, T, ct.byref(inp), _ptr(out),
-                               _spec(spec_ssm, spec_conv, spec_slots), _stream(stream))
+                               _spec(spec_ssm, spec_conv, spec_slots), _ptr(work),
+                               _stream(stream))
     _check(st, "gdn_decode_step")
     return out
 

@@ -1,6 +1,7 @@
 // gdn_api.hip -- the C ABI of libgdn (declared in include/gdn.h): host-side
 // validation of every host-checkable argument, then one asynchronous launch
-// on the caller's stream.  Nothing is allocated and no global state is kept.
+// on the caller's stream.  Nothing is allocated and no state is kept between
+// calls.
 #include "gdn.h"
 #include "gdn_internal.hpp"
 
@@ -183,7 +184,8 @@ const char* gdn_status_string(gdn_status s) {
 
 gdn_status gdn_decode_step(const gdn_layer* L, const gdn_pool* P, const int32_t* idx,
                            const int32_t* init_slot, int32_t B, int32_t T, const gdn_inputs* in,
-                           float* out, const gdn_spec_cache* spec, void* stream) {
+                           float* out, const gdn_spec_cache* spec, uint32_t* work,
+                           void* stream) {
   gdn_status st = check_layer(L);
   if (st != GDN_OK) return st;
   if ((st = check_pool(L, P)) != GDN_OK) return st;
@@ -198,6 +200,7 @@ gdn_status gdn_decode_step(const gdn_layer* L, const gdn_pool* P, const int32_t*
   if (!gdn::decode_rows_per_wave(L->d_k, G, L->d_v, L->conv_width - 1,
                                  L->gate == GDN_GATE_CHANNEL))
     return GDN_ERR_UNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(work) & 3u) return GDN_ERR_BAD_SHAPE;
   if (static_cast<int64_t>(B) * L->n_k_heads > INT32_MAX) return GDN_ERR_BAD_SHAPE;
   if (B == 0) return GDN_OK;
   if (debug_checks()) {
@@ -243,6 +246,7 @@ gdn_status gdn_decode_step(const gdn_layer* L, const gdn_pool* P, const int32_t*
   a.spec_ssm = spec && !spec->slots ? spec->ssm : nullptr;
   a.spec_conv = spec && !spec->slots ? spec->conv : nullptr;
   a.t_max = spec ? spec->t_max : 0;
+  a.work = work;
   return from_hip(gdn::launch_decode(a, L->d_k, L->act_dtype == GDN_BF16,
                                      L->gate == GDN_GATE_CHANNEL,
                                      static_cast<hipStream_t>(stream)));

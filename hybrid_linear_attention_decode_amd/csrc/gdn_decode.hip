@@ -36,9 +36,6 @@
 // run the same instantiation and the same per-token arithmetic (built with
 // -ffp-contract=off, explicit fmaf), so a draft of T tokens followed by a
 // commit of L equals an in-place decode of L tokens bit for bit.
-#include <mutex>
-#include <vector>
-
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
@@ -100,7 +97,7 @@ struct DecodeCta {
     TC = a.tchunk;
     Hv = a.Hv;
     Hk = a.Hk;
-    per_tok = Cg + GA + G + 4;
+    per_tok = (Cg + GA + G + 4 + 3) & ~3;  // 16-byte aligned token records
     kh = unit % Hk;
     b = unit / Hk;
     spec_pool = a.spec_slots != nullptr;
@@ -409,31 +406,26 @@ struct DecodeCta {
   }
 };
 
-// Work counters of the ticket tail, one per (device, stream) that decodes;
-// each is zero whenever no call is running on its stream.
-constexpr int kQueues = 64;
-__device__ unsigned int g_decode_queue[kQueues];
-
 // The unit of this workgroup, or -1 for none.  Workgroup x runs on XCD
 // x mod 8 (the dispatcher deals workgroups out round-robin over the XCDs).
 // The first nstatic units are fixed: XCD k is given the k-th eighth of them
-// (a block of requests with all their key heads), in order.  With a counter
-// (queue >= 0), the rest are handed out by ticket: each of the nticket
-// workgroups after them draws one when it starts, so XCDs that run ahead take
-// more of the tail (XCDs of one MI355X differ by up to ~10 % in how fast they
-// stream); the workgroup that draws the last ticket puts the counter back to
-// zero, and those past the last unit exit.
+// (a block of requests with all their key heads), in order.  With the
+// caller's work counter, the rest are handed out by ticket: each of the
+// nticket workgroups after them draws one when it starts, so XCDs that run
+// ahead take more of the tail (XCDs of one MI355X differ by up to ~10 % in
+// how fast they stream); the workgroup that draws the last ticket puts the
+// counter back to zero, and those past the last unit exit.  Without a
+// counter every unit is fixed.
 __device__ __forceinline__ int decode_unit(const DecodeArgs& a, int& drawn) {
   const unsigned x = blockIdx.x;
-  const unsigned nfix = a.queue >= 0 ? static_cast<unsigned>(a.nstatic) : gridDim.x;
+  const unsigned nfix = a.work ? static_cast<unsigned>(a.nstatic) : gridDim.x;
   if (x < nfix) {
     const unsigned q = nfix >> 3;
     return static_cast<int>(x < 8 * q ? (x & 7) * q + (x >> 3) : x);
   }
   if (threadIdx.x == 0) {
-    unsigned int* const ctr = &g_decode_queue[a.queue];
-    const unsigned t = atomicAdd(ctr, 1u);
-    if (t == static_cast<unsigned>(a.nticket) - 1) atomicExch(ctr, 0u);
+    const unsigned t = atomicAdd(a.work, 1u);
+    if (t == static_cast<unsigned>(a.nticket) - 1) atomicExch(a.work, 0u);
     const int64_t u = static_cast<int64_t>(a.nstatic) + t;
     drawn = u < static_cast<int64_t>(a.B) * a.Hk ? static_cast<int>(u) : -1;
   }
@@ -480,7 +472,7 @@ __global__ void __launch_bounds__(512, 4) decode_kernel(const DecodeArgs a) {
 
 // Dynamic LDS bytes of the decode kernel: the activations of tchunk tokens.
 size_t decode_lds_bytes(int dk, int G, int dv, int kda, int tchunk) {
-  const int per_tok = 2 * dk + G * dv + G * (kda ? dk : 1) + G + 4;
+  const int per_tok = (2 * dk + G * dv + G * (kda ? dk : 1) + G + 4 + 3) & ~3;
   return sizeof(float) * static_cast<size_t>(tchunk) * per_tok;
 }
 
@@ -530,36 +522,6 @@ hipError_t launch_dk(const DecodeArgs& a, int dk, int rpw, dim3 grid, size_t lds
 
 int rows_per_pass(int dk) { return dk >= 64 ? 4 : 256 / dk; }
 
-// The work counter of (current device, stream): each stream that decodes
-// keeps its own, so calls that share one run in stream order and calls on
-// different streams never share one.  -1 (every unit fixed) when the stream
-// is being captured into a graph (a replay could then run beside another
-// stream's call on the same counter) or when all counters of the device are
-// taken.
-int decode_queue(hipStream_t s) {
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(s, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return -1;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return -1;
-  struct Entry {
-    int dev;
-    hipStream_t stream;
-    int queue;
-  };
-  static std::mutex mu;
-  static std::vector<Entry> table;
-  std::lock_guard<std::mutex> lock(mu);
-  int used = 0;
-  for (const Entry& e : table) {
-    if (e.dev != dev) continue;
-    if (e.stream == s) return e.queue;
-    ++used;
-  }
-  if (used >= kQueues) return -1;
-  table.push_back({dev, s, used});
-  return used;
-}
-
 }  // namespace
 
 // Rows of state per wave (32, 16 or 8; a divisor of d_v, so a wave stays in
@@ -596,14 +558,12 @@ hipError_t launch_decode(const DecodeArgs& args, int dk, int act_bf16, int kda, 
   const int64_t unit_bytes = static_cast<int64_t>(args.G) * args.dv * dk * 4;
   size_t lds = decode_lds_bytes(dk, args.G, args.dv, kda, a.tchunk);
   if (unit_bytes >= 128 * 1024 && lds < kHalfLds + 16) lds = kHalfLds + 16;
-  // The last quarter of the units goes out by ticket (Qwen3.5 shape, B=64:
-  // 49.4 us against 50.6 us with every unit fixed), with half again as many
-  // ticket workgroups as tail units so that fast XCDs can take up to 1.5x
-  // their share; without a counter of its own for this stream every unit is
-  // fixed.
-  a.queue = decode_queue(s);
+  // With the caller's work counter the last quarter of the units goes out by
+  // ticket (Qwen3.5 shape, B=64: 49.4-50.1 us against 50.6-51.2 us with every
+  // unit fixed), with half again as many ticket workgroups as tail units so
+  // that fast XCDs can take up to 1.5x their share.
   int64_t nwg = units;
-  if (a.queue >= 0) {
+  if (a.work) {
     a.nstatic = static_cast<int32_t>((units - units / 4) / 8 * 8);
     const int64_t tail = units - a.nstatic;
     a.nticket = static_cast<int32_t>(tail + tail / 2);

@@ -30,9 +30,9 @@ struct DecodeArgs {
   void* spec_conv;           // [B][t_max][W-1][C]
   const int32_t* spec_slots; // [B][t_max] pool slots taking the snapshots, or nullptr
   int32_t t_max;
-  int32_t queue;             // work counter of the ticket tail, or -1 (all units fixed)
-  int32_t nstatic;           // units run by the workgroup of the same index (queue >= 0)
-  int32_t nticket;           // workgroups that draw a ticket each (queue >= 0)
+  uint32_t* work;            // the caller's work counter (zero between calls), or nullptr
+  int32_t nstatic;           // units run by the workgroup of the same index (work given)
+  int32_t nticket;           // workgroups that draw a ticket each (work given)
 };
 
 // Bulk slot operations (copy, zero, commit of a snapshot).

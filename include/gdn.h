@@ -34,12 +34,9 @@
  *
  * Conventions for every entry point.
  *   - Pointers are DEVICE pointers unless marked (host).  The caller owns and
- *     allocates every buffer; the library allocates nothing and is safe to
- *     call from several host threads.  Its only state between calls is one
- *     4-byte work counter per (device, stream) that has run gdn_decode_step
- *     (at most 64 per device, in the library's own device memory): calls on
- *     one stream use it in stream order and leave it at zero.  A call on a
- *     stream under graph capture, or on a 65th stream, uses none.
+ *     allocates every buffer; the library allocates nothing, keeps no state
+ *     between calls and is safe to call from several host threads, on any
+ *     streams (hipStreamPerThread included) and under graph capture.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *     default stream).  Returning GDN_OK means "validated and enqueued".
  *   - Host-checkable errors (NULL pointers, shapes, dtypes, unsupported sizes,
@@ -149,6 +146,7 @@ typedef struct {
  * Decode T >= 1 tokens per request ("Scheduler dual": the state of the slot
  * named by mamba_pool_indices is updated in place every decode step; with a
  * spec cache, per-speculative-step Conv/SSM snapshots are kept for rollback).
+ * One workgroup per (request, key head) unit.
  *   mamba_pool_indices [B] int32 (device); B >= 0; 1 <= T.
  *   init_slot [B] int32 (device) or NULL -- slot preparation fused into the
  *     step ("Riesgo de correctitud": a fresh working slot must start clean):
@@ -161,11 +159,18 @@ typedef struct {
  *   spec != NULL: T <= spec->t_max; the state after token t (0-based) goes to
  *     snapshot t of request b (see gdn_spec_cache); working slots are not
  *     written.
+ *   work: NULL, or one uint32 word of device memory owned by the caller,
+ *     zero before its first use; every call leaves it at zero.  With it the
+ *     last quarter of the units is handed out at run time (an atomic ticket
+ *     per workgroup), so the XCDs that stream faster take more of the tail;
+ *     without it every unit has a fixed workgroup.  Calls that may run at the
+ *     same time (on different streams, or graph replays beside other work)
+ *     need distinct words; calls on one stream may share one.
  */
 gdn_status gdn_decode_step(const gdn_layer* layer, const gdn_pool* pool,
                            const int32_t* mamba_pool_indices, const int32_t* init_slot,
                            int32_t B, int32_t T, const gdn_inputs* in, float* out,
-                           const gdn_spec_cache* spec, void* stream);
+                           const gdn_spec_cache* spec, uint32_t* work, void* stream);
 
 /*
  * Rollback / commit after verification ("Scheduler dual": rollback from the

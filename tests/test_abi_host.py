@@ -47,7 +47,7 @@ def decode(L, pool=None, idx=FAKE, B=4, T=1, inp=None, out=FAKE, spec=None):
     pool = pool or GdnPool(FAKE, FAKE, 8)
     inp = inp or GdnInputs(FAKE, FAKE, FAKE, FAKE, None)
     return gdn.lib().gdn_decode_step(ct.byref(L), ct.byref(pool), idx, None, B, T,
-                                     ct.byref(inp), out, spec, None)
+                                     ct.byref(inp), out, spec, None, None)
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -70,7 +70,8 @@ def test_bad_layer(field, value, status):
 
 def test_bad_decode_arguments():
     L = qwen_layer()
-    assert gdn.lib().gdn_decode_step(None, None, FAKE, None, 1, 1, None, FAKE, None, None) == \
+    assert gdn.lib().gdn_decode_step(None, None, FAKE, None, 1, 1, None, FAKE, None, None,
+                                     None) == \
         gdn.GDN_ERR_NULL_ARG
     assert decode(L, pool=GdnPool(None, FAKE, 8)) == gdn.GDN_ERR_NULL_ARG
     assert decode(L, pool=GdnPool(FAKE, None, 8)) == gdn.GDN_ERR_NULL_ARG
@@ -78,6 +79,11 @@ def test_bad_decode_arguments():
     assert decode(L, out=None) == gdn.GDN_ERR_NULL_ARG
     assert decode(L, inp=GdnInputs(FAKE, None, FAKE, FAKE, None)) == gdn.GDN_ERR_NULL_ARG
     assert decode(L, T=0) == gdn.GDN_ERR_BAD_SHAPE
+    # a misaligned work counter word
+    assert gdn.lib().gdn_decode_step(ct.byref(L), ct.byref(GdnPool(FAKE, FAKE, 8)), FAKE, None,
+                                     4, 1, ct.byref(GdnInputs(FAKE, FAKE, FAKE, FAKE, None)),
+                                     FAKE, None, ct.c_void_p(0x10002), None) == \
+        gdn.GDN_ERR_BAD_SHAPE
     assert decode(L, B=-1) == gdn.GDN_ERR_BAD_SHAPE
     assert decode(L, B=70000) == gdn.GDN_ERR_BAD_SHAPE
     assert decode(L, pool=GdnPool(ct.c_void_p(0x10004), FAKE, 8)) == gdn.GDN_ERR_BAD_SHAPE

@@ -19,13 +19,16 @@ def _torch():
 
 
 class DevCase:
-    """Device copies of a seeded decode case."""
+    """Device copies of a seeded decode case; with_work: a work counter is
+    passed to every call (the last quarter of the units handed out by
+    ticket)."""
 
-    def __init__(self, case: synth.DecodeCase):
+    def __init__(self, case: synth.DecodeCase, with_work: bool = False):
         self.ssm = dev(case.pool.ssm)
         self.conv = dev(case.pool.conv)
         self.w = dev(case.conv_w)
         self.case = case
+        self.work = gdn.decode_work() if with_work else None
 
     def call(self, g, c, out=None, spec=None, idx=None):
         cs = self.case
@@ -33,7 +36,10 @@ class DevCase:
         spec_ssm, spec_conv = spec if spec is not None else (None, None)
         return gdn.gdn_decode_step(g, self.ssm, self.conv, ix, dev(cs.x[c]), dev(cs.alpha[c]),
                                    dev(cs.beta[c]), self.w, out=out, spec_ssm=spec_ssm,
-                                   spec_conv=spec_conv)
+                                   spec_conv=spec_conv, work=self.work)
+
+    def work_is_zero(self):
+        return self.work is None or not bool(self.work.any())
 
 
 def run_oracle(o, case, s64, c64, calls, T=None):
@@ -82,23 +88,29 @@ def test_tiny_multi_token_call_equals_single_steps_bitwise():
     np.testing.assert_array_equal(bits(a.conv), bits(b.conv))
 
 
-@pytest.mark.parametrize("B,slots,n_calls,seed", [(16, 256, 1000, 1), (64, 1024, 40, 5)],
-                         ids=["b16_1000_calls", "b64_headline"])
-def test_qwen35_full_run(B, slots, n_calls, seed):
+@pytest.mark.parametrize("B,slots,n_calls,seed,with_work",
+                         [(16, 256, 1000, 1, True), (64, 1024, 40, 5, True),
+                          (64, 1024, 10, 5, False)],
+                         ids=["b16_1000_calls", "b64_headline", "b64_no_work_counter"])
+def test_qwen35_full_run(B, slots, n_calls, seed, with_work):
     """Qwen3.5-shaped layer, 16/32 heads, d=128, 8192 channels, bf16 inputs,
     fp32 state, rotating distinct indices, T=1, in the launch configuration
-    the bench times: B=16 over a 256-slot pool for 1000 calls, and the
-    headline B=64 over a 1024-slot pool (seed of the bench) for 40 calls.
-    Every output of every call against the oracle, then the final pool."""
+    the bench times (a work counter passed: the last quarter of the units by
+    ticket): B=16 over a 256-slot pool for 1000 calls, and the headline B=64
+    over a 1024-slot pool (seed of the bench) for 40 calls; and without the
+    counter (every unit fixed).  Every output of every call against the
+    oracle, then the final pool; the counter ends at zero."""
     torch = _torch()
     case = synth.decode_case(synth.QWEN35, B=B, T=1, num_slots=slots, n_calls=n_calls, seed=seed)
     g, o = layers(synth.QWEN35)
-    d = DevCase(case)
+    d = DevCase(case, with_work)
     out = torch.empty((n_calls, B, 1, 32, 128), dtype=torch.float32, device="cuda")
     x, al, be, ix = dev(case.x), dev(case.alpha), dev(case.beta), dev(case.indices)
     for c in range(n_calls):
-        gdn.gdn_decode_step(g, d.ssm, d.conv, ix[c], x[c], al[c], be[c], d.w, out=out[c])
+        gdn.gdn_decode_step(g, d.ssm, d.conv, ix[c], x[c], al[c], be[c], d.w, out=out[c],
+                            work=d.work)
     torch.cuda.synchronize()
+    assert d.work_is_zero()
     got = host(out)
     s64, c64 = shadow(case.pool)
     worst = 0.0
@@ -267,17 +279,22 @@ def test_poisoned_fresh_slots_clean_after_zero_or_cow():
     dict(shape=synth.Shape(2, 2, 32, 48, 1, "channel", "bf16"), layer=dict(l2norm=False)),
     dict(shape=synth.Shape(1, 4, 16, 64, 3, "channel", "f32"), layer=dict(q_scale=0.5)),
     dict(shape=synth.Shape(8, 8, 128, 256, 4, "scalar", "bf16"), layer=dict()),
+    dict(shape=synth.Shape(2, 8, 128, 32, 4, "scalar", "bf16"), layer=dict()),
+    dict(shape=synth.Shape(1, 2, 128, 64, 3, "channel", "f32"), layer=dict()),
 ])
-def test_other_shapes_against_oracle(kw):
+@pytest.mark.parametrize("with_work", [False, True], ids=["fixed", "ticket"])
+def test_other_shapes_against_oracle(kw, with_work):
     """d_k in {16, 32, 64, 128}, d_v != d_k, GQA 1:1 / 2:1 / 4:1, conv widths
-    1-4, both gates and dtypes, flags off; 5 steps of T=2."""
+    1-4, both gates and dtypes, flags off; 5 steps of T=2; without and with a
+    work counter."""
     torch = _torch()
     shape = kw["shape"]
     case = synth.decode_case(shape, B=3, T=2, num_slots=8, n_calls=5, seed=11)
     g, o = layers(shape, **kw["layer"])
-    d = DevCase(case)
+    d = DevCase(case, with_work)
     outs = [d.call(g, c) for c in range(5)]
     torch.cuda.synchronize()
+    assert d.work_is_zero()
     s64, c64 = shadow(case.pool)
     refs = run_oracle(o, case, s64, c64, range(5))
     for c in range(5):
@@ -286,17 +303,17 @@ def test_other_shapes_against_oracle(kw):
     assert rel_err(host(d.ssm)[live], s64[live]) <= STATE_TOL_16
 
 
-@pytest.mark.parametrize("shape,B", [(synth.TINY, 9), (synth.Shape(4, 8, 32, 32, 4, "scalar", "bf16"), 5)])
+@pytest.mark.parametrize("shape,B", [(synth.TINY, 9), (synth.Shape(3, 6, 128, 64, 4, "scalar", "bf16"), 5)])
 def test_unit_counts_not_a_multiple_of_eight(shape, B):
-    """B * H_k = 18 and 20 units: the workgroup -> unit order deals blocks of
-    units to the XCDs and leaves the remainder in place; every unit is run
-    exactly once (outputs and states against the oracle, every slot outside
-    the batch bit-identical)."""
+    """B * H_k = 18 and 15 units, with a work counter: the workgroup -> unit
+    order deals blocks of units to the XCDs, leaves the remainder in place and
+    hands out the tail by ticket; every unit is run exactly once (outputs and
+    states against the oracle, every slot outside the batch bit-identical)."""
     torch = _torch()
     slots = 2 * B + 3
     case = synth.decode_case(shape, B=B, T=1, num_slots=slots, n_calls=3, seed=12)
     g, o = layers(shape)
-    d = DevCase(case)
+    d = DevCase(case, with_work=True)
     before = bits(d.ssm), bits(d.conv)
     outs = [d.call(g, c) for c in range(3)]
     torch.cuda.synchronize()
@@ -389,11 +406,11 @@ def test_max_batch_tiny():
 
 
 def test_graph_capture_and_two_streams():
-    """A decode call captured into a graph (its units then all fixed, no
-    ticket) replays bit-identical to eager calls, three replays with eager
-    work between them; and two streams decoding disjoint slots at once (each
-    with its own ticket counter) give what one stream gives one call after
-    the other."""
+    """A decode call with a work counter captured into a graph replays
+    bit-identical to eager calls (no counter), three replays with eager work
+    between them; and two streams decoding disjoint slots of one pool at once,
+    each with its own counter, give what one stream gives one call after the
+    other.  The counters end at zero."""
     torch = _torch()
     shape = synth.QWEN35
     B = 64
@@ -404,7 +421,7 @@ def test_graph_capture_and_two_streams():
     ins = [(dev(case.x[c]), dev(case.alpha[c]), dev(case.beta[c])) for c in range(3)]
     w = dev(case.conv_w)
 
-    # eager reference: one stream, calls in order
+    # eager reference: one stream, calls in order, no counters
     ref_ssm, ref_conv = dev(case.pool.ssm), dev(case.pool.conv)
     ref_out = [gdn.gdn_decode_step(g, ref_ssm, ref_conv, idx, *ins[c], w) for c in range(3)]
     torch.cuda.synchronize()
@@ -412,15 +429,16 @@ def test_graph_capture_and_two_streams():
 
     # graph: static input buffers refilled before every replay
     ssm, conv = dev(case.pool.ssm), dev(case.pool.conv)
+    work = gdn.decode_work()
     xs, als, bes = (t.clone() for t in ins[0])
     out = torch.empty_like(ref_out[0])
-    gdn.gdn_decode_step(g, ssm, conv, idx, xs, als, bes, w, out=out)   # warm-up call ...
+    gdn.gdn_decode_step(g, ssm, conv, idx, xs, als, bes, w, out=out, work=work)  # warm-up ...
     torch.cuda.synchronize()
     ssm.copy_(dev(case.pool.ssm)); conv.copy_(dev(case.pool.conv))    # ... undone
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        gdn.gdn_decode_step(g, ssm, conv, idx, xs, als, bes, w, out=out)
+        gdn.gdn_decode_step(g, ssm, conv, idx, xs, als, bes, w, out=out, work=work)
     torch.cuda.synchronize()
     for c in range(3):
         xs.copy_(ins[c][0]); als.copy_(ins[c][1]); bes.copy_(ins[c][2])
@@ -428,11 +446,13 @@ def test_graph_capture_and_two_streams():
         graph.replay()
         torch.cuda.synchronize()
         np.testing.assert_array_equal(bits(out), bits(ref_out[c]))
+        assert not bool(work.any())
     np.testing.assert_array_equal(bits(ssm), ref_bits[0])
     np.testing.assert_array_equal(bits(conv), ref_bits[1])
 
     # two streams, disjoint halves of the batch, launched back to back
     ssm2, conv2 = dev(case.pool.ssm), dev(case.pool.conv)
+    works = [gdn.decode_work(), gdn.decode_work()]
     halves = [(slice(0, B), torch.cuda.Stream()), (slice(B, 2 * B), torch.cuda.Stream())]
     parts = [[(idx[h].contiguous(), *(t[h].contiguous() for t in ins[c])) for c in range(3)]
              for h, _ in halves]
@@ -441,14 +461,71 @@ def test_graph_capture_and_two_streams():
     for c in range(3):
         for k, (h, st) in enumerate(halves):
             with torch.cuda.stream(st):
-                outs[k][c] = gdn.gdn_decode_step(g, ssm2, conv2, *parts[k][c], w)
+                outs[k][c] = gdn.gdn_decode_step(g, ssm2, conv2, *parts[k][c], w, work=works[k])
     torch.cuda.synchronize()
     for c in range(3):
         got = torch.cat([outs[0][c], outs[1][c]])
         np.testing.assert_array_equal(bits(got), bits(ref_out[c]))
     np.testing.assert_array_equal(bits(ssm2), ref_bits[0])
     np.testing.assert_array_equal(bits(conv2), ref_bits[1])
+    assert not any(bool(x.any()) for x in works)
 
+
+class _PerThreadStream:
+    """hipStreamPerThread: one handle value that names a different stream on
+    every host thread."""
+    cuda_stream = 2
+
+
+def test_two_host_threads_on_the_per_thread_stream():
+    """Two host threads decode disjoint halves of a batch on
+    hipStreamPerThread (the same handle value, a different stream on each
+    thread), three calls each, sharing one pool, each thread with its own work
+    counter; outputs and pools equal, bit for bit, one stream running the
+    calls one after the other."""
+    import threading
+    torch = _torch()
+    shape = synth.QWEN35
+    B = 32
+    case = synth.decode_case(shape, B=2 * B, T=1, num_slots=128, n_calls=3, seed=19,
+                             rotate=False)
+    g, _ = layers(shape)
+    w = dev(case.conv_w)
+    ref_ssm, ref_conv = dev(case.pool.ssm), dev(case.pool.conv)
+    idx = dev(case.indices[0])
+    ref = [gdn.gdn_decode_step(g, ref_ssm, ref_conv, idx, dev(case.x[c]), dev(case.alpha[c]),
+                               dev(case.beta[c]), w) for c in range(3)]
+    ssm, conv = dev(case.pool.ssm), dev(case.pool.conv)
+    works = [gdn.decode_work(), gdn.decode_work()]
+    halves = [slice(0, B), slice(B, 2 * B)]
+    args = [[(dev(case.indices[0][h]), dev(case.x[c][h]), dev(case.alpha[c][h]),
+              dev(case.beta[c][h]),
+              torch.empty((B, 1, shape.n_v_heads, shape.d_v), device="cuda"))
+             for c in range(3)] for h in halves]
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(k):
+        try:
+            for c in range(3):
+                ix, x, al, be, out = args[k][c]
+                gdn.gdn_decode_step(g, ssm, conv, ix, x, al, be, w, out=out, work=works[k],
+                                    stream=_PerThreadStream)
+        except Exception as e:  # pragma: no cover - reported below
+            errors.append(e)
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for c in range(3):
+        got = torch.cat([args[0][c][4], args[1][c][4]])
+        np.testing.assert_array_equal(bits(got), bits(ref[c]))
+    np.testing.assert_array_equal(bits(ssm), bits(ref_ssm))
+    np.testing.assert_array_equal(bits(conv), bits(ref_conv))
+    assert not any(bool(x.any()) for x in works)
 
 
 @pytest.mark.parametrize("shape", [synth.QWEN35, synth.Shape(2, 4, 64, 64, 3, "channel", "f32")],

@@ -9,10 +9,11 @@ checkpoint slots, 32 continuing in place.
 Two device copies of the stack run the same steps: one with the separate
 slot kernels (gdn_slot_zero / gdn_slot_copy, then the decode), one with the
 preparation fused into the decode call (init_slot: -1 zero start, else the
-checkpoint).  Both are checked: every output and every working slot against
-the fp64 oracle (max-normalised error <= 2e-3, conv windows exact), the two
-bit for bit against each other over the whole pools, and every slot no step
-wrote bit-identical to its initial contents."""
+checkpoint) and a work counter passed (the last quarter of the units handed
+out by ticket, as the bench runs it).  Both are checked: every output
+and every working slot against the fp64 oracle (max-normalised error <= 2e-3,
+conv windows exact), the two bit for bit against each other over the whole
+pools, and every slot no step wrote bit-identical to its initial contents."""
 import numpy as np
 import pytest
 
@@ -60,6 +61,7 @@ def test_kda_stack_b64_pool1024_fused_and_separate_prep():
 
     outs = {k: torch.empty((LAYERS, STEPS, B, 1, 32, 128), device="cuda")
             for k in ("separate", "fused")}
+    work = gdn.decode_work()
     nan = float("nan")
     for c, r in enumerate(roles):
         idx, fresh, cow_dst, cow_src = r[:B], r[:16], r[16:32], r[B:B + 16]
@@ -85,8 +87,10 @@ def test_kda_stack_b64_pool1024_fused_and_separate_prep():
         for l, L in enumerate(per_layer):
             ssm, conv = L["pools"]["fused"]
             gdn.gdn_decode_step(g, ssm, conv, idx_d, L["x_d"][c], L["al_d"][c], L["be_d"][c],
-                                L["w_d"], out=outs["fused"][l, c], init_slot=init_d)
+                                L["w_d"], out=outs["fused"][l, c], init_slot=init_d,
+                                work=work)
     torch.cuda.synchronize()
+    assert not bool(work.any())
 
     # fused == separate, bit for bit: outputs and the whole pools
     assert torch.equal(_ints(outs["separate"]), _ints(outs["fused"]))
