@@ -8,7 +8,8 @@ loudly.  Build it with ``python -m hybrid_linear_attention_decode_amd.build``.
 
 Entry points (same names as the C ABI):
     gdn_decode_step (+ decode_work, a zero work counter for it), gdn_spec_decode_commit,
-    gdn_spec_commit_index, gdn_prefill_chunked, gdn_prefill_workspace_size, gdn_slot_copy, gdn_slot_zero, gdn_slot_bytes, gdn_slot_pack,
+    gdn_spec_commit_index, gdn_prefill_chunked, gdn_prefill_chunked_static,
+    gdn_prefill_workspace_size, gdn_slot_copy, gdn_slot_zero, gdn_slot_bytes, gdn_slot_pack,
     gdn_slot_unpack, gdn_status_string
 """
 from __future__ import annotations
@@ -33,9 +34,11 @@ GDN_GATE_SCALAR, GDN_GATE_CHANNEL = 0, 1
 GDN_F_CONV_SILU, GDN_F_L2NORM_QK = 1, 2
 
 EXPORTED = ("gdn_decode_step", "gdn_spec_decode_commit", "gdn_spec_commit_index",
-            "gdn_prefill_chunked", "gdn_prefill_workspace_size", "gdn_slot_copy",
-            "gdn_slot_zero", "gdn_slot_bytes", "gdn_slot_pack", "gdn_slot_unpack",
-            "gdn_status_string")
+            "gdn_prefill_chunked", "gdn_prefill_chunked_static", "gdn_prefill_workspace_size",
+            "gdn_slot_copy", "gdn_slot_zero", "gdn_slot_bytes", "gdn_slot_pack",
+            "gdn_slot_unpack", "gdn_status_string")
+
+GDN_PREFILL_STATIC_BYTES = 64 * 1024 * 1024
 
 
 class GdnError(RuntimeError):
@@ -90,6 +93,8 @@ def lib() -> ct.CDLL:
         L.gdn_spec_commit_index.argtypes = [pp, sp, P, P, P, i32, P]
         L.gdn_prefill_chunked.argtypes = [lp, pp, P, P, i32, P, i32, i32, i32, ip, P,
                                           ct.POINTER(GdnPrefillCkpt), P, ct.c_size_t, P]
+        L.gdn_prefill_chunked_static.argtypes = [lp, pp, P, P, i32, P, i32, i32, i32, ip, P,
+                                                 ct.POINTER(GdnPrefillCkpt), P]
         L.gdn_prefill_workspace_size.argtypes = [lp, i32, i32, i32, i32]
         L.gdn_prefill_workspace_size.restype = ct.c_size_t
         L.gdn_slot_copy.argtypes = [lp, pp, P, P, i32, P]
@@ -101,8 +106,8 @@ def lib() -> ct.CDLL:
         L.gdn_status_string.argtypes = [ct.c_int]
         L.gdn_status_string.restype = ct.c_char_p
         for f in ("gdn_decode_step", "gdn_spec_decode_commit", "gdn_spec_commit_index",
-                  "gdn_prefill_chunked", "gdn_slot_copy", "gdn_slot_zero", "gdn_slot_pack",
-                  "gdn_slot_unpack"):
+                  "gdn_prefill_chunked", "gdn_prefill_chunked_static", "gdn_slot_copy",
+                  "gdn_slot_zero", "gdn_slot_pack", "gdn_slot_unpack"):
             getattr(L, f).restype = ct.c_int
         _lib = L
     return _lib
@@ -441,4 +446,45 @@ def gdn_prefill_chunked(layer: Layer, ssm, conv, dst_slots, init_slot, cu_seqlen
                                    ct.byref(inp), _ptr(out), ck, _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "gdn_prefill_chunked")
+    return out
+
+
+def gdn_prefill_chunked_static(layer: Layer, ssm, conv, dst_slots, init_slot, cu_seqlens,
+                               max_seqlen, x, alpha, beta, conv_w, conv_b=None, out=None,
+                               chunk: int = 64, ckpt_slots=None, ckpt_every: int = 128,
+                               stream=None):
+    """gdn_prefill_chunked with the library's own workspace array (nothing is
+    allocated by the library; `out` must be given for a call that allocates
+    nothing at all).  See include/gdn.h."""
+    import torch
+    _check_pool(layer, ssm, conv)
+    N = dst_slots.numel()
+    _i32(dst_slots, N, "dst_slots", required=True)
+    _i32(init_slot, N, "init_slot")
+    _i32(cu_seqlens, N + 1, "cu_seqlens", required=True)
+    ck = None
+    if ckpt_slots is not None:
+        if ckpt_slots.dtype != torch.int32 or ckpt_slots.dim() != 2 or \
+                ckpt_slots.shape[0] != N:
+            raise ValueError("ckpt_slots must be int32 [N, per_seq]")
+        ck = ct.byref(GdnPrefillCkpt(_ptr(ckpt_slots), int(ckpt_every), ckpt_slots.shape[1]))
+    if x.dim() != 2:
+        raise ValueError("x must be [total, C]")
+    total = x.shape[0]
+    _check_inputs(layer, total, x, alpha, beta, conv_w, conv_b)
+    shape = (total, layer.n_v_heads, layer.d_v)
+    _check_out(out, shape)
+    if out is None:
+        with _on(stream):
+            out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    _dev(ssm, conv, dst_slots, init_slot, cu_seqlens, x, alpha, beta, conv_w, conv_b, out,
+         ckpt_slots)
+    L = layer.c_struct()
+    P = _pool(ssm, conv)
+    inp = GdnInputs(_ptr(x), _ptr(alpha), _ptr(beta), _ptr(conv_w), _ptr(conv_b))
+    st = lib().gdn_prefill_chunked_static(ct.byref(L), ct.byref(P), _ptr(dst_slots),
+                                          _ptr(init_slot), N, _ptr(cu_seqlens), int(max_seqlen),
+                                          int(total), int(chunk), ct.byref(inp), _ptr(out), ck,
+                                          _stream(stream))
+    _check(st, "gdn_prefill_chunked_static")
     return out

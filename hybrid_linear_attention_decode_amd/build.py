@@ -21,7 +21,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gdn_api.hip", "gdn_decode.hip", "gdn_prefill.hip", "gdn_slots.hip", "kda_prefill.hip"]
+SOURCES = ["gdn_api.hip", "gdn_decode.hip", "gdn_prefill.hip", "gdn_slots.hip", "kda_prefill.hip",
+           "gdn_static.hip"]
 ARCH = "gfx950"
 
 

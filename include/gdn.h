@@ -237,6 +237,28 @@ gdn_status gdn_prefill_chunked(const gdn_layer* layer, const gdn_pool* pool,
                                float* out, const gdn_prefill_ckpt* ckpt, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/*
+ * Chunked prefill that allocates nothing, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): gdn_prefill_chunked with the same arguments except
+ * the workspace, which is a device array of GDN_PREFILL_STATIC_BYTES inside
+ * the library -- one per GPU the library runs on, held until the process
+ * ends.  A call that would need more workspace than that
+ * (gdn_prefill_workspace_size) returns GDN_ERR_WORKSPACE with nothing
+ * enqueued; GDN_ERR_LAUNCH if the array's address cannot be looked up.
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time
+ * on one GPU (different streams, graph replays beside other work) race and
+ * must not be issued.  The array keeps the last call's contents; nothing in
+ * it needs to start at zero.  64 MiB holds, e.g., the scalar-decay workspace
+ * of 4096 tokens of a 16-key-head, d_k = 128 layer (16 KiB per token).
+ */
+#define GDN_PREFILL_STATIC_BYTES (64u * 1024u * 1024u)
+gdn_status gdn_prefill_chunked_static(const gdn_layer* layer, const gdn_pool* pool,
+                                      const int32_t* dst_slots, const int32_t* init_slot,
+                                      int32_t N, const int32_t* cu_seqlens, int32_t max_seqlen,
+                                      int32_t total_tokens, int32_t chunk, const gdn_inputs* in,
+                                      float* out, const gdn_prefill_ckpt* ckpt, void* stream);
+
 /* Bytes of workspace gdn_prefill_chunked needs for these sizes: for the
  * scalar decay 8 * total * H_k * d_k; for the per-channel decay 2048 * H_v *
  * (floor(total/16) + 4 * min(N, total)).  0 on bad arguments. */

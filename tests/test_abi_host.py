@@ -231,3 +231,17 @@ def test_per_channel_prefill_workspace():
     assert prefill(K, ws=ct.c_void_p(0x10080), ws_bytes=need) == gdn.GDN_ERR_WORKSPACE
     assert prefill(K, N=0) == gdn.GDN_OK
     assert prefill(K, chunk=32) == gdn.GDN_ERR_UNSUPPORTED
+
+
+def test_static_prefill_refuses_oversized_calls_on_the_host():
+    """gdn_prefill_chunked_static: a call whose workspace would exceed the
+    library's array is refused before any HIP call (no device needed)."""
+    L = qwen_layer()
+    cu = FAKE
+    inp = GdnInputs(FAKE, FAKE, FAKE, FAKE, None)
+    st = gdn.lib().gdn_prefill_chunked_static(ct.byref(L), ct.byref(GdnPool(FAKE, FAKE, 8)),
+                                             FAKE, None, 1, cu, 8192, 8192, 64, ct.byref(inp),
+                                             FAKE, None, None)
+    assert st == gdn.GDN_ERR_WORKSPACE
+    need = gdn.gdn_prefill_workspace_size(gdn.Layer(16, 32, 128, 128), 1, 8192, 8192)
+    assert need > gdn.GDN_PREFILL_STATIC_BYTES
