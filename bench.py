@@ -203,6 +203,82 @@ def cpu_baseline(synth, shape, bench: DecodeBench, budget_s: float):
                       f"(fp64 oracle, {nthreads} threads, {dt:.1f} s)"}
 
 
+def _timed(fn, budget_s: float):
+    """Calls fn() until about budget_s seconds have passed (at least twice);
+    returns (calls, seconds)."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        fn()
+        n += 1
+        dt = time.perf_counter() - t0
+        if n >= 2 and dt >= budget_s:
+            return n, dt
+
+
+def oracle_rates(synth, budget_s: float = 2.0) -> dict:
+    """The fp64 oracle, as it stands, on bounded samples of each path's
+    workload (same shapes and input recipe, fewer requests or tokens), timed
+    on the host cores beside the GPU figures: tokens/s per path, and for the
+    headline decode also a one-thread rate on 10 calls."""
+    import oracle
+    nthreads = oracle.default_threads()
+    out = {}
+
+    def olayer(shape):
+        return oracle.Layer(shape.n_k_heads, shape.n_v_heads, shape.d_k, shape.d_v,
+                            shape.conv_width, shape.gate)
+
+    def decode_sample(shape, B, T, seed, spec=False, threads=nthreads, calls=None):
+        case = synth.decode_case(shape, B=B, T=T, num_slots=B, n_calls=1, seed=seed,
+                                 rotate=False)
+        o = olayer(shape)
+        s64, c64 = oracle.as_f64(case.pool.ssm).copy(), oracle.as_f64(case.pool.conv).copy()
+        sp = None
+        if spec:
+            sp = (np.zeros((B, T) + s64.shape[1:]), np.zeros((B, T) + c64.shape[1:]))
+
+        def one():
+            oracle.decode(o, s64, c64, case.indices[0], case.x[0], case.alpha[0], case.beta[0],
+                          case.conv_w, spec_ssm=None if sp is None else sp[0],
+                          spec_conv=None if sp is None else sp[1], nthreads=threads)
+        if calls is not None:
+            t0 = time.perf_counter()
+            for _ in range(calls):
+                one()
+            return calls, time.perf_counter() - t0
+        return _timed(one, budget_s)
+
+    def rec(tok_s, sample, threads=nthreads):
+        return {"oracle_tok_s": round(tok_s, 2), "oracle_cores": threads,
+                "oracle_sample": sample}
+
+    n, dt = decode_sample(synth.QWEN35, 64, 1, 5, threads=1, calls=10)
+    out["headline_one_thread"] = rec(64 * n / dt, f"{n} B=64 decode calls of the headline "
+                                                  f"shape, one thread, {dt:.1f} s", 1)
+    n, dt = decode_sample(synth.QWEN35, 16, 1, 1)
+    out["decode_qwen35_b16"] = rec(16 * n / dt, f"{n} B=16 decode calls, {dt:.1f} s")
+    n, dt = decode_sample(synth.QWEN35, 8, 7, 2, spec=True)
+    out["spec_draft_qwen35_b64_t7"] = rec(8 * 7 * n / dt, f"{n} drafts of 7 tokens for 8 "
+                                                          f"requests (snapshots), {dt:.1f} s")
+    n, dt = decode_sample(synth.KDA, 64, 1, 4)
+    out["kda_stack_b64_48layers"] = rec(64 * n / (48 * dt), f"{n} B=64 KDA layer calls "
+                                                            f"(48 per step), {dt:.1f} s")
+    for key, shape in (("prefill_qwen35_4x8192", synth.QWEN35), ("prefill_kda_4x8192", synth.KDA)):
+        lens = [256] * 4
+        case = synth.prefill_case(shape, lens, 8, seed=17)
+        o = olayer(shape)
+
+        def one():
+            s64, c64 = oracle.as_f64(case.pool.ssm).copy(), oracle.as_f64(case.pool.conv).copy()
+            oracle.prefill(o, s64, c64, case.dst, case.init_slot, case.cu_seqlens, case.x,
+                           case.alpha, case.beta, case.conv_w, nthreads=nthreads)
+        n, dt = _timed(one, budget_s)
+        out[key] = rec(1024 * n / dt, f"{n} sequential prefills of 4 x 256 tokens (the "
+                                      f"token-by-token recurrence), {dt:.1f} s")
+    return out
+
+
 def path_record(ms_per_call: float, nbytes: float, tokens: int, what: str) -> dict:
     gbs = nbytes / (ms_per_call * 1e-3) / 1e9
     return {"what": what, "us_per_call": round(ms_per_call * 1e3, 2),
@@ -212,14 +288,27 @@ def path_record(ms_per_call: float, nbytes: float, tokens: int, what: str) -> di
 
 
 def bench_decode_b16(torch, gdn, synth, K=500, W=50):
-    """Qwen3.5-shaped decode at B=16 on a 256-slot pool (reuse after 15 calls)."""
+    """Qwen3.5-shaped decode at B=16 on a 256-slot pool: indices rotating
+    through a seeded permutation (reuse after 15 calls), and the literal
+    draw -- 16 distinct slots drawn afresh for every call (reuse distance
+    random, the pool's 512 MiB twice the Infinity Cache)."""
     shape = synth.QWEN35
     b = DecodeBench(torch, gdn, synth, shape, 16, 256, W + K, seed=1)
     for c in range(W):
         b.call(c)
     ms = time_calls(torch, b.call, W, K) / K
-    return path_record(ms, decode_bytes(shape, 16), 16,
-                       "GDN decode, Qwen3.5 shape, B=16, T=1, pool 256")
+    rot = path_record(ms, decode_bytes(shape, 16), 16,
+                      "GDN decode, Qwen3.5 shape, B=16, T=1, pool 256")
+    g = np.random.default_rng(101)
+    iid = np.stack([g.choice(256, 16, replace=False) for _ in range(W + K)]).astype(np.int32)
+    b.idx.copy_(torch.from_numpy(iid))
+    for c in range(W):
+        b.call(c)
+    ms = time_calls(torch, b.call, W, K) / K
+    lit = path_record(ms, decode_bytes(shape, 16), 16,
+                      "GDN decode, Qwen3.5 shape, B=16, T=1, pool 256, 16 distinct slots "
+                      "drawn independently for every call")
+    return rot, lit
 
 
 def bench_spec(torch, gdn, synth, K=100, W=10):
@@ -543,17 +632,23 @@ def bench_prefill_ckpt(torch, gdn, synth, K=10, W=2):
     return rec, arec
 
 
-def copy_rate(torch, nbytes: int, reps: int = 200) -> float:
+def copy_rate(torch, nbytes: int, reps: int = 200, pairs: int = 4) -> float:
     """GB/s of a plain device copy (torch copy_, read nbytes/2 + write
-    nbytes/2) moving the same byte volume as one decode call: the practical
-    streaming ceiling the decode kernel is set against."""
+    nbytes/2 per call) moving the same byte volume as one decode call, over
+    `pairs` rotating source / destination buffers so that a buffer comes back
+    only after (pairs - 1) * nbytes of other traffic (1.1 GB here, more than
+    twice the 256 MB Infinity Cache): the practical streaming ceiling the
+    decode kernel is set against."""
     n = nbytes // 2 // 4
-    a = torch.ones(n, device="cuda")
-    b = torch.empty(n, device="cuda")
-    for _ in range(20):
-        b.copy_(a)
-    ms = time_calls(torch, lambda c: b.copy_(a), 0, reps) / reps
-    del a, b
+    bufs = [(torch.ones(n, device="cuda"), torch.empty(n, device="cuda")) for _ in range(pairs)]
+
+    def one(c):
+        src, dst = bufs[c % pairs]
+        dst.copy_(src)
+    for c in range(20):
+        one(c)
+    ms = time_calls(torch, one, 0, reps) / reps
+    del bufs
     return 2 * n * 4 / (ms * 1e-3) / 1e9
 
 
@@ -602,7 +697,7 @@ def main():
         copy_calibration(torch)
         return
     if args.only == "paths":
-        for r in (bench_decode_b16(torch, gdn, synth), *bench_spec(torch, gdn, synth),
+        for r in (*bench_decode_b16(torch, gdn, synth), *bench_spec(torch, gdn, synth),
                   *bench_spec_pool(torch, gdn, synth), *bench_kda_stack(torch, gdn, synth),
                   *bench_slot_pack(torch, gdn, synth),
                   bench_prefill(torch, gdn, synth), *bench_prefill_ckpt(torch, gdn, synth),
@@ -648,7 +743,7 @@ def main():
             "spec buffers and in pool slots, KDA 48-layer stack with separate and fused slot "
             "preparation, slot pack / unpack, chunked prefill of both layers, with checkpoints and "
             "the append from them)")
-        d16 = bench_decode_b16(torch, gdn, synth)
+        d16, d16_iid = bench_decode_b16(torch, gdn, synth)
         draft, commit = bench_spec(torch, gdn, synth)
         pdraft, pcommit = bench_spec_pool(torch, gdn, synth)
         kda, kda_fused = bench_kda_stack(torch, gdn, synth)
@@ -656,7 +751,8 @@ def main():
         pf = bench_prefill(torch, gdn, synth)
         pfc, app = bench_prefill_ckpt(torch, gdn, synth)
         pfk = bench_prefill(torch, gdn, synth, shape=synth.KDA)
-        paths = {"decode_qwen35_b16": d16, "spec_draft_qwen35_b64_t7": draft,
+        paths = {"decode_qwen35_b16": d16, "decode_qwen35_b16_iid": d16_iid,
+                 "spec_draft_qwen35_b64_t7": draft,
                  "spec_commit_qwen35_b64": commit,
                  "spec_draft_pool_slots_qwen35_b64_t7": pdraft,
                  "spec_commit_index_b64": pcommit,
@@ -669,6 +765,12 @@ def main():
     if not args.no_cpu_baseline and args.only == "all":
         log("bench: timing the oracle sample")
         cpu = cpu_baseline(synth, shape, bench, args.cpu_budget)
+        log("bench: timing the oracle on samples of the other paths")
+        rates = oracle_rates(synth)
+        cpu["one_thread_value"] = rates.pop("headline_one_thread")["oracle_tok_s"]
+        for key, r in rates.items():
+            if paths is not None and key in paths:
+                paths[key].update(r)
 
     rec = {
         "metric": "GDN decode tokens/s and achieved HBM GB/s (fraction of peak) at B=64",

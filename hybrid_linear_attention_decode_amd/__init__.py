@@ -18,7 +18,10 @@ import ctypes as ct
 import os
 from dataclasses import dataclass
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+# GDN_LIB_PATH names another build of the library to load (e.g. one with
+# host-side sanitizers); by default the in-tree libgdn.so.
+LIB_PATH = os.environ.get("GDN_LIB_PATH") or \
+    os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
 
 GDN_OK = 0
 GDN_ERR_NULL_ARG = 1

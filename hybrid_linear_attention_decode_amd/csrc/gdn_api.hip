@@ -7,6 +7,7 @@
 
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <algorithm>
 #include <vector>
@@ -167,7 +168,11 @@ gdn_status pack_common(const gdn_layer* L, const gdn_pool* P, const int32_t* idx
 
 extern "C" {
 
-const char* gdn_status_string(gdn_status s) {
+const char* gdn_status_string(gdn_status status) {
+  // A C caller may pass any int: read it as one (an out-of-range value of
+  // the enum type must not be loaded as that type).
+  int s = 0;
+  memcpy(&s, &status, sizeof(s));
   switch (s) {
     case GDN_OK: return "ok";
     case GDN_ERR_NULL_ARG: return "a required pointer is NULL";

@@ -26,7 +26,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gdn_oracle.c")
-_LIB = os.path.join(_HERE, "libgdn_oracle.so")
+# GDN_ORACLE_LIB_PATH names another build of the oracle (e.g. one with
+# sanitizers); by default the in-tree libgdn_oracle.so.
+_LIB = os.environ.get("GDN_ORACLE_LIB_PATH") or os.path.join(_HERE, "libgdn_oracle.so")
 _lib = None
 
 
@@ -97,7 +99,8 @@ class Layer:
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """Exact decoding of bf16 bit patterns (uint16) to fp64."""
     b = np.ascontiguousarray(bits).view(np.uint16).astype(np.uint32) << 16
-    return b.view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):   # NaN patterns widen to NaN
+        return b.view(np.float32).astype(np.float64)
 
 
 def as_f64(a) -> np.ndarray:
