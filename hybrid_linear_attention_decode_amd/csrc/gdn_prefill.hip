@@ -271,11 +271,21 @@ struct Prefill : PrefillCore<DK, Act> {
   __device__ __forceinline__ static int qk(int r, int sl) { return QkRow<DK>::at(r, sl); }
 
   // ================= producers =================
-  // Thread (co, tau): channel octet co of q|k (q first), tokens 4 tau..+3.
+  // The prepared K, Q rows of a chunk are copied as 16-byte pieces: piece x
+  // = tid + 256 i of the chunk is token x / (4 kNc), workspace plane
+  // (x / kNc) % 4 (q hi, q lo, k hi, k lo), chunk x % kNc -- a wave reads
+  // whole workspace rows, and each 8 lanes of a store write 8 chunks of one
+  // row, which the swizzle keeps in distinct banks.  A thread's pieces are
+  // one plane and chunk at tokens t_0 + i kTs, so their addresses are a
+  // per-thread base plus a uniform or immediate offset.
+  static constexpr int kNc = QkRow<DK>::kChunks;   // 16-byte chunks per K / Q row
+  static constexpr int kCopy = kNc / 2;            // pieces per producer thread and chunk
+  static constexpr int kTs = 64 / kNc;             // token step between a thread's pieces
   struct Prod {
-    s4 hi[kTpt][2], lo[kTpt][2];  // the next chunk's prepared rows, not yet stored
-    int co, tau, oc;
-    bool isk, on;
+    u4 row[kCopy];              // the next chunk's prepared pieces, not yet stored
+    int qoff;                   // workspace bytes of piece 0 from the chunk's first row
+    int lds[2];                 // LDS bytes of piece 0 (pieces with bit 1 of i set: [1])
+                                //   within a K / Q buffer
     // value conv: channels 2 vp, 2 vp + 1 of the column block, tokens 4 vt..+3
     uint32_t vraw[kRaw][sizeof(Act) == 2 ? 1 : 2];
     f4 vo[2];                   // [channel], not yet stored
@@ -284,11 +294,13 @@ struct Prefill : PrefillCore<DK, Act> {
   };
 
   __device__ void prod_init(Prod& p) const {
-    p.on = tid < 8 * kNco;
-    p.co = tid % kNco;
-    p.tau = tid / kNco;
-    p.isk = p.co >= kGrp;
-    p.oc = p.isk ? p.co - kGrp : p.co;
+    const int u = tid % (4 * kNc), t = tid / (4 * kNc), pp = u / kNc, cl = u % kNc;
+    p.qoff = qk_off<DK>(a, t, hk, pp >> 1, pp & 1, 8 * cl);
+    // the swizzle of token t + kTs i differs from token t's only by bit 1
+    // (i >> 1 odd: rows 8..15 of the 16-row block; d_k = 128, t < 4)
+    const int plane = (pp ^ 2) * P::kQK;   // q hi, q lo, k hi, k lo -> Qh, Ql, Kh, Kl
+    p.lds[0] = plane + 2 * qk(t, 8 * cl);
+    p.lds[1] = QkRow<DK>::kSwz ? plane + 2 * qk(t, 8 * (cl ^ 2)) : p.lds[0];
     p.vp = tid % 32;
     p.vt = tid / 32;
     p.von = e0 + 2 * p.vp < a.dv;
@@ -313,23 +325,14 @@ struct Prefill : PrefillCore<DK, Act> {
     return __builtin_bit_cast(s4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
   }
 
-  // Prepared q / k rows of chunk c0 (the thread's two 4-channel groups of
-  // each of its tokens, hi and lo) and the raw value inputs.
+  // Prepared q / k pieces of chunk c0 and the raw value inputs.
   __device__ __forceinline__ void prod_load(Prod& p, int c0) const {
-    const int tau = opaque(p.tau), vt = opaque(p.vt), vch = opaque(p.vch);
-    if (p.on) {
-      const rsrc_t rq = qk_rows<DK>(a, t0, T, c0, kT);
-      const int sb = slot(8 * opaque(p.oc));
+    const int vt = opaque(p.vt), vch = opaque(p.vch);
+    const rsrc_t rq = qk_rows<DK>(a, t0, T, c0, kT);
+    const int step = kTs * a.Hk * 4 * DK * 2;   // workspace bytes between a thread's pieces
 #pragma unroll
-      for (int tt = 0; tt < kTpt; ++tt) {
-        const int oh = qk_off<DK>(a, kTpt * tau + tt, hk, p.isk, 0, sb);
-        const int ol = qk_off<DK>(a, kTpt * tau + tt, hk, p.isk, 1, sb);
-        p.hi[tt][0] = ld8(rq, oh);
-        p.hi[tt][1] = ld8(rq, oh + 16);
-        p.lo[tt][0] = ld8(rq, ol);
-        p.lo[tt][1] = ld8(rq, ol + 16);
-      }
-    }
+    for (int i = 0; i < kCopy; ++i)
+      p.row[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, p.qoff, i * step, 0);
     const rsrc_t rx = x_rows(c0);
     if (p.von) {
 #pragma unroll
@@ -451,23 +454,12 @@ struct Prefill : PrefillCore<DK, Act> {
     }
   }
 
-  // Store prepared chunk c: rows of K or Q (two groups of 4 channels at
-  // slot(8 oc) and +8) and the value columns.
+  // Store prepared chunk c: the K, Q pieces and the value columns.
   __device__ void prod_store(const Prod& p, int c) const {
-    if (p.on) {
-      short* hi = sp(P::kq(c, p.isk ? P::Kh : P::Qh));
-      short* lo = sp(P::kq(c, p.isk ? P::Kl : P::Ql));
-      const int tau = opaque(p.tau);
-      const int sb = slot(8 * opaque(p.oc));
+    unsigned char* buf = lds + P::kq(c, 0);
 #pragma unroll
-      for (int tt = 0; tt < kTpt; ++tt) {
-        const int o0 = qk(kTpt * tau + tt, sb), o1 = qk(kTpt * tau + tt, sb + 8);
-        *reinterpret_cast<s4*>(hi + o0) = p.hi[tt][0];
-        *reinterpret_cast<s4*>(hi + o1) = p.hi[tt][1];
-        *reinterpret_cast<s4*>(lo + o0) = p.lo[tt][0];
-        *reinterpret_cast<s4*>(lo + o1) = p.lo[tt][1];
-      }
-    }
+    for (int i = 0; i < kCopy; ++i)
+      *reinterpret_cast<u4*>(buf + p.lds[(i >> 1) & 1] + 2 * kTs * i * P::kRowQK) = p.row[i];
     if (p.von) {
       float* vt = fp(P::v(c));
       const int vp = opaque(p.vp), vtk = opaque(p.vt);

@@ -14,6 +14,7 @@ namespace {
 typedef short s4 __attribute__((ext_vector_type(4)));
 typedef short s8 __attribute__((ext_vector_type(8)));
 typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 constexpr int kC = 64;         // chunk length
 constexpr int kThreads = 512;  // 4 producer + 4 consumer waves
@@ -152,18 +153,27 @@ __device__ __forceinline__ f4 unit_lower_inverse(const f4& na, const f4& nb, int
 }
 
 // Element offset of storage slot sl of row r in a [token][d_k] bf16 plane.
-// Rows of d_k = 128 (256 bytes, all 64 banks) are swizzled: 16-byte chunk c
-// of row r sits at chunk c ^ (((r & 3) << 2) | ((r >> 2) & 3)), so both the
-// 16-rows-at-one-chunk reads of MFMA operands and the 4-rows-by-4-chunks
-// transposing reads touch 16 distinct chunks.  Narrower rows are padded by
-// 16 bytes instead.
+// Rows of d_k = 128 (256 bytes: one pass over the 64 four-byte banks) are
+// swizzled: 16-byte chunk c of row r sits at chunk c ^ f(r), f(r) =
+// 4 (r & 3) + 2 ((r >> 3) & 1).  How gfx950 serves LDS reads (measured per
+// lane pair with SQ_LDS_BANK_CONFLICT): a 16-byte read splits each half-wave
+// into two sets of 16 lanes by the parity of lane bits 2..4, a set being
+// conflict-free when its 16 chunks are distinct; an 8-byte read (the
+// transposing one too) takes 32 consecutive lanes over 64 banks.  With f the
+// MFMA operand reads (lane 16 g + r: row r, chunk 4 s + g) are conflict-free
+// -- the rows of each set map to all the even chunks, XOR 0 or 1 -- and the
+// transposing reads (rows 4 g + r / 4, chunks 4 D + r % 4) cover every
+// chunk twice, their minimum.  f depends on r mod 16 only, so offsets may
+// be moved by whole 16-row blocks.  Narrower rows are padded by 16 bytes.
 template <int DK>
 struct QkRow {
   static constexpr bool kSwz = DK == 128;
   static constexpr int kElems = kSwz ? DK : DK + 8;   // bf16 per row
+  static constexpr int kChunks = DK / 8;              // 16-byte chunks per row
+  __device__ __forceinline__ static int swz(int r) { return ((r & 3) << 2) | (((r >> 3) & 1) << 1); }
   __device__ __forceinline__ static int at(int r, int sl) {
     if constexpr (kSwz)
-      return r * DK + (((sl >> 3) ^ (((r & 3) << 2) | ((r >> 2) & 3))) << 3) + (sl & 7);
+      return r * DK + (((sl >> 3) ^ swz(r)) << 3) + (sl & 7);
     else
       return r * kElems + sl;
   }
