@@ -26,7 +26,7 @@
 //   consumers (waves 4-7), 16 value columns each, run chunk c: K S0^T,
 //     Q S0^T, U, O and the state update;
 //   producers (waves 0-3) copy chunk c + 2's prepared K, Q rows into LDS with
-//     its value conv (wave 3 also its gates, the log-decay prefix sums, from
+//     its value conv (wave 1 also its gates, the log-decay prefix sums, from
 //     inputs loaded a chunk ahead), and form chunk c + 1's A and P from the
 //     lower 16x16 tiles of K K^T and Q K^T, with the inverses of the diagonal
 //     blocks of (I + A): for N strictly lower triangular, (I + N)^{-1} =
@@ -52,6 +52,9 @@ namespace {
 constexpr int kT = 32;         // chunk length (tokens)
 constexpr int kNb = kT / 16;   // 16-token blocks per chunk
 constexpr int kTpt = kT / 8;   // tokens per producer thread
+// The producer wave that writes the gates: one of the two that form the
+// block inverses (the other two run the value conv).
+constexpr int kGateWave = 1;
 
 // LDS plan (bytes).  Chunk c's planes sit in buffer c % 3 (K, Q, V^T and
 // gates) or c % 2 (P and A): while the consumers read chunk c, the producers
@@ -265,7 +268,8 @@ struct Prefill : PrefillCore<DK, Act> {
   static constexpr int kDt = DK / 16;   // 16-row tiles of d_k
   static constexpr int kNco = DK / 4;   // channel octets of q and k
   static constexpr int kGrp = DK / 8;   // octets per head (lanes of one norm)
-  static constexpr int kRaw = kTpt + 3; // raw rows per producer thread
+  static constexpr int kVt = 8;          // tokens per value-conv thread
+  static constexpr int kVRaw = kVt + 3;  // raw rows per value-conv thread
 
   // Element offset of storage slot sl of row r in a K or Q plane.
   __device__ __forceinline__ static int qk(int r, int sl) { return QkRow<DK>::at(r, sl); }
@@ -286,9 +290,10 @@ struct Prefill : PrefillCore<DK, Act> {
     int qoff;                   // workspace bytes of piece 0 from the chunk's first row
     int lds[2];                 // LDS bytes of piece 0 (pieces with bit 1 of i set: [1])
                                 //   within a K / Q buffer
-    // value conv: channels 2 vp, 2 vp + 1 of the column block, tokens 4 vt..+3
-    uint32_t vraw[kRaw][sizeof(Act) == 2 ? 1 : 2];
-    f4 vo[2];                   // [channel], not yet stored
+    // value conv (waves 2, 3, which carry no block inverse): channels 2 vp,
+    // 2 vp + 1 of the column block, tokens 8 vt..+7
+    uint32_t vraw[kVRaw][sizeof(Act) == 2 ? 1 : 2];
+    f4 vo[2][2];                // [channel][token half], not yet stored
     int vp, vt, vch;
     bool von;
   };
@@ -301,9 +306,10 @@ struct Prefill : PrefillCore<DK, Act> {
     const int plane = (pp ^ 2) * P::kQK;   // q hi, q lo, k hi, k lo -> Qh, Ql, Kh, Kl
     p.lds[0] = plane + 2 * qk(t, 8 * cl);
     p.lds[1] = QkRow<DK>::kSwz ? plane + 2 * qk(t, 8 * (cl ^ 2)) : p.lds[0];
-    p.vp = tid % 32;
-    p.vt = tid / 32;
-    p.von = e0 + 2 * p.vp < a.dv;
+    const int vtid = tid >= kProd / 2 ? tid - kProd / 2 : 0;
+    p.vp = vtid % 32;
+    p.vt = vtid / 32;
+    p.von = tid >= kProd / 2 && e0 + 2 * p.vp < a.dv;
     p.vch = 2 * a.Hk * DK + h * a.dv + e0 + 2 * p.vp;
   }
 
@@ -336,8 +342,8 @@ struct Prefill : PrefillCore<DK, Act> {
     const rsrc_t rx = x_rows(c0);
     if (p.von) {
 #pragma unroll
-      for (int r = 0; r < kRaw; ++r) {
-        const int off = x_off(c0, c0 + kTpt * vt - 3 + r, vch);
+      for (int r = 0; r < kVRaw; ++r) {
+        const int off = x_off(c0, c0 + kVt * vt - 3 + r, vch);
         if constexpr (sizeof(Act) == 2) {
           p.vraw[r][0] = __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0);
         } else {
@@ -355,7 +361,7 @@ struct Prefill : PrefillCore<DK, Act> {
       if (p.von) {
 #pragma unroll
         for (int r = 0; r < 3; ++r) {
-          const int off = win_off(kTpt * vt - 3 + r, vch);
+          const int off = win_off(kVt * vt - 3 + r, vch);
           if constexpr (sizeof(Act) == 2) {
             p.vraw[r][0] |= __builtin_amdgcn_raw_buffer_load_b32(rw, off, 0, 0);
           } else {
@@ -374,9 +380,9 @@ struct Prefill : PrefillCore<DK, Act> {
     const float* wl = fp(P::oW);
     const float* bl = fp(P::oB);
     if (p.von) {
-      float xr[kRaw][2];
+      float xr[kVRaw][2];
 #pragma unroll
-      for (int r = 0; r < kRaw; ++r) {
+      for (int r = 0; r < kVRaw; ++r) {
         if constexpr (sizeof(Act) == 2) {
           xr[r][0] = __uint_as_float(p.vraw[r][0] << 16);
           xr[r][1] = __uint_as_float(p.vraw[r][0] & 0xffff0000u);
@@ -390,11 +396,11 @@ struct Prefill : PrefillCore<DK, Act> {
         const f4 vw = *reinterpret_cast<const f4*>(wl + 4 * (2 * p.vp + m));
         const float vb = bl[2 * p.vp + m];
 #pragma unroll
-        for (int tt = 0; tt < kTpt; ++tt) {
+        for (int tt = 0; tt < kVt; ++tt) {
           float y = vb;
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) y = fmaf(vw[jj], xr[tt + jj][m], y);
-          p.vo[m][tt] = c0 + kTpt * p.vt + tt < T ? act(y) : 0.f;
+          p.vo[m][tt / 4][tt % 4] = c0 + kVt * p.vt + tt < T ? act(y) : 0.f;
         }
       }
     }
@@ -465,7 +471,9 @@ struct Prefill : PrefillCore<DK, Act> {
       const int vp = opaque(p.vp), vtk = opaque(p.vt);
 #pragma unroll
       for (int m = 0; m < 2; ++m)
-        *reinterpret_cast<f4*>(vt + (2 * vp + m) * P::kRowV + kTpt * vtk) = p.vo[m];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          *reinterpret_cast<f4*>(vt + (2 * vp + m) * P::kRowV + kVt * vtk + 4 * hf) = p.vo[m][hf];
     }
   }
 
@@ -490,28 +498,38 @@ struct Prefill : PrefillCore<DK, Act> {
     const short* qh = sp(P::kq(c, P::Qh));
     const short* ql = sp(P::kq(c, P::Ql));
     // two accumulators per product (even and odd slices) halve the chain
-    // of dependent MFMAs
+    // of dependent MFMAs; every operand read is issued first
     f4 gs[2], ps[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       gs[i] = f4{0.f, 0.f, 0.f, 0.f};
       ps[i] = f4{0.f, 0.f, 0.f, 0.f};
     }
+    s8 ah[kSl], al[kSl], bkh[kSl], bkl[kSl], bqh[kSl], bql[kSl];
 #pragma unroll
     for (int sl = 0; sl < kSl; ++sl) {
       const int oa = 16 * JB * P::kRowQK + ob[sl], obr = 16 * IB * P::kRowQK + ob[sl];
-      const s8 ah = *reinterpret_cast<const s8*>(kh + oa);
-      const s8 al = *reinterpret_cast<const s8*>(kl + oa);
-      if constexpr (G) {
-        const s8 bkh = IB == JB ? ah : *reinterpret_cast<const s8*>(kh + obr);
-        const s8 bkl = IB == JB ? al : *reinterpret_cast<const s8*>(kl + obr);
-        gs[sl & 1] = mma32x3(ah, al, bkh, bkl, gs[sl & 1]);
+      ah[sl] = *reinterpret_cast<const s8*>(kh + oa);
+      al[sl] = *reinterpret_cast<const s8*>(kl + oa);
+      if constexpr (G && IB != JB) {
+        bkh[sl] = *reinterpret_cast<const s8*>(kh + obr);
+        bkl[sl] = *reinterpret_cast<const s8*>(kl + obr);
       }
       if constexpr (PQ) {
-        const s8 bqh = *reinterpret_cast<const s8*>(qh + obr);
-        const s8 bql = *reinterpret_cast<const s8*>(ql + obr);
-        ps[sl & 1] = mma32x3(ah, al, bqh, bql, ps[sl & 1]);
+        bqh[sl] = *reinterpret_cast<const s8*>(qh + obr);
+        bql[sl] = *reinterpret_cast<const s8*>(ql + obr);
       }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int sl = 0; sl < kSl; ++sl) {
+      if constexpr (G) {
+        if constexpr (IB == JB)
+          gs[sl & 1] = mma32x3(ah[sl], al[sl], ah[sl], al[sl], gs[sl & 1]);
+        else
+          gs[sl & 1] = mma32x3(ah[sl], al[sl], bkh[sl], bkl[sl], gs[sl & 1]);
+      }
+      if constexpr (PQ) ps[sl & 1] = mma32x3(ah[sl], al[sl], bqh[sl], bql[sl], ps[sl & 1]);
     }
     g = gs[0] + gs[1];
     pq = ps[0] + ps[1];
@@ -616,62 +634,71 @@ struct Prefill : PrefillCore<DK, Act> {
   }
 
   // ================= consumers =================
-  // First half of chunk c for the wave's 16 value columns:
-  // K S0^T, Q S0^T and the updates U.  S[d] holds rows 16d + 4 lg + v (key
-  // index) of S^T at column e0 + lr (value index); U[b] and qs[b] rows
-  // 16 b + 4 lg + v (token) at that column.
-  __device__ void updates(const f4 (&S)[kDt], f4 (&U)[kNb], f4 (&qs)[kNb], int c) const {
-    const int l = lane_now(), lr = l & 15, lg = l >> 4;
-    const float* gt = fp(P::gate(c));
-    const short* kh = sp(P::kq(c, P::Kh));
-    const short* kl = sp(P::kq(c, P::Kl));
-    const short* qh = sp(P::kq(c, P::Qh));
-    const short* ql = sp(P::kq(c, P::Ql));
-    // K S0^T and Q S0^T, rows 16 tb + 4 lg + v
-    f4 ks[kNb];
-#pragma unroll
-    for (int tb = 0; tb < kNb; ++tb) {
-      ks[tb] = f4{0.f, 0.f, 0.f, 0.f};
-      qs[tb] = f4{0.f, 0.f, 0.f, 0.f};
-    }
-    int ob[kSl];
-    op_bases(ob);
+  // The loop-carried chain of a consumer is S -> K S0^T -> U -> S; Q S0^T and
+  // the outputs hang off it.  So S enters a chunk already split into bf16
+  // (hi, lo) operands (split at the end of the previous chunk, where it
+  // overlaps the state update), K S0^T comes first, and Q S0^T follows the
+  // serial U chain, whose MFMA gaps it fills.
+  //
+  // S[d] holds rows 16d + 4 lg + v (key index) of S^T at column e0 + lr
+  // (value index); Sh[sl], Sl[sl] its 32-row slice sl as 16x16x32 B
+  // operands.  U[b] and qs[b] hold rows 16 b + 4 lg + v (token) at that
+  // column.
+  __device__ __forceinline__ static void split_state(const f4 (&S)[kDt], s8 (&Sh)[kSl],
+                                                     s8 (&Sl)[kSl]) {
 #pragma unroll
     for (int sl = 0; sl < kSl; ++sl) {
-      s8 xh[kNb], xl[kNb], yh[kNb], yl[kNb];
-#pragma unroll
-      for (int tb = 0; tb < kNb; ++tb) {
-        const int ra = 16 * tb * P::kRowQK + ob[sl];
-        xh[tb] = *reinterpret_cast<const s8*>(kh + ra);
-        xl[tb] = *reinterpret_cast<const s8*>(kl + ra);
-        yh[tb] = *reinterpret_cast<const s8*>(qh + ra);
-        yl[tb] = *reinterpret_cast<const s8*>(ql + ra);
-      }
       s4 h0, l0, h1, l1;
       split4(S[2 * sl], h0, l0);
       split4(S[2 * sl + 1], h1, l1);
-      const s8 sbh = cat(h0, h1), sbl = cat(l0, l1);
-#pragma unroll
-      for (int tb = 0; tb < kNb; ++tb) {
-        ks[tb] = mma32(xl[tb], sbh, ks[tb]);
-        qs[tb] = mma32(yl[tb], sbh, qs[tb]);
-      }
-#pragma unroll
-      for (int tb = 0; tb < kNb; ++tb) {
-        ks[tb] = mma32(xh[tb], sbl, ks[tb]);
-        qs[tb] = mma32(yh[tb], sbl, qs[tb]);
-      }
-#pragma unroll
-      for (int tb = 0; tb < kNb; ++tb) {
-        ks[tb] = mma32(xh[tb], sbh, ks[tb]);
-        qs[tb] = mma32(yh[tb], sbh, qs[tb]);
-      }
+      Sh[sl] = cat(h0, h1);
+      Sl[sl] = cat(l0, l1);
     }
+  }
+
+  // X S0^T for the chunk's rows X (K or Q planes), rows 16 tb + 4 lg + v.
+  __device__ __forceinline__ void rows_times_state(const short* xh_, const short* xl_,
+                                                   const s8 (&Sh)[kSl], const s8 (&Sl)[kSl],
+                                                   f4 (&r)[kNb]) const {
+#pragma unroll
+    for (int tb = 0; tb < kNb; ++tb) r[tb] = f4{0.f, 0.f, 0.f, 0.f};
+    int ob[kSl];
+    op_bases(ob);
+    // every operand read is issued before the first product, so their LDS
+    // latencies overlap instead of each one stalling its MFMA
+    s8 xh[kSl][kNb], xl[kSl][kNb];
+#pragma unroll
+    for (int sl = 0; sl < kSl; ++sl)
+#pragma unroll
+      for (int tb = 0; tb < kNb; ++tb) {
+        const int ra = 16 * tb * P::kRowQK + ob[sl];
+        xh[sl][tb] = *reinterpret_cast<const s8*>(xh_ + ra);
+        xl[sl][tb] = *reinterpret_cast<const s8*>(xl_ + ra);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int sl = 0; sl < kSl; ++sl) {
+#pragma unroll
+      for (int tb = 0; tb < kNb; ++tb) r[tb] = mma32(xl[sl][tb], Sh[sl], r[tb]);
+#pragma unroll
+      for (int tb = 0; tb < kNb; ++tb) r[tb] = mma32(xh[sl][tb], Sl[sl], r[tb]);
+#pragma unroll
+      for (int tb = 0; tb < kNb; ++tb) r[tb] = mma32(xh[sl][tb], Sh[sl], r[tb]);
+    }
+  }
+
+  // First half of chunk c for the wave's 16 value columns: K S0^T, the
+  // updates U (and their (hi, lo) split), then Q S0^T.
+  __device__ void updates(const s8 (&Sh)[kSl], const s8 (&Sl)[kSl], f4 (&U)[kNb],
+                          s4 (&uh)[kNb], s4 (&ul)[kNb], f4 (&qs)[kNb], int c) const {
+    const int l = lane_now(), lr = l & 15, lg = l >> 4;
+    const float* gt = fp(P::gate(c));
+    f4 ks[kNb];
+    rows_times_state(sp(P::kq(c, P::Kh)), sp(P::kq(c, P::Kl)), Sh, Sl, ks);
     // U_b = X_bb (b_b R_b - sum_{j<b} A_bj U_j),  R = V - e^g (K S0^T)
     const float* vt = fp(P::v(c)) + (e0 % kCols + lr) * P::kRowV;
     const short* ah_ = sp(P::pa(c, P::Ah));
     const short* al_ = sp(P::pa(c, P::Al));
-    s4 uh[kNb], ul[kNb];
 #pragma unroll
     for (int b = 0; b < kNb; ++b) {
       const int row = (16 * b + lr) * P::kRowT;
@@ -693,19 +720,19 @@ struct Prefill : PrefillCore<DK, Act> {
       U[b] = mma16x3(xh, xl, zh, zl, f4{0.f, 0.f, 0.f, 0.f});
       split4(U[b], uh[b], ul[b]);
     }
+    rows_times_state(sp(P::kq(c, P::Qh)), sp(P::kq(c, P::Ql)), Sh, Sl, qs);
   }
 
   // Second half: O = e^g (Q S0^T) + P U to the output rows of chunk c
   // (rows past the sequence lie past the descriptor and are dropped), then
-  // S^T <- e^{g_c} S^T + K^T diag(e^{g_c - g}) U.
-  __device__ void outputs_and_state(f4 (&S)[kDt], const f4 (&U)[kNb], const f4 (&qs)[kNb],
-                                    int c) const {
+  // S^T <- e^{g_c} S^T + K^T diag(e^{g_c - g}) U, and its split for the
+  // next chunk.
+  __device__ void outputs_and_state(f4 (&S)[kDt], s8 (&Sh)[kSl], s8 (&Sl)[kSl],
+                                    const f4 (&U)[kNb], const s4 (&uh)[kNb],
+                                    const s4 (&ul)[kNb], const f4 (&qs)[kNb], int c) const {
     const int c0 = c * kT;
     const int l = lane_now(), lr = l & 15, lg = l >> 4;
     const float* gt = fp(P::gate(c));
-    s4 uh[kNb], ul[kNb];
-#pragma unroll
-    for (int b = 0; b < kNb; ++b) split4(U[b], uh[b], ul[b]);
     const s8 u0h = cat(uh[0], uh[1]), u0l = cat(ul[0], ul[1]);
     {
       const short* ph_ = sp(P::pa(c, P::Ph));
@@ -753,29 +780,25 @@ struct Prefill : PrefillCore<DK, Act> {
 #pragma unroll
       for (int D = 0; D < kSl; ++D) tb0[D] = qk(4 * g + (r >> 2), 32 * D + 8 * (r & 3));
     }
-    constexpr int kG = kDt < 4 ? kDt : 4;
+    // all transposing reads first (their latencies overlap), then the products
+    s8 th[kDt], tl[kDt];
 #pragma unroll
-    for (int d0 = 0; d0 < kDt; d0 += kG) {
-      s8 th[kG], tl[kG];
-      f4 acc[kG];
-#pragma unroll
-      for (int dd = 0; dd < kG; ++dd) {
-        const int d = d0 + dd;
-        const int r0 = tb0[d >> 1] + 4 * (d & 1);
-        const int r1 = r0 + 16 * P::kRowQK;
-        th[dd] = cat(ld_tr(kh + r0), ld_tr(kh + r1));
-        tl[dd] = cat(ld_tr(kl + r0), ld_tr(kl + r1));
-        acc[dd] = ec * S[d];
-      }
-#pragma unroll
-      for (int dd = 0; dd < kG; ++dd) acc[dd] = mma32(tl[dd], wh, acc[dd]);
-#pragma unroll
-      for (int dd = 0; dd < kG; ++dd) acc[dd] = mma32(th[dd], wl, acc[dd]);
-#pragma unroll
-      for (int dd = 0; dd < kG; ++dd) acc[dd] = mma32(th[dd], wh, acc[dd]);
-#pragma unroll
-      for (int dd = 0; dd < kG; ++dd) S[d0 + dd] = acc[dd];
+    for (int d = 0; d < kDt; ++d) {
+      const int r0 = tb0[d >> 1] + 4 * (d & 1);
+      const int r1 = r0 + 16 * P::kRowQK;
+      th[d] = cat(ld_tr(kh + r0), ld_tr(kh + r1));
+      tl[d] = cat(ld_tr(kl + r0), ld_tr(kl + r1));
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = 0; d < kDt; ++d) S[d] = ec * S[d];
+#pragma unroll
+    for (int d = 0; d < kDt; ++d) S[d] = mma32(tl[d], wh, S[d]);
+#pragma unroll
+    for (int d = 0; d < kDt; ++d) S[d] = mma32(th[d], wl, S[d]);
+#pragma unroll
+    for (int d = 0; d < kDt; ++d) S[d] = mma32(th[d], wh, S[d]);
+    split_state(S, Sh, Sl);
   }
 };
 
@@ -820,7 +843,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
   k.load_taps();
 
   // One barrier per chunk.  Between barriers c - 1 and c the consumers run
-  // chunk c while the producers store chunk c + 2 (wave 3: its gates too) and
+  // chunk c while the producers store chunk c + 2 (wave 1: its gates too) and
   // form chunk c + 1's A, P and inverses (its K, Q and gates were stored an
   // iteration earlier).
   if (k.tid < kProd) {
@@ -830,7 +853,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
     if (nch > 0) k.prod_load(p, 0);
     lds_barrier();            // planes zeroed, taps loaded
     typename K::GateIn gin{0u, 0u, 0};
-    if (k.wave == 3) {
+    if (k.wave == kGateWave) {
       for (int c = 0; c < 2 && c < nch; ++c) k.gates(k.gate_load(c * kT), c);
       if (nch > 2) gin = k.gate_load(2 * kT);
     }
@@ -851,7 +874,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
         if (c + 3 < nch) k.prod_load(p, (c + 3) * kT);
       }
       if (c + 1 < nch) k.gram_phase(c + 1);
-      if (k.wave == 3 && c + 2 < nch) {
+      if (k.wave == kGateWave && c + 2 < nch) {
         k.gates(gin, c + 2);
         if (c + 3 < nch) gin = k.gate_load((c + 3) * kT);
       }
@@ -872,15 +895,16 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
                                            static_cast<int64_t>(k.e0 + k.lr) * DK + 16 * d +
                                            4 * k.lg);
     }
+    s8 Sh[K::kSl], Sl[K::kSl];
+    K::split_state(S, Sh, Sl);
     lds_barrier();            // planes zeroed, taps loaded
     lds_barrier();            // chunks 0 and 1 stored, their gates written
     lds_barrier();            // chunk 0 complete
     for (int c = 0; c < nch; ++c) {
       f4 U[kNb], qs[kNb];
-      if (cols) k.updates(S, U, qs, c);
-      // chunk c + 2's gates (their buffer's last readers, chunk c - 1 here
-      // and chunk c - 1's A and P, are done), then the inputs of the next
-      if (cols) k.outputs_and_state(S, U, qs, c);
+      s4 uh[kNb], ul[kNb];
+      if (cols) k.updates(Sh, Sl, U, uh, ul, qs, c);
+      if (cols) k.outputs_and_state(S, Sh, Sl, U, uh, ul, qs, c);
       const int32_t cs = __builtin_amdgcn_readfirstlane(ckpt_slot(a, s, (c + 1) * kT, k.T));
       if (cols && cs >= 0) {  // the state after (c + 1) * kT tokens, to a checkpoint slot
         const int l = k.lane_now();

@@ -21,21 +21,25 @@ constexpr int kThreads = 512;  // 4 producer + 4 consumer waves
 constexpr int kProd = 256;     // producer threads
 constexpr int kCols = 64;      // value columns per workgroup (16 per consumer wave)
 
-// x ~= hi + lo with hi = bf16(x), lo = bf16(x - hi) (round to nearest even).
-__device__ __forceinline__ void split(float x, short& hi, short& lo) {
-  const __bf16 h = static_cast<__bf16>(x);
-  const __bf16 l = static_cast<__bf16>(x - static_cast<float>(h));
-  hi = __builtin_bit_cast(short, h);
-  lo = __builtin_bit_cast(short, l);
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
+// x ~= hi + lo with hi = bf16(x), lo = bf16(x - hi) (round to nearest even),
+// two values at a time: one packed conversion per pair, and the pair's hi
+// words are already the packed operand halves.
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{x0, x1}, bf2));
+  const f2 r = {x0 - __uint_as_float(h << 16), x1 - __uint_as_float(h & 0xffff0000u)};
+  hi = h;
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf2));
 }
 __device__ __forceinline__ void split4(f4 x, s4& hi, s4& lo) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    short h, l;
-    split(x[i], h, l);
-    hi[i] = h;
-    lo[i] = l;
-  }
+  uint32_t h0, l0, h1, l1;
+  split2(x[0], x[1], h0, l0);
+  split2(x[2], x[3], h1, l1);
+  hi = __builtin_bit_cast(s4, u2{h0, h1});
+  lo = __builtin_bit_cast(s4, u2{l0, l1});
 }
 
 __device__ __forceinline__ f4 mma32(s8 a, s8 b, f4 c) {
