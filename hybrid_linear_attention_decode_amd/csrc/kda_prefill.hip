@@ -325,11 +325,15 @@ struct KdaChunk : PrefillCore<DK, Act> {
 
   // ================= producers =================
   // Thread (co, tau): channel octet co of q|k (q first), tokens 8 tau..+7.
+  // Octet oc of a head is the 8 channels of storage chunk oc of the K / Q
+  // rows, 32 (oc / 4) + 4 (oc % 4) + {0..3, 16..19} (see slot()), so each
+  // row of a thread is stored as one 16-byte chunk.
+  __device__ __forceinline__ static int oct_base(int oc) { return 32 * (oc >> 2) + 4 * (oc & 3); }
   struct Prod {
     Row8<Act> raw[11];        // rows 8 tau - 3 .. 8 tau + 7 of a chunk
     Row8<Act> dec[8];         // decays of tokens 8 tau .. +7 at the 8 channels
-    s4 eh[8][2], el[8][2];    // KE (k) or QE (q) rows, not yet stored
-    s4 fh[4][2], fl[4][2];    // KF rows: tokens 0..3 of the octet (k thread), 4..7 (q thread)
+    s8 eh[8], el[8];          // KE (k) or QE (q) rows, not yet stored
+    s8 fh[4], fl[4];          // KF rows: tokens 0..3 of the octet (k thread), 4..7 (q thread)
     float lam[8];             // decay over the whole 16-token block
     uint32_t diag[8];         // this thread's 32 bytes of a diagonal-block record
     float beta;               // wave 3: b of token = lane
@@ -343,7 +347,7 @@ struct KdaChunk : PrefillCore<DK, Act> {
     p.tau = tid / kNco;
     p.isk = p.co >= kGrp;
     p.oc = p.isk ? p.co - kGrp : p.co;
-    p.ch = (p.isk ? a.Hk * DK : 0) + hk * DK + 8 * p.oc;
+    p.ch = (p.isk ? a.Hk * DK : 0) + hk * DK + oct_base(p.oc);
   }
 
   // Taps and bias of the key head's q and k channels, stored [m][octet] (m =
@@ -354,7 +358,10 @@ struct KdaChunk : PrefillCore<DK, Act> {
     float* bs = fp(P::oB);
     for (int i = tid; i < 2 * DK; i += kThreads) {
       const int ch = i < DK ? hk * DK + i : a.Hk * DK + hk * DK + (i - DK);
-      const int at = (i & 7) * kNco + (i >> 3);
+      // channel r of a 32-block: octet 4 (block) + (r % 16) / 4, place
+      // r % 4 (+ 4 in the block's upper half)
+      const int r = i & 31, oc = 4 * (i >> 5) + ((r & 15) >> 2), m = (r & 3) + 4 * (r >> 4);
+      const int at = m * kNco + oc;
       *reinterpret_cast<f4*>(wt + 4 * at) = f4{tap(ch, 0), tap(ch, 1), tap(ch, 2), tap(ch, 3)};
       bs[at] = a.bias ? to_f32(static_cast<const Act*>(a.bias)[ch]) : 0.f;
     }
@@ -365,20 +372,20 @@ struct KdaChunk : PrefillCore<DK, Act> {
     if (p.on) {
       const rsrc_t rx = x_rows(c0);
 #pragma unroll
-      for (int r = 0; r < 11; ++r) p.raw[r].load(rx, x_off(c0, c0 + 8 * tau - 3 + r, ch));
+      for (int r = 0; r < 11; ++r) p.raw[r].load_split(rx, x_off(c0, c0 + 8 * tau - 3 + r, ch));
       const int n = T - c0 < kC ? T - c0 : kC;
       const int64_t rowe = static_cast<int64_t>(a.Hv) * DK;
       const rsrc_t ra = make_rsrc(static_cast<const Act*>(a.alpha) + (t0 + static_cast<int64_t>(c0)) * rowe,
                                   static_cast<uint32_t>(n * rowe * sizeof(Act)));
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt)
-        p.dec[tt].load(ra, static_cast<int>((((8 * tau + tt) * a.Hv + h) * DK + 8 * oc) * sizeof(Act)));
+        p.dec[tt].load_split(ra, static_cast<int>((((8 * tau + tt) * a.Hv + h) * DK + oct_base(oc)) * sizeof(Act)));
       if (c0 == 0) {
         const rsrc_t rw = win_rows();
 #pragma unroll
         for (int r = 0; r < 3; ++r) {
           Row8<Act> wr;
-          wr.load(rw, win_off(8 * tau - 3 + r, ch));
+          wr.load_split(rw, win_off(8 * tau - 3 + r, ch));
           p.raw[r].merge(wr);
         }
       }
@@ -484,16 +491,16 @@ struct KdaChunk : PrefillCore<DK, Act> {
           const float kv = tt < 4 ? yv : __shfl_xor(yv, kGrp);
           vf[m >> 2][m & 3] = kv * fs[tt & 3][m];
         }
-        split4(ve[0], p.eh[tt][0], p.el[tt][0]);
-        split4(ve[1], p.eh[tt][1], p.el[tt][1]);
         s4 h0, l0, h1, l1;
+        split4(ve[0], h0, l0);
+        split4(ve[1], h1, l1);
+        p.eh[tt] = cat(h0, h1);
+        p.el[tt] = cat(l0, l1);
         split4(vf[0], h0, l0);
         split4(vf[1], h1, l1);
         if (tt < 4 || !p.isk) {
-          p.fh[tt & 3][0] = h0;
-          p.fh[tt & 3][1] = h1;
-          p.fl[tt & 3][0] = l0;
-          p.fl[tt & 3][1] = l1;
+          p.fh[tt & 3] = cat(h0, h1);
+          p.fl[tt & 3] = cat(l0, l1);
         }
       }
     }
@@ -507,14 +514,12 @@ struct KdaChunk : PrefillCore<DK, Act> {
       short* eh = sp(p.isk ? P::oEKh : P::oEQh);
       short* el = sp(p.isk ? P::oEKl : P::oEQl);
       const int tau = opaque(p.tau);
-      const int sb = slot(8 * opaque(p.oc));
+      const int sb = 8 * opaque(p.oc);   // the octet's storage chunk
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
-        const int o0 = qk(8 * tau + tt, sb), o1 = qk(8 * tau + tt, sb + 8);
-        *reinterpret_cast<s4*>(eh + o0) = p.eh[tt][0];
-        *reinterpret_cast<s4*>(eh + o1) = p.eh[tt][1];
-        *reinterpret_cast<s4*>(el + o0) = p.el[tt][0];
-        *reinterpret_cast<s4*>(el + o1) = p.el[tt][1];
+        const int o = qk(8 * tau + tt, sb);
+        *reinterpret_cast<s8*>(eh + o) = p.eh[tt];
+        *reinterpret_cast<s8*>(el + o) = p.el[tt];
       }
       {
         short* fh = sp(P::oFKh);
@@ -522,18 +527,16 @@ struct KdaChunk : PrefillCore<DK, Act> {
         const int t4 = 8 * tau + (p.isk ? 0 : 4);
 #pragma unroll
         for (int jx = 0; jx < 4; ++jx) {
-          const int o0 = qk(t4 + jx, sb), o1 = qk(t4 + jx, sb + 8);
-          *reinterpret_cast<s4*>(fh + o0) = p.fh[jx][0];
-          *reinterpret_cast<s4*>(fh + o1) = p.fh[jx][1];
-          *reinterpret_cast<s4*>(fl + o0) = p.fl[jx][0];
-          *reinterpret_cast<s4*>(fl + o1) = p.fl[jx][1];
+          const int o = qk(t4 + jx, sb);
+          *reinterpret_cast<s8*>(fh + o) = p.fh[jx];
+          *reinterpret_cast<s8*>(fl + o) = p.fl[jx];
         }
       }
       if (p.isk) {
         if (tau & 1) {
-          float* lam = fp(P::oLam) + (tau >> 1) * DK + 8 * opaque(p.oc);
+          float* lam = fp(P::oLam) + (tau >> 1) * DK + oct_base(opaque(p.oc));
           *reinterpret_cast<f4*>(lam) = f4{p.lam[0], p.lam[1], p.lam[2], p.lam[3]};
-          *reinterpret_cast<f4*>(lam + 4) = f4{p.lam[4], p.lam[5], p.lam[6], p.lam[7]};
+          *reinterpret_cast<f4*>(lam + 16) = f4{p.lam[4], p.lam[5], p.lam[6], p.lam[7]};
         }
       }
     }
@@ -916,15 +919,17 @@ __global__ void __launch_bounds__(kThreads, 1) kda_chunk_kernel(PrefillArgs a) {
     k.prod_init(p);
     if (nch > 0) k.prod_load(p, 0);
     lds_barrier();            // planes zeroed, taps loaded
-    // The next chunk's raw rows and decays are fetched right after a chunk's
-    // planes are stored (into the registers the stored results free), and
-    // land during the off-diagonal blocks and the wait for the consumers.
+    // The next chunk's raw rows and decays are fetched once a chunk's planes
+    // are stored and its off-diagonal blocks formed (into registers those
+    // phases no longer hold), and land during the consumers' pass, which the
+    // preparation that needs them overlaps; fetched earlier, they would be
+    // spilled with a wait for the whole prefetch inside the serial store phase.
     if (nch > 0) {
       k.prod_prep(p, 0);
       k.prod_store(p);
-      if (nch > 1) k.prod_load(p, kC);
       lds_barrier();
       k.gram_phase();
+      if (nch > 1) k.prod_load(p, kC);
       lds_barrier();
     }
     for (int c = 0; c < nch; ++c) {
@@ -933,9 +938,9 @@ __global__ void __launch_bounds__(kThreads, 1) kda_chunk_kernel(PrefillArgs a) {
       lds_barrier();          // consumers are done with chunk c
       if (next) {
         k.prod_store(p);
-        if (c + 2 < nch) k.prod_load(p, (c + 2) * kC);
         lds_barrier();
         k.gram_phase();
+        if (c + 2 < nch) k.prod_load(p, (c + 2) * kC);
         lds_barrier();
       }
     }

@@ -100,6 +100,22 @@ struct Row8 {
       w[4] = v[0], w[5] = v[1], w[6] = v[2], w[7] = v[3];
     }
   }
+  // Channels c..c+3 and c+16..c+19 (the channels of one 16-byte storage
+  // chunk of K / Q rows): off is c's byte offset.
+  __device__ __forceinline__ void load_split(rsrc_t r, int off) {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    if constexpr (kWords == 4) {
+      const u2 u = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+      const u2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off + 32, 0, 0);
+      w[0] = u[0], w[1] = u[1], w[2] = v[0], w[3] = v[1];
+    } else {
+      const u4 u = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+      const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 64, 0, 0);
+      w[0] = u[0], w[1] = u[1], w[2] = u[2], w[3] = u[3];
+      w[4] = v[0], w[5] = v[1], w[6] = v[2], w[7] = v[3];
+    }
+  }
   __device__ __forceinline__ void merge(const Row8& o) {
 #pragma unroll
     for (int i = 0; i < kWords; ++i) w[i] |= o.w[i];
