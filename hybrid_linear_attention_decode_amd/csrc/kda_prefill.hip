@@ -919,28 +919,30 @@ __global__ void __launch_bounds__(kThreads, 1) kda_chunk_kernel(PrefillArgs a) {
     k.prod_init(p);
     if (nch > 0) k.prod_load(p, 0);
     lds_barrier();            // planes zeroed, taps loaded
-    // The next chunk's raw rows and decays are fetched once a chunk's planes
-    // are stored and its off-diagonal blocks formed (into registers those
-    // phases no longer hold), and land during the consumers' pass, which the
-    // preparation that needs them overlaps; fetched earlier, they would be
-    // spilled with a wait for the whole prefetch inside the serial store phase.
+    // A chunk's raw rows and decays are fetched when its preparation starts:
+    // the preparation runs beside the consumers' pass over the chunk before,
+    // which is longer by more than the fetch takes, and fetched any earlier
+    // (while the stored rows or the off-diagonal operands hold registers)
+    // they were spilled, each spill waiting for the whole fetch inside the
+    // serial store and off-diagonal phases.
     if (nch > 0) {
       k.prod_prep(p, 0);
       k.prod_store(p);
       lds_barrier();
       k.gram_phase();
-      if (nch > 1) k.prod_load(p, kC);
       lds_barrier();
     }
     for (int c = 0; c < nch; ++c) {
       const bool next = c + 1 < nch;
-      if (next) k.prod_prep(p, (c + 1) * kC);
+      if (next) {
+        k.prod_load(p, (c + 1) * kC);
+        k.prod_prep(p, (c + 1) * kC);
+      }
       lds_barrier();          // consumers are done with chunk c
       if (next) {
         k.prod_store(p);
         lds_barrier();
         k.gram_phase();
-        if (c + 2 < nch) k.prod_load(p, (c + 2) * kC);
         lds_barrier();
       }
     }
