@@ -287,6 +287,37 @@ def path_record(ms_per_call: float, nbytes: float, tokens: int, what: str) -> di
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def bench_decode_graph(torch, gdn, synth, n_calls=48, replays=20):
+    """The headline decode (Qwen3.5 shape, B=64, 1024-slot pool) as a serving
+    loop runs it: 48 calls (one per layer of a step, each with its own index
+    row) captured in one HIP graph and replayed; the ticket tail keeps its
+    caller-owned work counter (one word: the captured calls run in order).
+    Returns the graph's per-call record and, for comparison, the same 48
+    calls launched eagerly."""
+    shape = synth.QWEN35
+    b = DecodeBench(torch, gdn, synth, shape, 64, 1024, n_calls, seed=7)
+    for c in range(n_calls):
+        b.call(c)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    eager_stream = b.stream
+    with torch.cuda.graph(graph):
+        b.stream = ct.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for c in range(n_calls):
+            b.call(c)
+    b.stream = eager_stream
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms = time_calls(torch, lambda _c: graph.replay(), 0, replays) / (replays * n_calls)
+    eager = time_calls(torch, b.call, 0, n_calls) / n_calls
+    nbytes = decode_bytes(shape, 64)
+    rec = path_record(ms, nbytes, 64, "GDN decode, Qwen3.5 shape, B=64, pool 1024: 48 calls "
+                      "captured in one HIP graph, replayed (work counter kept)")
+    rec["eager_us_per_call_same_calls"] = round(eager * 1e3, 2)
+    return rec
+
+
 def bench_decode_b16(torch, gdn, synth, K=500, W=50):
     """Qwen3.5-shaped decode at B=16 on a 256-slot pool: indices rotating
     through a seeded permutation (reuse after 15 calls), and the literal
@@ -697,7 +728,8 @@ def main():
         copy_calibration(torch)
         return
     if args.only == "paths":
-        for r in (*bench_decode_b16(torch, gdn, synth), *bench_spec(torch, gdn, synth),
+        for r in (*bench_decode_b16(torch, gdn, synth), bench_decode_graph(torch, gdn, synth),
+                  *bench_spec(torch, gdn, synth),
                   *bench_spec_pool(torch, gdn, synth), *bench_kda_stack(torch, gdn, synth),
                   *bench_slot_pack(torch, gdn, synth),
                   bench_prefill(torch, gdn, synth), *bench_prefill_ckpt(torch, gdn, synth),
@@ -739,11 +771,13 @@ def main():
 
     paths = None
     if args.only == "all":
-        log("bench: other paths (B=16 decode, speculative draft + commit with snapshots in "
+        log("bench: other paths (B=16 decode, B=64 decode replayed from a HIP graph, "
+            "speculative draft + commit with snapshots in "
             "spec buffers and in pool slots, KDA 48-layer stack with separate and fused slot "
             "preparation, slot pack / unpack, chunked prefill of both layers, with checkpoints and "
             "the append from them)")
         d16, d16_iid = bench_decode_b16(torch, gdn, synth)
+        dgraph = bench_decode_graph(torch, gdn, synth)
         draft, commit = bench_spec(torch, gdn, synth)
         pdraft, pcommit = bench_spec_pool(torch, gdn, synth)
         kda, kda_fused = bench_kda_stack(torch, gdn, synth)
@@ -752,6 +786,7 @@ def main():
         pfc, app = bench_prefill_ckpt(torch, gdn, synth)
         pfk = bench_prefill(torch, gdn, synth, shape=synth.KDA)
         paths = {"decode_qwen35_b16": d16, "decode_qwen35_b16_iid": d16_iid,
+                 "decode_qwen35_b64_graph": dgraph,
                  "spec_draft_qwen35_b64_t7": draft,
                  "spec_commit_qwen35_b64": commit,
                  "spec_draft_pool_slots_qwen35_b64_t7": pdraft,
