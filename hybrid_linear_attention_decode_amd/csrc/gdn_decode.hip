@@ -442,14 +442,19 @@ __global__ void __launch_bounds__(512, 4) decode_kernel(const DecodeArgs a) {
   __shared__ int drawn;
   const int unit = decode_unit(a, drawn);
   if (unit < 0) return;
-  const Cta cta(a, unit);
 
   // The unit's destination slot (an index outside the pool skips the unit)
   // and source slot (the destination itself, a copy-on-write source, or
   // negative for a zero start; a source past the pool skips the unit).
-  // The slot lookups and the inputs that need no slot are in flight together.
-  const int32_t sl = uniform(a.idx[cta.b]);
-  const int32_t sr_in = a.init ? uniform(a.init[cta.b]) : sl;
+  // Both lookups go out first and together, as scalar loads (the index
+  // arrays are only read here), then the inputs that need no slot; the
+  // workgroup waits for the lookups alone.
+  typedef const __attribute__((address_space(4))) int32_t* const_i32;
+  const int b = unit / a.Hk;
+  const int32_t* srcs = a.init ? a.init : a.idx;
+  const int32_t sl = ((const_i32)a.idx)[b];
+  const int32_t sr_in = ((const_i32)srcs)[b];
+  const Cta cta(a, unit);
   typename Cta::Raw raw;
   cta.load_fixed(raw);
   asm volatile("" ::: "memory");
