@@ -29,7 +29,8 @@
 // The four diagonal 16 x 16 blocks need e^{g_r - g_i} inside one block, which
 // has no bounded factorisation; they are formed exactly, with products of
 // the decays, by a first kernel (kda_diag_kernel) that also inverts each
-// block of I + A by forward substitution in fp32.  The second kernel
+// block of I + A with the nilpotent product series on MFMA that the
+// scalar-decay kernel uses.  The second kernel
 // (kda_chunk_kernel) has the work split and pipeline of the scalar-decay
 // kernel (gdn_prefill.hip): producers prepare the next chunk (conv1d, SiLU,
 // L2 norm, the decay products and the three planes), all waves form the six
@@ -52,7 +53,8 @@ __device__ __forceinline__ int64_t ws_block(int s, int t0, int jb) {
 
 // =====================================================================
 // Kernel 1: the diagonal 16 x 16 blocks, one workgroup of four waves per
-// (sequence, value head, token block).  Workspace record (2 KiB): lane
+// (sequence, value head, token block); past 65535 blocks in a sequence,
+// workgroup y takes blocks y, y + 65535, ...  Workspace record (2 KiB): lane
 // l = 4 r + q holds columns 4q..4q+3 of row r as X hi, X lo, P hi, P lo (4
 // bf16 each), where X = (I + N)^{-1}, N_ri = b_r sum_c k_rc k_ic
 // prod_{i < s <= r} a_sc (i < r), and P_ri = sum_c q_rc k_ic
