@@ -6,15 +6,18 @@
 // writer of every conv-window channel it touches: no cross-workgroup
 // ordering exists.
 //
-// Schedule.  The grid is B * H_k workgroups, one per unit, each small in LDS
-// (the activations of a few tokens) and in registers, and the dispatcher
-// hands the next unit to whichever CU frees a slot first.  Units of up to
-// 64 KiB of state run two per CU (one's stores drain while the other's loads
-// stream in); larger ones one per CU, which keeps fewer requests queued at
-// HBM and measures faster.
-// Within a unit the first-token inputs (x, conv window, taps, gates, betas)
-// are loaded first and the state rows, straight into registers, once they
-// are in: the conv and the norms run while the state streams in.
+// Schedule.  Each workgroup is small in LDS (the activations of a few
+// tokens) and in registers.  The first three quarters of the units are
+// fixed, a block of requests per XCD; with the caller's work counter the
+// rest go out by ticket to the workgroups that start next, so XCDs that
+// stream faster take more of them (decode_unit); without it every unit is
+// fixed.  Units of up to 64 KiB of state run two per CU (one's stores drain
+// while the other's loads stream in); larger ones one per CU, which keeps
+// fewer requests queued at HBM and measures faster.
+// Within a unit the slot lookups and the first-token inputs (x, taps,
+// gates, betas, then the source slot's conv window) are issued first and
+// the state rows, straight into registers, right after them; loads complete
+// in order, so the conv and the norms run while the state streams in.
 //
 // Per unit, per token (state in registers across all T tokens of the call):
 //   conv update + SiLU of the unit's channels          -> LDS
