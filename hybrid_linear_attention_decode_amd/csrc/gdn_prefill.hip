@@ -114,9 +114,13 @@ __device__ __forceinline__ int qk_off(const PrefillArgs& a, int r, int hk, bool 
 // each repeat it.  Group oc of a head holds channels 4j..4j+3 and
 // 4j+16..4j+19 of 32-block b (oc = 4b + j): exactly the channels of storage
 // slots 8 oc..8 oc+7, so each row half goes out as one 16-byte store.
-template <int DK, typename Act>
+template <int DK, typename Act, int DKR>
 struct QkPrep : PrefillCore<DK, Act> {
   GDN_PREFILL_CORE(DK, Act);
+  // DKR: the layer's d_k.  Below DK (d_k = 16 runs the d_k = 32 layout) the
+  // channels from DKR on are padding: read as zero with zero taps and bias,
+  // so their prepared rows are zero and add nothing to any product.
+  static constexpr bool kPad = DKR < DK;
   static constexpr int kNco = DK / 4;   // channel groups of q and k
   static constexpr int kGrp = DK / 8;   // groups per head (lanes of one norm)
   static constexpr int kRaw = kTpt + 3; // raw rows per thread
@@ -131,13 +135,15 @@ struct QkPrep : PrefillCore<DK, Act> {
   __device__ __forceinline__ static void load_row(Row8<Act>& r, rsrc_t rs, int off) {
     typedef uint32_t u2 __attribute__((ext_vector_type(2)));
     typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    // the second half (16 channels on) lies in the padding when d_k = 16
+    const uint32_t off1 = kPad ? kOutOfRange : static_cast<uint32_t>(off + 16 * kE);
     if constexpr (kE == 2) {
       const u2 a0 = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
-      const u2 a1 = __builtin_amdgcn_raw_buffer_load_b64(rs, off + 16 * kE, 0, 0);
+      const u2 a1 = __builtin_amdgcn_raw_buffer_load_b64(rs, off1, 0, 0);
       r.w[0] = a0[0], r.w[1] = a0[1], r.w[2] = a1[0], r.w[3] = a1[1];
     } else {
       const u4 a0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-      const u4 a1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * kE, 0, 0);
+      const u4 a1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off1, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) r.w[i] = a0[i], r.w[4 + i] = a1[i];
     }
@@ -205,6 +211,15 @@ struct QkPrep : PrefillCore<DK, Act> {
         for (int m = 0; m < 8; ++m) bias[m] = to_f32(b[c + (m < 4 ? m : 12 + m)]);
       }
     }
+    if constexpr (kPad) {
+      // the second half's taps and bias were read from the channels that
+      // follow (in bounds); the padding has none
+#pragma unroll
+      for (int m = 4; m < 8; ++m) {
+        wt[m] = f4{0.f, 0.f, 0.f, 0.f};
+        bias[m] = 0.f;
+      }
+    }
   }
 
   // Chunks first, first + step, ... of the sequence, the next one's rows
@@ -214,7 +229,7 @@ struct QkPrep : PrefillCore<DK, Act> {
     const int co = tid % kNco, tau = tid / kNco;
     const bool isk = co >= kGrp;
     const int oc = isk ? co - kGrp : co;
-    const int c = (isk ? a.Hk * DK : 0) + hk * DK + chan(oc, 0);
+    const int c = (isk ? a.Hk * DKR : 0) + hk * DKR + chan(oc, 0);
     if (first * kT >= T) return;
     f4 wt[8];
     float bias[8];
@@ -260,9 +275,12 @@ struct QkPrep : PrefillCore<DK, Act> {
   }
 };
 
-template <int DK, typename Act>
+template <int DK, typename Act, int DKR>
 struct Prefill : PrefillCore<DK, Act> {
   GDN_PREFILL_CORE(DK, Act);
+  // DKR: the layer's d_k (DK but for d_k = 16, run in the d_k = 32 layout;
+  // the padded K, Q channels are zero, so rows DKR.. of S^T stay zero and
+  // are neither read nor written).
   using P = Plan<DK>;
   static constexpr int kSl = DK / 32;   // 32-wide slices of d_k
   static constexpr int kDt = DK / 16;   // 16-row tiles of d_k
@@ -310,7 +328,7 @@ struct Prefill : PrefillCore<DK, Act> {
     p.vp = vtid % 32;
     p.vt = vtid / 32;
     p.von = tid >= kProd / 2 && e0 + 2 * p.vp < a.dv;
-    p.vch = 2 * a.Hk * DK + h * a.dv + e0 + 2 * p.vp;
+    p.vch = 2 * a.Hk * DKR + h * a.dv + e0 + 2 * p.vp;
   }
 
   // Taps and bias of the workgroup's value columns into LDS (all threads).
@@ -318,7 +336,7 @@ struct Prefill : PrefillCore<DK, Act> {
     float* wt = fp(P::oW);
     float* bs = fp(P::oB);
     for (int i = tid; i < P::kWch; i += kThreads) {
-      const int ch = 2 * a.Hk * DK + h * a.dv + e0 + i;
+      const int ch = 2 * a.Hk * DKR + h * a.dv + e0 + i;
       const bool ok = e0 + i < a.dv;
       f4 t = {0.f, 0.f, 0.f, 0.f};
       if (ok) t = f4{tap(ch, 0), tap(ch, 1), tap(ch, 2), tap(ch, 3)};
@@ -802,10 +820,10 @@ struct Prefill : PrefillCore<DK, Act> {
   }
 };
 
-template <int DK, typename Act>
+template <int DK, typename Act, int DKR>
 __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
-  using K = Prefill<DK, Act>;
+  using K = Prefill<DK, Act, DKR>;
   using P = Plan<DK>;
   K k{{a, lds_raw}};
   k.tid = threadIdx.x;
@@ -885,14 +903,16 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
     k.e0 = j * kCols + (k.wave - 4) * 16;
     const bool cols = k.e0 < a.dv;
     f4 S[K::kDt];
-    const int64_t head = static_cast<int64_t>(k.h) * a.dv * DK;
-    const int64_t slot_elems = static_cast<int64_t>(a.Hv) * a.dv * DK;
+    // rows of S^T in the slots: d_k = DKR floats per value index
+    const int64_t head = static_cast<int64_t>(k.h) * a.dv * DKR;
+    const int64_t slot_elems = static_cast<int64_t>(a.Hv) * a.dv * DKR;
+    constexpr int kDtR = DKR / 16;   // 16-row tiles that exist in the slots
 #pragma unroll
     for (int d = 0; d < K::kDt; ++d) {
       S[d] = f4{0.f, 0.f, 0.f, 0.f};
-      if (cols && k.init >= 0)
+      if (d < kDtR && cols && k.init >= 0)
         S[d] = *reinterpret_cast<const f4*>(a.ssm + k.init * slot_elems + head +
-                                           static_cast<int64_t>(k.e0 + k.lr) * DK + 16 * d +
+                                           static_cast<int64_t>(k.e0 + k.lr) * DKR + 16 * d +
                                            4 * k.lg);
     }
     s8 Sh[K::kSl], Sl[K::kSl];
@@ -908,22 +928,22 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
       const int32_t cs = __builtin_amdgcn_readfirstlane(ckpt_slot(a, s, (c + 1) * kT, k.T));
       if (cols && cs >= 0) {  // the state after (c + 1) * kT tokens, to a checkpoint slot
         const int l = k.lane_now();
-        float* o = a.ssm + cs * slot_elems + head + static_cast<int64_t>(k.e0 + (l & 15)) * DK;
+        float* o = a.ssm + cs * slot_elems + head + static_cast<int64_t>(k.e0 + (l & 15)) * DKR;
 #pragma unroll
-        for (int d = 0; d < K::kDt; ++d) *reinterpret_cast<f4*>(o + 16 * d + 4 * (l >> 4)) = S[d];
+        for (int d = 0; d < kDtR; ++d) *reinterpret_cast<f4*>(o + 16 * d + 4 * (l >> 4)) = S[d];
       }
       lds_barrier();          // chunk c consumed
     }
     if (cols) {
-      float* out = a.ssm + dst * slot_elems + head + static_cast<int64_t>(k.e0 + k.lr) * DK;
+      float* out = a.ssm + dst * slot_elems + head + static_cast<int64_t>(k.e0 + k.lr) * DKR;
 #pragma unroll
-      for (int d = 0; d < K::kDt; ++d) *reinterpret_cast<f4*>(out + 16 * d + 4 * k.lg) = S[d];
+      for (int d = 0; d < kDtR; ++d) *reinterpret_cast<f4*>(out + 16 * d + 4 * k.lg) = S[d];
     }
   }
 }
 
 
-template <int DK, typename Act>
+template <int DK, typename Act, int DKR>
 __global__ void __launch_bounds__(256) qk_prep_kernel(PrefillArgs a, int nchunk) {
   const int hk = blockIdx.x % a.Hk;
   const int first = (blockIdx.x / a.Hk) % nchunk;
@@ -933,7 +953,7 @@ __global__ void __launch_bounds__(256) qk_prep_kernel(PrefillArgs a, int nchunk)
   const int32_t init = a.init ? a.init[s] : dst;
   if (t0 < 0 || t1 < t0 || t1 > a.total || dst < 0 || dst >= a.num_slots || init >= a.num_slots)
     return;
-  QkPrep<DK, Act> q{{a, nullptr}};
+  QkPrep<DK, Act, DKR> q{{a, nullptr}};
   q.tid = threadIdx.x;
   q.wave = __builtin_amdgcn_readfirstlane(q.tid >> 6);
   q.lane = q.tid & 63;
@@ -949,7 +969,8 @@ __global__ void __launch_bounds__(256) qk_prep_kernel(PrefillArgs a, int nchunk)
   q.run(first, nchunk);
 }
 
-template <int DK, typename Act>
+// DKR: the layer's d_k; DK the layout it runs in (32 for d_k = 16).
+template <int DK, typename Act, int DKR = DK>
 hipError_t launch_one(const PrefillArgs& a, int max_seqlen, hipStream_t st) {
   // About 8 workgroups per CU: each covers every nchunk-th chunk of its
   // (sequence, key head), prefetching the next while computing one.
@@ -957,16 +978,16 @@ hipError_t launch_one(const PrefillArgs& a, int max_seqlen, hipStream_t st) {
   const int64_t want = 2048 / per > 0 ? 2048 / per : 1;
   const int64_t most = max_seqlen > 0 ? (max_seqlen + kT - 1) / kT : 1;
   const int64_t nchunk = want < most ? want : most;
-  hipLaunchKernelGGL((qk_prep_kernel<DK, Act>), dim3(static_cast<uint32_t>(nchunk * per)),
+  hipLaunchKernelGGL((qk_prep_kernel<DK, Act, DKR>), dim3(static_cast<uint32_t>(nchunk * per)),
                      dim3(256), 0, st, a, static_cast<int>(nchunk));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int bytes = Plan<DK>::kBytes;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<DK, Act>),
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<DK, Act, DKR>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
   const int grid = a.N * a.Hv * a.nblk;
-  hipLaunchKernelGGL((prefill_kernel<DK, Act>), dim3(grid), dim3(kThreads), bytes, st, a);
+  hipLaunchKernelGGL((prefill_kernel<DK, Act, DKR>), dim3(grid), dim3(kThreads), bytes, st, a);
   e = hipGetLastError();
   if (e != hipSuccess || a.W < 2) return e;
   hipLaunchKernelGGL((prefill_conv_tail<Act>), conv_tail_grid(a), dim3(256), 0, st, a);
@@ -980,17 +1001,21 @@ static_assert(kT == 32, "the tile code assumes two 16-token blocks per chunk");
 
 int prefill_supported(int dk, int kda) {
   (void)kda;
-  return dk == 32 || dk == 64 || dk == 128;
+  return dk == 16 || dk == 32 || dk == 64 || dk == 128;   // 16 in the 32 layout
 }
 
 size_t qk_workspace_bytes(int Hk, int dk, int64_t total) {
-  return static_cast<size_t>(total) * Hk * dk * 8;
+  const int dk_layout = dk < 32 ? 32 : dk;   // d_k = 16 runs the d_k = 32 layout
+  return static_cast<size_t>(total) * Hk * dk_layout * 8;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int dk, int act_bf16, int max_seqlen,
                           hipStream_t s) {
   if (a.N == 0) return hipSuccess;
   switch (dk) {
+    case 16:
+      return act_bf16 ? launch_one<32, bf16, 16>(a, max_seqlen, s)
+                      : launch_one<32, float, 16>(a, max_seqlen, s);
     case 32:
       return act_bf16 ? launch_one<32, bf16>(a, max_seqlen, s)
                       : launch_one<32, float>(a, max_seqlen, s);

@@ -89,7 +89,9 @@ struct DiagPlan {
   static constexpr int kBytes = oB + 2 * DK * 4;
 };
 
-template <int DK, typename Act>
+// DKR: the layer's d_k; DK the layout it runs in (32 for d_k = 16, whose
+// channels from DKR on are padding: zero q, k, taps and bias, decay 1).
+template <int DK, typename Act, int DKR>
 __global__ void __launch_bounds__(kDiagThreads, 4) kda_diag_kernel(PrefillArgs a) {
   using DP = DiagPlan<DK>;
   constexpr int kGrp = DK / 8;        // channel octets per head
@@ -129,7 +131,9 @@ __global__ void __launch_bounds__(kDiagThreads, 4) kda_diag_kernel(PrefillArgs a
   const int co = tid % (2 * kGrp);
   const bool isk = co >= kGrp;
   const int oc = isk ? co - kGrp : co;
-  const int ch = (isk ? a.Hk * DK : 0) + core.hk * DK + 8 * oc;
+  const int ch = (isk ? a.Hk * DKR : 0) + core.hk * DKR + 8 * oc;
+  constexpr bool kPad = DKR < DK;
+  const bool pad_item = kPad && 8 * oc >= DKR;   // an octet of padding: its rows read zero
   // decay stage: item = (token r, channel octet)
   // pair stage: lane = (column pair cp, channel group cg of 4 channels);
   // columns cp and 15 - cp take 17 (row, column) steps in all
@@ -138,10 +142,14 @@ __global__ void __launch_bounds__(kDiagThreads, 4) kda_diag_kernel(PrefillArgs a
   float* wl = reinterpret_cast<float*>(lds + DP::oW);
   float* bl = reinterpret_cast<float*>(lds + DP::oB);
   for (int i = tid; i < 2 * DK; i += kDiagThreads) {
-    const int c = i < DK ? core.hk * DK + i : a.Hk * DK + core.hk * DK + (i - DK);
+    const int ih = i < DK ? i : i - DK;
+    const int c = i < DK ? core.hk * DKR + i : a.Hk * DKR + core.hk * DKR + (i - DK);
     const int at = (i & 7) * (2 * kGrp) + (i >> 3);
-    *reinterpret_cast<f4*>(wl + 4 * at) = f4{core.tap(c, 0), core.tap(c, 1), core.tap(c, 2), core.tap(c, 3)};
-    bl[at] = a.bias ? to_f32(static_cast<const Act*>(a.bias)[c]) : 0.f;
+    const bool on = !kPad || ih < DKR;
+    *reinterpret_cast<f4*>(wl + 4 * at) =
+        on ? f4{core.tap(c, 0), core.tap(c, 1), core.tap(c, 2), core.tap(c, 3)}
+           : f4{0.f, 0.f, 0.f, 0.f};
+    bl[at] = (on && a.bias) ? to_f32(static_cast<const Act*>(a.bias)[c]) : 0.f;
   }
 
   lds_barrier();                // taps and bias in LDS
@@ -160,10 +168,12 @@ __global__ void __launch_bounds__(kDiagThreads, 4) kda_diag_kernel(PrefillArgs a
           Row8<Act> raw[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            raw[r].load(rx, core.x_off(tb, tb + tok - 3 + r, ch));
+            raw[r].load(rx, pad_item ? static_cast<int>(kOutOfRange)
+                                     : core.x_off(tb, tb + tok - 3 + r, ch));
             if (tb == 0) {
               Row8<Act> wr;
-              wr.load(rw, core.win_off(tok - 3 + r, ch));
+              wr.load(rw, pad_item ? static_cast<int>(kOutOfRange)
+                                   : core.win_off(tok - 3 + r, ch));
               raw[r].merge(wr);
             }
           }
@@ -190,18 +200,21 @@ __global__ void __launch_bounds__(kDiagThreads, 4) kda_diag_kernel(PrefillArgs a
     }
     // ---- decays (1 past the sequence) and b ----
     {
-      const int64_t rowe = static_cast<int64_t>(a.Hv) * DK;
+      const int64_t rowe = static_cast<int64_t>(a.Hv) * DKR;
       const rsrc_t ra = make_rsrc(static_cast<const Act*>(a.alpha) + (t0 + static_cast<int64_t>(tb)) * rowe,
                                   static_cast<uint32_t>(n * rowe * sizeof(Act)));
       if (tid < kBlk * (DK / 8)) {
         const int r = tid / (DK / 8), c = 8 * (tid % (DK / 8));
+        const bool real = !kPad || c < DKR;   // padding decays by 1
+        const bool on = r < n && real;
         Row8<Act> v;
-        v.load(ra, static_cast<int>(((r * a.Hv + h) * DK + c) * sizeof(Act)));
+        v.load(ra, real ? static_cast<int>(((r * a.Hv + h) * DKR + c) * sizeof(Act))
+                        : static_cast<int>(kOutOfRange));
         f4 lo4, hi4;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          lo4[m] = r < n ? v.get(m) : 1.f;
-          hi4[m] = r < n ? v.get(m + 4) : 1.f;
+          lo4[m] = on ? v.get(m) : 1.f;
+          hi4[m] = on ? v.get(m + 4) : 1.f;
         }
         *reinterpret_cast<f4*>(al + diag_at<DK>(r, c)) = lo4;
         *reinterpret_cast<f4*>(al + diag_at<DK>(r, c + 4)) = hi4;
@@ -308,9 +321,14 @@ struct KdaPlan {
   static constexpr int kBytes = oB + 2 * DK * 4;
 };
 
-template <int DK, typename Act>
+template <int DK, typename Act, int DKR>
 struct KdaChunk : PrefillCore<DK, Act> {
   GDN_PREFILL_CORE(DK, Act);
+  // DKR: the layer's d_k.  Below DK (d_k = 16 in the d_k = 32 layout) the
+  // upper half of every octet (channels 16 + 4j..) is padding: zero rows,
+  // taps and bias, decay 1, so KE, QE and KF are zero there and the rows
+  // DKR.. of S^T stay zero.
+  static constexpr bool kPad = DKR < DK;
   using P = KdaPlan<DK>;
   static constexpr int kSl = DK / 32;
   static constexpr int kDt = DK / 16;
@@ -349,7 +367,7 @@ struct KdaChunk : PrefillCore<DK, Act> {
     p.tau = tid / kNco;
     p.isk = p.co >= kGrp;
     p.oc = p.isk ? p.co - kGrp : p.co;
-    p.ch = (p.isk ? a.Hk * DK : 0) + hk * DK + oct_base(p.oc);
+    p.ch = (p.isk ? a.Hk * DKR : 0) + hk * DKR + oct_base(p.oc);
   }
 
   // Taps and bias of the key head's q and k channels, stored [m][octet] (m =
@@ -359,13 +377,37 @@ struct KdaChunk : PrefillCore<DK, Act> {
     float* wt = fp(P::oW);
     float* bs = fp(P::oB);
     for (int i = tid; i < 2 * DK; i += kThreads) {
-      const int ch = i < DK ? hk * DK + i : a.Hk * DK + hk * DK + (i - DK);
+      const int ih = i < DK ? i : i - DK;
+      const int ch = i < DK ? hk * DKR + i : a.Hk * DKR + hk * DKR + (i - DK);
       // channel r of a 32-block: octet 4 (block) + (r % 16) / 4, place
       // r % 4 (+ 4 in the block's upper half)
       const int r = i & 31, oc = 4 * (i >> 5) + ((r & 15) >> 2), m = (r & 3) + 4 * (r >> 4);
       const int at = m * kNco + oc;
-      *reinterpret_cast<f4*>(wt + 4 * at) = f4{tap(ch, 0), tap(ch, 1), tap(ch, 2), tap(ch, 3)};
-      bs[at] = a.bias ? to_f32(static_cast<const Act*>(a.bias)[ch]) : 0.f;
+      const bool on = !kPad || ih < DKR;
+      *reinterpret_cast<f4*>(wt + 4 * at) =
+          on ? f4{tap(ch, 0), tap(ch, 1), tap(ch, 2), tap(ch, 3)} : f4{0.f, 0.f, 0.f, 0.f};
+      bs[at] = (on && a.bias) ? to_f32(static_cast<const Act*>(a.bias)[ch]) : 0.f;
+    }
+  }
+
+  // Row8::load_split, except that with padding the octet's upper half is
+  // not read but set to fill (0 for inputs, the bits of 1.0 for decays).
+  __device__ __forceinline__ static void load_oct(Row8<Act>& r, rsrc_t rs, int off, uint32_t fill) {
+    if constexpr (!kPad) {
+      r.load_split(rs, off);
+    } else {
+      typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+      typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+      constexpr int kH = Row8<Act>::kWords / 2;
+      if constexpr (kH == 2) {
+        const u2 u = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+        r.w[0] = u[0], r.w[1] = u[1];
+      } else {
+        const u4 u = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        r.w[0] = u[0], r.w[1] = u[1], r.w[2] = u[2], r.w[3] = u[3];
+      }
+#pragma unroll
+      for (int i = kH; i < 2 * kH; ++i) r.w[i] = fill;
     }
   }
 
@@ -374,20 +416,22 @@ struct KdaChunk : PrefillCore<DK, Act> {
     if (p.on) {
       const rsrc_t rx = x_rows(c0);
 #pragma unroll
-      for (int r = 0; r < 11; ++r) p.raw[r].load_split(rx, x_off(c0, c0 + 8 * tau - 3 + r, ch));
+      for (int r = 0; r < 11; ++r) load_oct(p.raw[r], rx, x_off(c0, c0 + 8 * tau - 3 + r, ch), 0u);
       const int n = T - c0 < kC ? T - c0 : kC;
-      const int64_t rowe = static_cast<int64_t>(a.Hv) * DK;
+      const int64_t rowe = static_cast<int64_t>(a.Hv) * DKR;
       const rsrc_t ra = make_rsrc(static_cast<const Act*>(a.alpha) + (t0 + static_cast<int64_t>(c0)) * rowe,
                                   static_cast<uint32_t>(n * rowe * sizeof(Act)));
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt)
-        p.dec[tt].load_split(ra, static_cast<int>((((8 * tau + tt) * a.Hv + h) * DK + oct_base(oc)) * sizeof(Act)));
+        load_oct(p.dec[tt], ra,
+                 static_cast<int>((((8 * tau + tt) * a.Hv + h) * DKR + oct_base(oc)) * sizeof(Act)),
+                 sizeof(Act) == 2 ? 0x3F803F80u : 0x3F800000u);
       if (c0 == 0) {
         const rsrc_t rw = win_rows();
 #pragma unroll
         for (int r = 0; r < 3; ++r) {
           Row8<Act> wr;
-          wr.load_split(rw, win_off(8 * tau - 3 + r, ch));
+          load_oct(wr, rw, win_off(8 * tau - 3 + r, ch), 0u);
           p.raw[r].merge(wr);
         }
       }
@@ -667,7 +711,7 @@ struct KdaChunk : PrefillCore<DK, Act> {
   };
 
   __device__ void cons_init(Cons& c) const {
-    c.vch = 2 * a.Hk * DK + h * a.dv + e0 + lr;
+    c.vch = 2 * a.Hk * DKR + h * a.dv + e0 + lr;
     c.von = e0 + lr < a.dv;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) c.vw[jj] = c.von ? tap(c.vch, jj) : 0.f;
@@ -877,10 +921,10 @@ struct KdaChunk : PrefillCore<DK, Act> {
   }
 };
 
-template <int DK, typename Act>
+template <int DK, typename Act, int DKR>
 __global__ void __launch_bounds__(kThreads, 1) kda_chunk_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
-  using K = KdaChunk<DK, Act>;
+  using K = KdaChunk<DK, Act, DKR>;
   using P = KdaPlan<DK>;
   K k{{a, lds_raw}};
   k.tid = threadIdx.x;
@@ -955,14 +999,16 @@ __global__ void __launch_bounds__(kThreads, 1) kda_chunk_kernel(PrefillArgs a) {
     k.cons_init(cv);
     if (cols && nch > 0) k.cons_load(cv, 0);
     f4 S[K::kDt];
-    const int64_t head = static_cast<int64_t>(k.h) * a.dv * DK;
-    const int64_t slot_elems = static_cast<int64_t>(a.Hv) * a.dv * DK;
+    // rows of S^T in the slots: d_k = DKR floats per value index
+    const int64_t head = static_cast<int64_t>(k.h) * a.dv * DKR;
+    const int64_t slot_elems = static_cast<int64_t>(a.Hv) * a.dv * DKR;
+    constexpr int kDtR = DKR / 16;   // 16-row tiles that exist in the slots
 #pragma unroll
     for (int d = 0; d < K::kDt; ++d) {
       S[d] = f4{0.f, 0.f, 0.f, 0.f};
-      if (cols && k.init >= 0)
+      if (d < kDtR && cols && k.init >= 0)
         S[d] = *reinterpret_cast<const f4*>(a.ssm + k.init * slot_elems + head +
-                                           static_cast<int64_t>(k.e0 + k.lr) * DK + 16 * d +
+                                           static_cast<int64_t>(k.e0 + k.lr) * DKR + 16 * d +
                                            4 * k.lg);
     }
     lds_barrier();            // planes zeroed, taps loaded
@@ -977,9 +1023,9 @@ __global__ void __launch_bounds__(kThreads, 1) kda_chunk_kernel(PrefillArgs a) {
       const int32_t cs = __builtin_amdgcn_readfirstlane(ckpt_slot(a, s, (c + 1) * kC, k.T));
       if (cols && cs >= 0) {  // the state after (c + 1) * 64 tokens, to a checkpoint slot
         const int l = k.lane_now();
-        float* o = a.ssm + cs * slot_elems + head + static_cast<int64_t>(k.e0 + (l & 15)) * DK;
+        float* o = a.ssm + cs * slot_elems + head + static_cast<int64_t>(k.e0 + (l & 15)) * DKR;
 #pragma unroll
-        for (int d = 0; d < K::kDt; ++d) *reinterpret_cast<f4*>(o + 16 * d + 4 * (l >> 4)) = S[d];
+        for (int d = 0; d < kDtR; ++d) *reinterpret_cast<f4*>(o + 16 * d + 4 * (l >> 4)) = S[d];
       }
       lds_barrier();          // chunk c consumed
       if (next) {
@@ -989,27 +1035,27 @@ __global__ void __launch_bounds__(kThreads, 1) kda_chunk_kernel(PrefillArgs a) {
       }
     }
     if (cols) {
-      float* out = a.ssm + dst * slot_elems + head + static_cast<int64_t>(k.e0 + k.lr) * DK;
+      float* out = a.ssm + dst * slot_elems + head + static_cast<int64_t>(k.e0 + k.lr) * DKR;
 #pragma unroll
-      for (int d = 0; d < K::kDt; ++d) *reinterpret_cast<f4*>(out + 16 * d + 4 * k.lg) = S[d];
+      for (int d = 0; d < kDtR; ++d) *reinterpret_cast<f4*>(out + 16 * d + 4 * k.lg) = S[d];
     }
   }
 }
 
-template <int DK, typename Act>
+template <int DK, typename Act, int DKR = DK>
 hipError_t launch_kda(const PrefillArgs& a, int max_seqlen, hipStream_t st) {
   // diagonal blocks: grid x strides over the token blocks of a sequence
   const int64_t want = 4 * ((static_cast<int64_t>(max_seqlen) + kC - 1) / kC);
   const int gy = static_cast<int>(want < 1 ? 1 : (want > 65535 ? 65535 : want));
-  hipLaunchKernelGGL((kda_diag_kernel<DK, Act>), dim3(a.N * a.Hv, gy), dim3(kDiagThreads), 0,
+  hipLaunchKernelGGL((kda_diag_kernel<DK, Act, DKR>), dim3(a.N * a.Hv, gy), dim3(kDiagThreads), 0,
                      st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int bytes = KdaPlan<DK>::kBytes;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_chunk_kernel<DK, Act>),
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_chunk_kernel<DK, Act, DKR>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((kda_chunk_kernel<DK, Act>), dim3(a.N * a.Hv * a.nblk), dim3(kThreads),
+  hipLaunchKernelGGL((kda_chunk_kernel<DK, Act, DKR>), dim3(a.N * a.Hv * a.nblk), dim3(kThreads),
                      bytes, st, a);
   e = hipGetLastError();
   if (e != hipSuccess || a.W < 2) return e;
@@ -1030,6 +1076,7 @@ hipError_t launch_prefill_kda(const PrefillArgs& a, int dk, int act_bf16, int ma
                               hipStream_t s) {
   if (a.N == 0) return hipSuccess;
   switch (dk) {
+    case 16: return act_bf16 ? launch_kda<32, bf16, 16>(a, max_seqlen, s) : launch_kda<32, float, 16>(a, max_seqlen, s);
     case 32: return act_bf16 ? launch_kda<32, bf16>(a, max_seqlen, s) : launch_kda<32, float>(a, max_seqlen, s);
     case 64: return act_bf16 ? launch_kda<64, bf16>(a, max_seqlen, s) : launch_kda<64, float>(a, max_seqlen, s);
     case 128: return act_bf16 ? launch_kda<128, bf16>(a, max_seqlen, s) : launch_kda<128, float>(a, max_seqlen, s);

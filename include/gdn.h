@@ -215,7 +215,8 @@ typedef struct {
  *     value stays correct, only slower); total_tokens (host) == cu_seqlens[N].
  *   chunk: 64, the only value accepted: the granularity of checkpoints (the
  *     scalar-decay kernel steps through 32-token blocks internally; results
- *     do not depend on it beyond rounding).  d_k in {32, 64, 128}.
+ *     do not depend on it beyond rounding).  d_k in {16, 32, 64, 128}
+ *     (16 runs in the d_k = 32 layout, its upper channels zero padding).
  *   in->alpha: [total][H_v] (scalar decay) or [total][H_v][d_k] (per-channel
  *     decay, 16-byte aligned).
  *   out [total][H_v][d_v] fp32.

@@ -185,8 +185,10 @@ def test_bad_prefill_arguments():
     assert prefill(L, N=-1) == gdn.GDN_ERR_BAD_SHAPE
     assert prefill(L, max_len=-1) == gdn.GDN_ERR_BAD_SHAPE
     assert prefill(L, chunk=32) == gdn.GDN_ERR_UNSUPPORTED
-    assert prefill(qwen_layer(n_k_heads=2, n_v_heads=2, d_k=16, d_v=16)) == \
+    assert prefill(qwen_layer(n_k_heads=2, n_v_heads=2, d_k=48, d_v=16)) == \
         gdn.GDN_ERR_UNSUPPORTED
+    # d_k = 16 is taken (it runs in the d_k = 32 layout)
+    assert prefill(qwen_layer(n_k_heads=2, n_v_heads=2, d_k=16, d_v=16), N=0) == gdn.GDN_OK
     assert prefill(L, dst=None) == gdn.GDN_ERR_NULL_ARG
     assert prefill(L, cu=None) == gdn.GDN_ERR_NULL_ARG
     assert prefill(L, inp=GdnInputs(None, FAKE, FAKE, FAKE, None)) == gdn.GDN_ERR_NULL_ARG
@@ -211,6 +213,9 @@ def test_bad_prefill_arguments():
     assert prefill(L) == gdn.GDN_ERR_WORKSPACE
     assert prefill(L, ws=FAKE, ws_bytes=need - 1) == gdn.GDN_ERR_WORKSPACE
     assert prefill(L, ws=ct.c_void_p(0x10080), ws_bytes=need) == gdn.GDN_ERR_WORKSPACE
+    # d_k = 16 keeps its rows at the d_k = 32 layout's width
+    L16 = qwen_layer(n_k_heads=2, n_v_heads=2, d_k=16, d_v=16)
+    assert size(ct.byref(L16), 2, 64, 128, 64) == 128 * 2 * 32 * 8
 
 
 def test_per_channel_prefill_workspace():

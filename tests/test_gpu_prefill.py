@@ -185,16 +185,41 @@ def test_split_prefill_equals_one_shot_bitwise():
     np.testing.assert_array_equal(bits(conv)[one], bits(conv)[two])
 
 
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_dk16(gate, dtype):
+    """d_k = 16 (the tiny decode shape's heads), run in the d_k = 32 layout
+    with the upper channels as zero padding: ragged lengths around the
+    16-token block and chunk edges, zero and copy-on-write starts, against
+    the oracle; slots hold d_k = 16 rows, untouched slots stay bit-equal."""
+    shape = synth.Shape(2, 2, 16, 16, 4, gate, dtype)
+    r = run_case(shape, [1, 15, 17, 63, 64, 65, 130, 200], seed=31)
+    print("d_k=16 %s %s: out %.2e state %.2e" % ((gate, dtype) + check(r)))
+
+
+def test_dk16_gqa_with_conv_bias():
+    """d_k = 16 with two value heads per key head, d_v = 32 and a conv bias
+    (the padded channels must take no bias), bf16 inputs."""
+    torch = _torch()
+    shape = synth.Shape(2, 4, 16, 32, 4, "scalar", "bf16")
+    case = synth.prefill_case(shape, [70, 33, 128], 8, seed=32)
+    bias = synth.encode(np.random.default_rng(32).standard_normal(shape.channels) * 0.3, "bf16")
+    g, o = layers(shape)
+    ssm, conv = dev(case.pool.ssm), dev(case.pool.conv)
+    out = gdn.gdn_prefill_chunked(g, ssm, conv, dev(case.dst), dev(case.init_slot),
+                                  dev(case.cu_seqlens), 128, dev(case.x), dev(case.alpha),
+                                  dev(case.beta), dev(case.conv_w), conv_b=dev(bias))
+    torch.cuda.synchronize()
+    s64, c64 = shadow(case.pool)
+    ref = oracle.prefill(o, s64, c64, case.dst, case.init_slot, case.cu_seqlens, case.x,
+                         case.alpha, case.beta, case.conv_w, conv_b=bias)
+    assert rel_err(host(out), ref) <= OUT_TOL
+    assert rel_err(host(ssm)[case.dst], s64[case.dst]) <= STATE_TOL
+    np.testing.assert_array_equal(oracle.as_f64(host(conv)[case.dst]), c64[case.dst])
+
+
 def test_unsupported_shapes_raise():
     torch = _torch()
-    for shape, kw in [(synth.Shape(2, 2, 16, 16, 4, "scalar", "f32"), {}),
-                      (synth.Shape(2, 2, 16, 16, 4, "channel", "f32"), {})]:
-        case = synth.prefill_case(shape, [64], 4, seed=0)
-        g, _ = layers(shape, **kw)
-        with pytest.raises(gdn.GdnError):
-            gdn.gdn_prefill_chunked(g, dev(case.pool.ssm), dev(case.pool.conv), dev(case.dst),
-                                    dev(case.init_slot), dev(case.cu_seqlens), 64, dev(case.x),
-                                    dev(case.alpha), dev(case.beta), dev(case.conv_w))
     case = synth.prefill_case(SMALL, [64], 4, seed=0)
     g, _ = layers(SMALL)
     with pytest.raises(gdn.GdnError):

@@ -20,11 +20,13 @@ pytestmark = pytest.mark.gpu
 
 STATE_TOL = 2e-3
 
-SHAPES = [synth.Shape(2, 4, 64, 64, 4, "scalar", "bf16"),
+SHAPES = [synth.Shape(2, 4, 16, 16, 4, "scalar", "bf16"),
+          synth.Shape(2, 2, 16, 16, 4, "channel", "bf16"),
+          synth.Shape(2, 4, 64, 64, 4, "scalar", "bf16"),
           synth.Shape(2, 2, 64, 64, 4, "channel", "bf16"),
           synth.Shape(2, 4, 128, 128, 4, "scalar", "bf16"),
           synth.Shape(2, 2, 128, 128, 4, "channel", "bf16")]
-IDS = ["scalar_d64", "channel_d64", "scalar_d128", "channel_d128"]
+IDS = ["scalar_d16", "channel_d16", "scalar_d64", "channel_d64", "scalar_d128", "channel_d128"]
 
 
 def _torch():
