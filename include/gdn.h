@@ -146,7 +146,13 @@ typedef struct {
  * Decode T >= 1 tokens per request ("Scheduler dual": the state of the slot
  * named by mamba_pool_indices is updated in place every decode step; with a
  * spec cache, per-speculative-step Conv/SSM snapshots are kept for rollback).
- * One workgroup per (request, key head) unit.
+ * One workgroup per (request, key head) unit.  With G = H_v / H_k, the
+ * unit's G * d_v state rows go to w <= 8 waves of r rows each, r in {32, 16,
+ * 8} dividing d_v and a multiple of 4 (d_k >= 64) or of 256 / d_k, and the
+ * workgroup's 64 w threads must cover the 2 d_k + G d_v conv channels and the
+ * G (scalar decay) or G d_k (KDA) gate values plus G betas; a shape with no
+ * such r returns GDN_ERR_UNSUPPORTED before anything is enqueued (the
+ * Qwen3.5 and KDA shapes: r = 32 and 16, 8 waves).
  *   mamba_pool_indices [B] int32 (device); B >= 0; 1 <= T.
  *   init_slot [B] int32 (device) or NULL -- slot preparation fused into the
  *     step ("Riesgo de correctitud": a fresh working slot must start clean):
