@@ -100,6 +100,18 @@ def test_bad_decode_arguments():
     assert decode(L1, pool=GdnPool(FAKE, None, 8), B=0) == gdn.GDN_OK
 
 
+def test_decode_shapes_that_do_not_fit_one_workgroup():
+    """The decode needs a key head's value rows, conv channels and gates in one
+    workgroup of at most 8 waves (include/gdn.h); other shapes are refused
+    before anything is enqueued."""
+    # 4 value heads of 128 rows per key head: 512 rows > 8 waves x 32
+    assert decode(qwen_layer(n_k_heads=8, n_v_heads=32, d_v=128)) == gdn.GDN_ERR_UNSUPPORTED
+    # 16 rows but 2 x 128 + 16 conv channels: more than two waves' threads
+    assert decode(qwen_layer(n_k_heads=16, n_v_heads=16, d_v=16)) == gdn.GDN_ERR_UNSUPPORTED
+    # 4 value heads of 64 rows: 256 rows in 8 waves of 32 -- taken
+    assert decode(qwen_layer(n_k_heads=8, n_v_heads=32, d_v=64), B=0) == gdn.GDN_OK
+
+
 def test_bad_commit_index_arguments():
     pool = GdnPool(FAKE, FAKE, 8)
     lib = gdn.lib()
