@@ -52,15 +52,22 @@ __device__ __forceinline__ int64_t ws_block(int s, int t0, int jb) {
 }
 
 // =====================================================================
-// Kernel 1: the diagonal 16 x 16 blocks, one workgroup of four waves per
-// (sequence, value head, token block); past 65535 blocks in a sequence,
-// workgroup y takes blocks y, y + 65535, ...  Workspace record (2 KiB): lane
+// Kernel 1: the diagonal 16 x 16 blocks, workgroups of four waves per
+// (sequence, value head); workgroup y of gridDim.y takes the token blocks y,
+// y + gridDim.y, ... of its sequence in turn.  Workspace record (2 KiB): lane
 // l = 4 r + q holds columns 4q..4q+3 of row r as X hi, X lo, P hi, P lo (4
 // bf16 each), where X = (I + N)^{-1}, N_ri = b_r sum_c k_rc k_ic
 // prod_{i < s <= r} a_sc (i < r), and P_ri = sum_c q_rc k_ic
 // prod_{i < s <= r} a_sc (i <= r).
 // =====================================================================
 constexpr int kDiagThreads = 256;
+// Token blocks per workgroup: the workgroup's set-up (taps and bias into
+// LDS, the pair stage's addresses) is paid once for all of them.  4 x 8192
+// tokens of a KDA layer, whole call: 1, 2, 4, 8 blocks per workgroup took
+// 2.13-2.14, 2.06-2.08, 2.07-2.08, 2.03 ms on one MI355X; 8, 16, 32 took
+// 2.07, 2.08-2.10, 2.09 ms on another.
+constexpr int kDiagPer = 8;
+constexpr int kDiagMinGroups = 2048;   // ... unless that leaves fewer workgroups
 
 // Rows of q, k and the decays in LDS: DK floats, the 16-byte chunk index of
 // odd rows XOR 8 (d_k >= 64), so two consecutive rows read at the same
@@ -1044,9 +1051,15 @@ __global__ void __launch_bounds__(kThreads, 1) kda_chunk_kernel(PrefillArgs a) {
 
 template <int DK, typename Act, int DKR = DK>
 hipError_t launch_kda(const PrefillArgs& a, int max_seqlen, hipStream_t st) {
-  // diagonal blocks: grid x strides over the token blocks of a sequence
+  // diagonal blocks: grid y strides over the token blocks of a sequence,
+  // kDiagPer of them per workgroup while that leaves kDiagMinGroups
+  // workgroups, fewer (down to one) when it would not
   const int64_t want = 4 * ((static_cast<int64_t>(max_seqlen) + kC - 1) / kC);
-  const int gy = static_cast<int>(want < 1 ? 1 : (want > 65535 ? 65535 : want));
+  const int64_t heads = static_cast<int64_t>(a.N) * a.Hv;
+  int64_t g = (want + kDiagPer - 1) / kDiagPer;
+  const int64_t enough = (kDiagMinGroups + heads - 1) / heads;
+  if (g < enough) g = enough < want ? enough : want;
+  const int gy = static_cast<int>(g < 1 ? 1 : (g > 65535 ? 65535 : g));
   hipLaunchKernelGGL((kda_diag_kernel<DK, Act, DKR>), dim3(a.N * a.Hv, gy), dim3(kDiagThreads), 0,
                      st, a);
   hipError_t e = hipGetLastError();
