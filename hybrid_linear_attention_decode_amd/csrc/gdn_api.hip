@@ -26,6 +26,10 @@ int64_t channels(const gdn_layer* L) {
 
 size_t act_size(const gdn_layer* L) { return L->act_dtype == GDN_BF16 ? 2 : 4; }
 
+// Largest number of elements of one token's row: conv channels C, H_v d_v
+// outputs, H_v d_k per-channel decays.
+constexpr int64_t kMaxRowElems = int64_t{1} << 22;
+
 gdn_status check_layer(const gdn_layer* L) {
   if (!L) return GDN_ERR_NULL_ARG;
   if (L->gate != GDN_GATE_SCALAR && L->gate != GDN_GATE_CHANNEL) return GDN_ERR_BAD_DTYPE;
@@ -39,6 +43,10 @@ gdn_status check_layer(const gdn_layer* L) {
   if (L->d_k != 16 && L->d_k != 32 && L->d_k != 64 && L->d_k != 128) return GDN_ERR_UNSUPPORTED;
   if (L->d_v % 16 || L->d_v > 256) return GDN_ERR_UNSUPPORTED;
   if (L->conv_width > 4) return GDN_ERR_UNSUPPORTED;
+  // the kernels address a token's channels, and a chunk's rows of them, with
+  // 32-bit offsets
+  if (channels(L) > kMaxRowElems || static_cast<int64_t>(L->n_v_heads) * L->d_k > kMaxRowElems)
+    return GDN_ERR_BAD_SHAPE;
   return GDN_OK;
 }
 
@@ -207,6 +215,10 @@ gdn_status gdn_decode_step(const gdn_layer* L, const gdn_pool* P, const int32_t*
     return GDN_ERR_UNSUPPORTED;
   if (reinterpret_cast<uintptr_t>(work) & 3u) return GDN_ERR_BAD_SHAPE;
   if (static_cast<int64_t>(B) * L->n_k_heads > INT32_MAX) return GDN_ERR_BAD_SHAPE;
+  // a request's T rows of x, out and the decays are addressed with 32-bit offsets
+  const int64_t row = std::max({channels(L), static_cast<int64_t>(L->n_v_heads) * L->d_v,
+                                static_cast<int64_t>(L->n_v_heads) * L->d_k});
+  if (static_cast<int64_t>(T) * row > INT32_MAX) return GDN_ERR_BAD_SHAPE;
   if (B == 0) return GDN_OK;
   if (debug_checks()) {
     const hipStream_t hs = static_cast<hipStream_t>(stream);

@@ -100,7 +100,8 @@ enum {
   GDN_F_L2NORM_QK = 1u << 1  /* L2-normalise q and k per head */
 };
 
-/* (host) layer description */
+/* (host) layer description.  The conv channels C = 2 H_k d_k + H_v d_v and
+ * H_v d_k are at most 2^22 (else GDN_ERR_BAD_SHAPE from every entry point). */
 typedef struct {
   int32_t n_k_heads, n_v_heads; /* H_v % H_k == 0 */
   int32_t d_k, d_v;             /* d_k in {16, 32, 64, 128}; d_v a multiple of 16, <= 256 */
@@ -153,7 +154,8 @@ typedef struct {
  * G (scalar decay) or G d_k (KDA) gate values plus G betas; a shape with no
  * such r returns GDN_ERR_UNSUPPORTED before anything is enqueued (the
  * Qwen3.5 and KDA shapes: r = 32 and 16, 8 waves).
- *   mamba_pool_indices [B] int32 (device); B >= 0; 1 <= T.
+ *   mamba_pool_indices [B] int32 (device); B >= 0; 1 <= T, with T C, T H_v d_v
+ *     and T H_v d_k at most 2^31 - 1 (else GDN_ERR_BAD_SHAPE).
  *   init_slot [B] int32 (device) or NULL -- slot preparation fused into the
  *     step ("Riesgo de correctitud": a fresh working slot must start clean):
  *     NULL or init_slot[b] == mamba_pool_indices[b]: start from the slot

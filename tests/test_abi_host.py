@@ -112,6 +112,28 @@ def test_decode_shapes_that_do_not_fit_one_workgroup():
     assert decode(qwen_layer(n_k_heads=8, n_v_heads=32, d_v=64), B=0) == gdn.GDN_OK
 
 
+def test_sizes_past_32_bit_offsets_are_refused():
+    """Conv channels C and H_v d_k are at most 2^22 for every entry point, and a
+    decode's T C, T H_v d_v and T H_v d_k at most 2^31 - 1 (include/gdn.h): the
+    kernels address a token's row, and a request's or a chunk's rows, with
+    32-bit offsets."""
+    # 16 key heads of d_k = 128 and 16384 value heads of d_v = 256: C > 2^22
+    big = qwen_layer(n_k_heads=16, n_v_heads=16384, d_v=256)
+    assert decode(big, B=0) == gdn.GDN_ERR_BAD_SHAPE
+    assert gdn.lib().gdn_slot_bytes(ct.byref(big)) == 0
+    # C = 2^22 exactly is taken
+    edge = qwen_layer(n_k_heads=8192, n_v_heads=8192, d_k=128, d_v=256)
+    assert 2 * 8192 * 128 + 8192 * 256 == 1 << 22
+    assert gdn.lib().gdn_slot_bytes(ct.byref(edge)) > 0
+    # H_v d_k = 2^23 with C about 2^20: the per-channel decays of one token
+    kda = qwen_layer(gate="channel", n_k_heads=1, n_v_heads=65536, d_k=128, d_v=16)
+    assert gdn.lib().gdn_slot_bytes(ct.byref(kda)) == 0
+    # Qwen3.5 shape, C = 8192: T up to (2^31 - 1) / 8192 tokens per request
+    L = qwen_layer()
+    assert decode(L, B=0, T=(2**31 - 1) // 8192) == gdn.GDN_OK
+    assert decode(L, B=0, T=(2**31 - 1) // 8192 + 1) == gdn.GDN_ERR_BAD_SHAPE
+
+
 def test_bad_commit_index_arguments():
     pool = GdnPool(FAKE, FAKE, 8)
     lib = gdn.lib()
