@@ -32,6 +32,10 @@
 //     blocks of (I + A): for N strictly lower triangular, (I + N)^{-1} =
 //     (I - N)(I + N^2)(I + N^4)(I + N^8), and K K^T is symmetric, so both
 //     operand layouts of N come from the one accumulator tile.
+// Each kernel also writes the destination's and the checkpoints' conv
+// windows of the channels it reads (q, k in the first, the value columns in
+// the second): a destination window by the threads that alone read the
+// initial window, after those reads (see load_window_out, vwin_load).
 // Every product runs on v_mfma_f32_16x16x{32,16}_bf16 with each fp32
 // operand split as x ~= hi + lo (two bf16), and a*b ~= ah*bh + ah*bl + al*bh
 // accumulated in fp32: about 16 significant bits per operand, which keeps
@@ -121,6 +125,8 @@ struct QkPrep : PrefillCore<DK, Act> {
   // channels from DKR on are padding: read as zero with zero taps and bias,
   // so their prepared rows are zero and add nothing to any product.
   static constexpr bool kPad = DKR < DK;
+  int s;          // sequence (checkpoint table row)
+  int32_t dst;    // destination slot
   static constexpr int kNco = DK / 4;   // channel groups of q and k
   static constexpr int kGrp = DK / 8;   // groups per head (lanes of one norm)
   static constexpr int kRaw = kTpt + 3; // raw rows per thread
@@ -166,6 +172,36 @@ struct QkPrep : PrefillCore<DK, Act> {
         raw[r].merge(wr);
       }
     }
+  }
+
+  // The group's 8 channels of raw row r to a conv-state row (channel c's
+  // element at p): the two 4-channel halves, the second not in the padding.
+  __device__ __forceinline__ static void put_row(Act* p, const Row8<Act>& r) {
+    if constexpr (kE == 2) {
+      *reinterpret_cast<uint2*>(p) = uint2{r.w[0], r.w[1]};
+      if constexpr (!kPad) *reinterpret_cast<uint2*>(p + 16) = uint2{r.w[2], r.w[3]};
+    } else {
+      *reinterpret_cast<uint4*>(p) = uint4{r.w[0], r.w[1], r.w[2], r.w[3]};
+      if constexpr (!kPad) *reinterpret_cast<uint4*>(p + 16) = uint4{r.w[4], r.w[5], r.w[6], r.w[7]};
+    }
+  }
+  // Row jj of the destination window of the group (first channel c): input
+  // T - (W-1) + jj of the sequence, or of the initial window before it.
+  __device__ __forceinline__ void load_window_out(Row8<Act> (&nw)[3], int c) const {
+    const int W1 = a.W - 1;
+#pragma unroll
+    for (int jj = 0; jj < 3; ++jj) {
+      if (jj < W1) {
+        const int rho = T - W1 + jj;   // uniform
+        if (rho >= 0)
+          load_row(nw[jj], seq_row(rho), c * kE);
+        else
+          load_row(nw[jj], win_rows(), win_off(rho, c));
+      }
+    }
+  }
+  __device__ __forceinline__ Act* conv_row(int32_t slot, int jj, int c) const {
+    return static_cast<Act*>(a.conv) + (static_cast<int64_t>(slot) * (a.W - 1) + jj) * a.C + c;
   }
 
   // Taps (4, left-padded) and bias of the group's channels (first at c): for
@@ -230,7 +266,20 @@ struct QkPrep : PrefillCore<DK, Act> {
     const bool isk = co >= kGrp;
     const int oc = isk ? co - kGrp : co;
     const int c = (isk ? a.Hk * DKR : 0) + hk * DKR + chan(oc, 0);
-    if (first * kT >= T) return;
+    // The destination window of the group's channels is written by the
+    // threads that alone read the initial window (token group 0 of the
+    // workgroup that takes chunk 0), once their reads of it are done.
+    const int W1 = a.W - 1;
+    const bool win = W1 > 0 && first == 0 && tau == 0;
+    Row8<Act> nw[3];
+    if (win) load_window_out(nw, c);
+    if (first * kT >= T) {   // an empty sequence: its window only
+      if (win)
+#pragma unroll
+        for (int jj = 0; jj < 3; ++jj)
+          if (jj < W1) put_row(conv_row(dst, jj, c), nw[jj]);
+      return;
+    }
     f4 wt[8];
     float bias[8];
     taps8(c, wt, bias);
@@ -267,6 +316,28 @@ struct QkPrep : PrefillCore<DK, Act> {
           *reinterpret_cast<s8*>(hi + DK) = cat(l0, l1);
         }
       }
+      if (win && cc == 0) {     // the initial window's rows in raw have been used
+#pragma unroll
+        for (int jj = 0; jj < 3; ++jj)
+          if (jj < W1) put_row(conv_row(dst, jj, c), nw[jj]);
+      }
+      // A checkpoint after this chunk: its window is the chunk's last W-1
+      // rows, the last raw rows of the last token group.
+      if (a.ckpt && W1 > 0 && tau == kT / kTpt - 1 && (c0 + kT) % a.ckpt_every == 0) {
+        const int32_t cs = ckpt_slot(a, s, c0 + kT, T);
+        if (cs >= 0) {
+          if (W1 == 3) {
+            put_row(conv_row(cs, 0, c), raw[kRaw - 3]);
+            put_row(conv_row(cs, 1, c), raw[kRaw - 2]);
+            put_row(conv_row(cs, 2, c), raw[kRaw - 1]);
+          } else if (W1 == 2) {
+            put_row(conv_row(cs, 0, c), raw[kRaw - 2]);
+            put_row(conv_row(cs, 1, c), raw[kRaw - 1]);
+          } else {
+            put_row(conv_row(cs, 0, c), raw[kRaw - 1]);
+          }
+        }
+      }
       if (more) {
 #pragma unroll
         for (int r = 0; r < kRaw; ++r) raw[r] = nxt[r];
@@ -282,6 +353,8 @@ struct Prefill : PrefillCore<DK, Act> {
   // the padded K, Q channels are zero, so rows DKR.. of S^T stay zero and
   // are neither read nor written).
   using P = Plan<DK>;
+  int s;          // sequence (checkpoint table row)
+  int32_t dst;    // destination slot
   static constexpr int kSl = DK / 32;   // 32-wide slices of d_k
   static constexpr int kDt = DK / 16;   // 16-row tiles of d_k
   static constexpr int kNco = DK / 4;   // channel octets of q and k
@@ -312,6 +385,7 @@ struct Prefill : PrefillCore<DK, Act> {
     // 2 vp + 1 of the column block, tokens 8 vt..+7
     uint32_t vraw[kVRaw][sizeof(Act) == 2 ? 1 : 2];
     f4 vo[2][2];                // [channel][token half], not yet stored
+    uint32_t vwin[3][sizeof(Act) == 2 ? 1 : 2];   // destination window rows (vt == 0)
     int vp, vt, vch;
     bool von;
   };
@@ -347,6 +421,44 @@ struct Prefill : PrefillCore<DK, Act> {
 
   __device__ __forceinline__ static s4 ld8(rsrc_t r, int off) {
     return __builtin_bit_cast(s4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  }
+
+  // Window rows of the thread's two value channels: row jj of the window
+  // ending before token `end`.  The destination's are loaded at the start by
+  // token group 0 (the only threads that read the initial window) -- input
+  // T - (W-1) + jj of the sequence, or of the initial window before it --
+  // and stored once those threads' chunk-0 reads are done.
+  static constexpr int kVw = sizeof(Act) == 2 ? 1 : 2;   // words per row of two channels
+  __device__ __forceinline__ void vwin_load(Prod& p) const {
+    const int W1 = a.W - 1, vch = opaque(p.vch);
+#pragma unroll
+    for (int jj = 0; jj < 3; ++jj) {
+      if (jj < W1) {
+        const int rho = T - W1 + jj;   // uniform
+        const rsrc_t r = rho >= 0 ? seq_row(rho) : win_rows();
+        const int off = rho >= 0 ? vch * static_cast<int>(sizeof(Act)) : win_off(rho, vch);
+        if constexpr (kVw == 1) {
+          p.vwin[jj][0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+        } else {
+          typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+          const u2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+          p.vwin[jj][0] = v[0];
+          p.vwin[jj][1] = v[1];
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ void vrow_put(int32_t slot, int jj, int vch, const uint32_t* w) const {
+    Act* d = static_cast<Act*>(a.conv) + (static_cast<int64_t>(slot) * (a.W - 1) + jj) * a.C + vch;
+    if constexpr (kVw == 1)
+      *reinterpret_cast<uint32_t*>(d) = w[0];
+    else
+      *reinterpret_cast<uint2*>(d) = uint2{w[0], w[1]};
+  }
+  __device__ __forceinline__ void vwin_store(const Prod& p) const {
+#pragma unroll
+    for (int jj = 0; jj < 3; ++jj)
+      if (jj < a.W - 1) vrow_put(dst, jj, p.vch, p.vwin[jj]);
   }
 
   // Prepared q / k pieces of chunk c0 and the raw value inputs.
@@ -419,6 +531,24 @@ struct Prefill : PrefillCore<DK, Act> {
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) y = fmaf(vw[jj], xr[tt + jj][m], y);
           p.vo[m][tt / 4][tt % 4] = c0 + kVt * p.vt + tt < T ? act(y) : 0.f;
+        }
+      }
+      // A checkpoint after this chunk: its window is the chunk's last W-1
+      // rows, the last raw rows of the last token group.
+      const int W1 = a.W - 1;
+      if (a.ckpt && W1 > 0 && p.vt == kT / kVt - 1 && (c0 + kT) % a.ckpt_every == 0) {
+        const int32_t cs = ckpt_slot(a, s, c0 + kT, T);
+        if (cs >= 0) {
+          if (W1 == 3) {
+            vrow_put(cs, 0, p.vch, p.vraw[kVRaw - 3]);
+            vrow_put(cs, 1, p.vch, p.vraw[kVRaw - 2]);
+            vrow_put(cs, 2, p.vch, p.vraw[kVRaw - 1]);
+          } else if (W1 == 2) {
+            vrow_put(cs, 0, p.vch, p.vraw[kVRaw - 2]);
+            vrow_put(cs, 1, p.vch, p.vraw[kVRaw - 1]);
+          } else {
+            vrow_put(cs, 0, p.vch, p.vraw[kVRaw - 1]);
+          }
         }
       }
     }
@@ -852,6 +982,8 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
     return;
   k.t0 = t0;
   k.T = t1 - t0;
+  k.s = s;
+  k.dst = dst;
   const int nch = (k.T + kT - 1) / kT;
 
   // P and A planes of both buffers: the tiles above the diagonal stay zero.
@@ -868,7 +1000,11 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
     // ---------------- producers ----------------
     typename K::Prod p;
     k.prod_init(p);
+    // the destination window of the value channels (see vwin_load)
+    const bool vwin = a.W > 1 && p.von && p.vt == 0;
+    if (vwin) k.vwin_load(p);
     if (nch > 0) k.prod_load(p, 0);
+    if (vwin && nch == 0) k.vwin_store(p);
     lds_barrier();            // planes zeroed, taps loaded
     typename K::GateIn gin{0u, 0u, 0};
     if (k.wave == kGateWave) {
@@ -879,6 +1015,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
     // stored from: each chunk's store comes before the next chunk's load)
     for (int c = 0; c < 2 && c < nch; ++c) {
       k.prod_prep(p, c * kT);
+      if (vwin && c == 0) k.vwin_store(p);   // chunk 0's reads of the initial window are used
       k.prod_store(p, c);
       if (c + 1 < nch) k.prod_load(p, (c + 1) * kT);
     }
@@ -954,6 +1091,8 @@ __global__ void __launch_bounds__(256) qk_prep_kernel(PrefillArgs a, int nchunk)
   if (t0 < 0 || t1 < t0 || t1 > a.total || dst < 0 || dst >= a.num_slots || init >= a.num_slots)
     return;
   QkPrep<DK, Act, DKR> q{{a, nullptr}};
+  q.s = s;
+  q.dst = dst;
   q.tid = threadIdx.x;
   q.wave = __builtin_amdgcn_readfirstlane(q.tid >> 6);
   q.lane = q.tid & 63;
@@ -988,9 +1127,6 @@ hipError_t launch_one(const PrefillArgs& a, int max_seqlen, hipStream_t st) {
   if (e != hipSuccess) return e;
   const int grid = a.N * a.Hv * a.nblk;
   hipLaunchKernelGGL((prefill_kernel<DK, Act, DKR>), dim3(grid), dim3(kThreads), bytes, st, a);
-  e = hipGetLastError();
-  if (e != hipSuccess || a.W < 2) return e;
-  hipLaunchKernelGGL((prefill_conv_tail<Act>), conv_tail_grid(a), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

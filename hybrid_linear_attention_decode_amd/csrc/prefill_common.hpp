@@ -241,6 +241,12 @@ struct PrefillCore {
                         : a.x,
                      on ? static_cast<uint32_t>(W1 * a.C * sizeof(Act)) : 0u);
   }
+  // Row rho (0 <= rho < T, uniform) of the sequence alone: channel ch at
+  // byte offset ch * sizeof(Act).
+  __device__ __forceinline__ rsrc_t seq_row(int rho) const {
+    return make_rsrc(static_cast<const Act*>(a.x) + (static_cast<int64_t>(t0) + rho) * a.C,
+                     static_cast<uint32_t>(a.C * sizeof(Act)));
+  }
   // Byte offsets of row rho at channel ch in the two descriptors.
   __device__ __forceinline__ int x_off(int c0, int rho, int ch) const {
     return (rho - chunk_base(c0)) * a.C * static_cast<int>(sizeof(Act)) +
@@ -268,6 +274,7 @@ struct PrefillCore {
   using Core::t0; using Core::T; using Core::init; using Core::sp; using Core::fp;        \
   using Core::opaque; using Core::lane_now; using Core::chunk_base; using Core::x_rows;  \
   using Core::win_rows; using Core::x_off; using Core::win_off; using Core::tap;          \
+  using Core::seq_row;                                                                   \
   using Core::act
 
 // Pool slot of checkpoint k = tok / every - 1 of sequence s, taken after its
@@ -282,11 +289,13 @@ __device__ __forceinline__ int32_t ckpt_slot(const PrefillArgs& a, int s, int to
   return (sl < 0 || sl >= a.num_slots) ? -1 : sl;
 }
 
-// Conv windows written after the main kernel.  z = 0: the destination's,
-// the last W-1 inputs of the sequence (taken from the initial window when
-// the sequence is shorter; the main kernel has read an in-place sequence's
-// old window by now, and each thread reads its channel's rows before writing
-// any).  z = k + 1: checkpoint k's, the W-1 inputs before its token.
+// Conv windows written after the main kernel (the per-channel-decay
+// prefill's; the scalar-decay kernels write theirs themselves).  z = 0: the
+// destination's, the last W-1 inputs of the sequence (taken from the initial
+// window when the sequence is shorter; the main kernel has read an in-place
+// sequence's old window by now, and each thread reads its channel's rows
+// before writing any).  z = k + 1: checkpoint k's, the W-1 inputs before its
+// token.
 template <typename Act>
 __global__ void __launch_bounds__(256) prefill_conv_tail(PrefillArgs a) {
   const int s = blockIdx.y;
