@@ -150,6 +150,43 @@ def test_empty_skipped_and_in_place():
     np.testing.assert_array_equal(bits(conv)[untouched], before[1][untouched])
 
 
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("width,dtype", [(4, "bf16"), (3, "bf16"), (4, "f32")])
+def test_short_sequences_continue_their_own_slot(gate, width, dtype):
+    """Every sequence continues its own live slot (init == dst), with lengths
+    0 .. W-1 among them: the new conv window then takes rows of the old one
+    from the slot it overwrites.  Windows bit-exact against the oracle,
+    outputs and states to the usual bar, other slots untouched."""
+    torch = _torch()
+    shape = synth.Shape(2, 4, 32, 32, width, gate, dtype)
+    lens = [0, 1, 2, 3, 5, 40, 70]
+    case = synth.prefill_case(shape, lens, 16, seed=31)
+    g, o = layers(shape)
+    dst = case.dst.copy()
+    for s in range(len(lens)):                # each destination holds a live state
+        src = case.init_slot[s] if case.init_slot[s] >= 0 else case.init_slot[1]
+        case.pool.ssm[dst[s]] = case.pool.ssm[src]
+        case.pool.conv[dst[s]] = case.pool.conv[src]
+    init = dst.copy()
+    ssm, conv = dev(case.pool.ssm), dev(case.pool.conv)
+    before = bits(ssm), bits(conv)
+    total = int(case.cu_seqlens[-1])
+    out = gdn.gdn_prefill_chunked(g, ssm, conv, dev(dst), dev(init), dev(case.cu_seqlens),
+                                  max(lens), dev(case.x), dev(case.alpha), dev(case.beta),
+                                  dev(case.conv_w))
+    torch.cuda.synchronize()
+    s64, c64 = shadow(case.pool)
+    ref = oracle.prefill(o, s64, c64, dst, init, case.cu_seqlens, case.x, case.alpha,
+                         case.beta, case.conv_w)
+    assert rel_err(host(out), ref) <= OUT_TOL
+    assert rel_err(host(ssm)[dst], s64[dst]) <= STATE_TOL
+    np.testing.assert_array_equal(oracle.as_f64(host(conv)[dst]), c64[dst])
+    untouched = np.setdiff1d(np.arange(16), dst)
+    np.testing.assert_array_equal(bits(ssm)[untouched], before[0][untouched])
+    np.testing.assert_array_equal(bits(conv)[untouched], before[1][untouched])
+    print(f"{gate} W={width} {dtype}: {total} tokens, windows bit-exact")
+
+
 def test_qwen35_4x8192_zero_and_cow():
     """The full workload: 4 x 8192 tokens, 16/32 heads, d = 128, chunk 64,
     bf16 inputs; sequences alternate zero start and copy-on-write from a
