@@ -25,8 +25,13 @@ SHAPES = [synth.Shape(2, 4, 16, 16, 4, "scalar", "bf16"),
           synth.Shape(2, 4, 64, 64, 4, "scalar", "bf16"),
           synth.Shape(2, 2, 64, 64, 4, "channel", "bf16"),
           synth.Shape(2, 4, 128, 128, 4, "scalar", "bf16"),
-          synth.Shape(2, 2, 128, 128, 4, "channel", "bf16")]
-IDS = ["scalar_d16", "channel_d16", "scalar_d64", "channel_d64", "scalar_d128", "channel_d128"]
+          synth.Shape(2, 2, 128, 128, 4, "channel", "bf16"),
+          # narrower convs: windows of 2 and 1 rows
+          synth.Shape(2, 4, 64, 64, 3, "scalar", "f32"),
+          synth.Shape(2, 4, 32, 32, 2, "scalar", "bf16"),
+          synth.Shape(2, 2, 32, 32, 3, "channel", "bf16")]
+IDS = ["scalar_d16", "channel_d16", "scalar_d64", "channel_d64", "scalar_d128", "channel_d128",
+       "scalar_d64_w3_f32", "scalar_d32_w2", "channel_d32_w3"]
 
 
 def _torch():
