@@ -174,6 +174,45 @@ def test_spec_draft_commit_equals_recomputation(shape, B):
     np.testing.assert_array_equal(got_c, want_c)
 
 
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("T", [9, 16, 20])
+def test_calls_longer_than_one_lds_chunk(gate, T):
+    """Calls of more than 8 tokens: the kernel holds the activations of 8
+    tokens in LDS at a time and walks the call's tokens in chunks of 8.  In
+    place: outputs, states and windows against the oracle.  With snapshots:
+    outputs bit for bit equal to the in-place call, the last snapshot equal to
+    the in-place state and window, every snapshot against the oracle."""
+    torch = _torch()
+    shape = synth.Shape(2, 4, 64, 64, 4, gate, "bf16")   # two value heads per key head
+    B = 6
+    case = synth.decode_case(shape, B=B, T=T, num_slots=16, n_calls=1, seed=40 + T)
+    g, o = layers(shape)
+    a, b = DevCase(case), DevCase(case)
+    out = a.call(g, 0)
+    sp_ssm = torch.full((B, T) + tuple(b.ssm.shape[1:]), float("nan"), device="cuda")
+    sp_conv = torch.zeros((B, T) + tuple(b.conv.shape[1:]), dtype=b.conv.dtype, device="cuda")
+    out_s = b.call(g, 0, spec=(sp_ssm, sp_conv))
+    torch.cuda.synchronize()
+    idx = case.indices[0]
+    s64, c64 = shadow(case.pool)
+    ref = oracle.decode(o, s64, c64, idx, case.x[0], case.alpha[0], case.beta[0], case.conv_w)
+    assert rel_err(host(out), ref) <= OUT_TOL
+    assert rel_err(host(a.ssm)[idx], s64[idx]) <= STATE_TOL_16
+    np.testing.assert_array_equal(host(a.conv)[idx],
+                                  synth.encode(c64[idx].astype(np.float32), shape.dtype))
+    np.testing.assert_array_equal(bits(out_s), bits(out))
+    np.testing.assert_array_equal(bits(sp_ssm)[:, T - 1], bits(a.ssm)[idx])
+    np.testing.assert_array_equal(bits(sp_conv)[:, T - 1], bits(a.conv)[idx])
+    s64, c64 = shadow(case.pool)
+    sp64 = np.zeros((B, T) + s64.shape[1:])
+    spc64 = np.zeros((B, T) + c64.shape[1:])
+    oracle.decode(o, s64, c64, idx, case.x[0], case.alpha[0], case.beta[0], case.conv_w,
+                  spec_ssm=sp64, spec_conv=spc64)
+    assert rel_err(host(sp_ssm), sp64) <= OUT_TOL
+    np.testing.assert_array_equal(host(sp_conv),
+                                  synth.encode(spc64.astype(np.float32), shape.dtype))
+
+
 def test_slot_zero_copy_bitwise_and_isolated():
     torch = _torch()
     shape = synth.QWEN35
