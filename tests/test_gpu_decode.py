@@ -213,6 +213,28 @@ def test_calls_longer_than_one_lds_chunk(gate, T):
                                   synth.encode(spc64.astype(np.float32), shape.dtype))
 
 
+@pytest.mark.parametrize("shape", [synth.QWEN35, synth.KDA], ids=["qwen35", "kda"])
+def test_run_twice_bitwise(shape):
+    """The same calls on two copies of the same pool give the same bits: with
+    the work counter the tail units go to whichever workgroups draw them, which
+    differs from run to run, and nothing of a unit's arithmetic may depend on
+    that.  B=64 over a 256-slot pool, 3 calls of T=2."""
+    torch = _torch()
+    case = synth.decode_case(shape, B=64, T=2, num_slots=256, n_calls=3, seed=44)
+    g, _ = layers(shape)
+    runs = []
+    for _ in range(2):
+        d = DevCase(case, with_work=True)
+        outs = [bits(d.call(g, c)) for c in range(3)]
+        torch.cuda.synchronize()
+        assert d.work_is_zero()
+        runs.append((outs, bits(d.ssm), bits(d.conv)))
+    for c in range(3):
+        np.testing.assert_array_equal(runs[0][0][c], runs[1][0][c])
+    np.testing.assert_array_equal(runs[0][1], runs[1][1])
+    np.testing.assert_array_equal(runs[0][2], runs[1][2])
+
+
 def test_slot_zero_copy_bitwise_and_isolated():
     torch = _torch()
     shape = synth.QWEN35

@@ -187,6 +187,31 @@ def test_short_sequences_continue_their_own_slot(gate, width, dtype):
     print(f"{gate} W={width} {dtype}: {total} tokens, windows bit-exact")
 
 
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_run_twice_bitwise(gate):
+    """The same prefill on two copies of the same pool gives the same bits
+    (outputs, final states, windows, checkpoints)."""
+    torch = _torch()
+    shape = synth.Shape(4, 8, 128, 128, 4, gate, "bf16")
+    lens = [700, 64, 333, 1]
+    case = synth.prefill_case(shape, lens, 20, seed=45)
+    g, _ = layers(shape)
+    used = set(case.dst.tolist()) | set(case.init_slot[case.init_slot >= 0].tolist())
+    spare = [s for s in range(20) if s not in used]
+    tab = dev(np.array([spare[3 * i:3 * i + 3] for i in range(len(lens))], np.int32))
+    runs = []
+    for _ in range(2):
+        ssm, conv = dev(case.pool.ssm), dev(case.pool.conv)
+        out = gdn.gdn_prefill_chunked(g, ssm, conv, dev(case.dst), dev(case.init_slot),
+                                      dev(case.cu_seqlens), max(lens), dev(case.x),
+                                      dev(case.alpha), dev(case.beta), dev(case.conv_w),
+                                      ckpt_slots=tab, ckpt_every=128)
+        torch.cuda.synchronize()
+        runs.append((bits(out), bits(ssm), bits(conv)))
+    for a, b in zip(*runs):
+        np.testing.assert_array_equal(a, b)
+
+
 def test_qwen35_4x8192_zero_and_cow():
     """The full workload: 4 x 8192 tokens, 16/32 heads, d = 128, chunk 64,
     bf16 inputs; sequences alternate zero start and copy-on-write from a
